@@ -1,0 +1,186 @@
+"""ctypes binding of the fp64 CPU oracle (oracle.c).
+
+TEST INFRASTRUCTURE ONLY: only the tests, the smoke check and the bench's CPU
+baseline may import this package.  It shares no code with the HIP library.
+
+Storage formats are taken from the numpy dtype of each array: float32 is
+fp32, uint16 is bf16 bit patterns, uint8 is FP8 e4m3fn codes (which then need
+an fp32 per-token scale array).
+"""
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liboracle_spmla.so")
+_lib = None
+
+BAD_PAGE, BAD_LEN, BAD_INDEX = 1, 2, 4
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        from .build import build
+        build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i32, i64, d = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_double
+    lib.oracle_fp8_e4m3_value.restype = d
+    lib.oracle_fp8_e4m3_value.argtypes = [ctypes.c_uint8]
+    lib.oracle_bf16_value.restype = d
+    lib.oracle_bf16_value.argtypes = [ctypes.c_uint16]
+    lib.oracle_indexer_scores.restype = ctypes.c_int
+    lib.oracle_indexer_scores.argtypes = [vp, ctypes.c_int, vp, vp, vp, ctypes.c_int, i32, i32, vp, i32, vp, i32,
+                                          i64, i32, i32, vp, vp, i64, vp]
+    lib.oracle_indexer_scores_at.restype = ctypes.c_int
+    lib.oracle_indexer_scores_at.argtypes = [vp, ctypes.c_int, vp, vp, vp, ctypes.c_int, i32, i32, vp, i32, i32, i32,
+                                             vp, vp, i64, vp, vp]
+    lib.oracle_topk.restype = ctypes.c_int
+    lib.oracle_topk.argtypes = [vp, i64, vp, i32, i32, vp]
+    lib.oracle_mla_attention.restype = ctypes.c_int
+    lib.oracle_mla_attention.argtypes = [vp, ctypes.c_int, vp, vp, ctypes.c_int, i32, i32, vp, i32, vp, i32, i64,
+                                         vp, i32, i32, i32, i32, d, vp, vp, vp]
+    lib.oracle_lse_merge.restype = ctypes.c_int
+    lib.oracle_lse_merge.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp]
+    lib.oracle_kv_bytes_per_token.restype = d
+    lib.oracle_kv_bytes_per_token.argtypes = [i32, i32, i32, d]
+    lib.oracle_mla_bytes_per_token.restype = d
+    lib.oracle_mla_bytes_per_token.argtypes = [i32, i32, d, d]
+    _lib = lib
+    return lib
+
+
+_FMT = {np.dtype(np.float32): 0, np.dtype(np.uint16): 1, np.dtype(np.uint8): 2}
+
+
+def _fmt(a):
+    return _FMT[np.asarray(a).dtype]
+
+
+def _c(a, dtype=None):
+    if a is None:
+        return None
+    a = np.ascontiguousarray(a if dtype is None else np.asarray(a, dtype))
+    return a
+
+
+def _p(a):
+    return None if a is None else ctypes.c_void_p(a.ctypes.data)
+
+
+def fp8_e4m3_value(code):
+    return _load().oracle_fp8_e4m3_value(int(code))
+
+
+def bf16_value(bits):
+    return _load().oracle_bf16_value(int(bits))
+
+
+def indexer_scores(q_idx, w, k_pool, k_scale, block_table, lens, max_len=None, score_stride=None):
+    """fp64 scores [B, score_stride] (NaN-free only where t < lens[b]), magnitudes, status."""
+    q_idx, w = _c(q_idx), _c(w, np.float32)
+    k_pool, k_scale = _c(k_pool), _c(k_scale, np.float32)
+    bt, lens = _c(block_table, np.int32), _c(lens, np.int32)
+    B, H, d = q_idx.shape
+    num_pages, P = k_pool.shape[0], k_pool.shape[1]
+    max_len = int(lens.max()) if max_len is None else int(max_len)
+    stride = max(int(lens.max()), 1) if score_stride is None else int(score_stride)
+    scores = np.full((B, stride), np.nan)
+    mags = np.full((B, stride), np.nan)
+    status = np.zeros(B, np.int32)
+    rc = _load().oracle_indexer_scores(_p(q_idx), _fmt(q_idx), _p(w), _p(k_pool), _p(k_scale), _fmt(k_pool),
+                                       num_pages, P, _p(bt), bt.shape[1], _p(lens), B, max_len, H, d,
+                                       _p(scores), _p(mags), stride, _p(status))
+    assert rc == 0
+    return scores, mags, status
+
+
+def indexer_scores_at(q_idx, w, k_pool, k_scale, block_table, sample_b, sample_t):
+    """fp64 scores and magnitudes at sampled (request, token) positions."""
+    q_idx, w = _c(q_idx), _c(w, np.float32)
+    k_pool, k_scale = _c(k_pool), _c(k_scale, np.float32)
+    bt = _c(block_table, np.int32)
+    sb, st = _c(sample_b, np.int32), _c(sample_t, np.int64)
+    B, H, d = q_idx.shape
+    n = sb.shape[0]
+    s = np.empty(n)
+    a = np.empty(n)
+    rc = _load().oracle_indexer_scores_at(_p(q_idx), _fmt(q_idx), _p(w), _p(k_pool), _p(k_scale), _fmt(k_pool),
+                                          k_pool.shape[0], k_pool.shape[1], _p(bt), bt.shape[1], H, d,
+                                          _p(sb), _p(st), n, _p(s), _p(a))
+    assert rc == 0
+    return s, a
+
+
+def topk(scores, lens, k):
+    """Indices [B, k] ascending, -1 padded; scores may be any float array [B, stride]."""
+    sc = _c(scores, np.float64)
+    lens = _c(lens, np.int32)
+    B = sc.shape[0]
+    out = np.empty((B, k), np.int32)
+    rc = _load().oracle_topk(_p(sc), sc.shape[1], _p(lens), B, k, _p(out))
+    assert rc == 0
+    return out
+
+
+def mla_attention(q, kv, kv_scale, block_table, lens, indices, n_heads, d_latent, d_rope, sm_scale,
+                  max_len=None):
+    """fp64 o [B, H, d_latent], lse [B, H], status [B]; indices None = every token t < L_b."""
+    q, kv, kv_scale = _c(q), _c(kv), _c(kv_scale, np.float32)
+    bt, lens = _c(block_table, np.int32), _c(lens, np.int32)
+    idx = _c(indices, np.int32)
+    B = q.shape[0]
+    k = 0 if idx is None else idx.shape[1]
+    max_len = int(lens.max()) if max_len is None else int(max_len)
+    o = np.empty((B, n_heads, d_latent))
+    lse = np.empty((B, n_heads))
+    status = np.zeros(B, np.int32)
+    rc = _load().oracle_mla_attention(_p(q), _fmt(q), _p(kv), _p(kv_scale), _fmt(kv), kv.shape[0], kv.shape[1],
+                                      _p(bt), bt.shape[1], _p(lens), B, max_len, _p(idx), k,
+                                      n_heads, d_latent, d_rope, float(sm_scale), _p(o), _p(lse), _p(status))
+    assert rc == 0
+    return o, lse, status
+
+
+def lse_merge(o_part, lse_part):
+    """Merge partials o_part [B, S, H, d], lse_part [B, S, H] -> o [B, H, d], lse [B, H] (fp64)."""
+    op = _c(o_part, np.float64)
+    lp = _c(lse_part, np.float64)
+    B, S, H, d = op.shape
+    o = np.empty((B, H, d))
+    lse = np.empty((B, H))
+    rc = _load().oracle_lse_merge(_p(op), _p(lp), B, S, H, d, _p(o), _p(lse))
+    assert rc == 0
+    return o, lse
+
+
+def kv_bytes_per_token(layers, kv_heads, head_dim, bytes_per_elem):
+    return _load().oracle_kv_bytes_per_token(layers, kv_heads, head_dim, float(bytes_per_elem))
+
+
+def mla_bytes_per_token(d_latent, d_rope, bytes_per_elem, scale_bytes=0.0):
+    return _load().oracle_mla_bytes_per_token(d_latent, d_rope, float(bytes_per_elem), float(scale_bytes))
+
+
+def decode_step(inp, k=None, splits=None):
+    """Whole step on one generator `Inputs`: indexer -> top-k -> attention (fp64).
+
+    Returns dict(scores, idx, o, lse, status).  Dense workloads (no indexer)
+    attend every token."""
+    cfg = inp.cfg
+    out = {}
+    if cfg.dense:
+        idx = None
+    else:
+        scores, _, st = indexer_scores(inp.q_idx, inp.w, inp.k_idx, inp.k_idx_scale, inp.block_table, inp.lens,
+                                       score_stride=inp.score_stride)
+        idx = topk(scores, inp.lens, cfg.topk if k is None else k)
+        out["scores"] = scores
+        out["idx"] = idx
+    o, lse, st = mla_attention(inp.q, inp.kv, inp.kv_scale, inp.block_table, inp.lens, idx, cfg.n_heads,
+                               cfg.d_latent, cfg.d_rope, cfg.softmax_scale)
+    out.update(o=o, lse=lse, status=st)
+    return out

@@ -1,0 +1,432 @@
+"""Pins of the fp64 oracle against things other than itself.
+
+Each check uses a closed form, an invariant, a brute force written
+independently with library routines (numpy einsum, scipy softmax/logsumexp,
+Python's sort, torch's float8/bfloat16 casts), or a value printed on the
+pages.  They are chosen so that a plausible slip in the oracle -- a dropped
+term (the rope dims, the ReLU, the head weight), a wrong sign, a wrong index
+or page mapping, a transposed operand, the wrong tie rule -- fails one.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+from scipy.special import logsumexp, softmax
+
+import oracle
+import spmla_gen as gen
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ------------------------------------------------------------------ decoders
+
+def test_fp8_closed_form_all_codes():
+    vals = np.array([oracle.fp8_e4m3_value(c) for c in range(256)])
+    assert vals[0x7E] == 448.0
+    assert vals[0x08] == 2.0 ** -6
+    assert vals[0x01] == 2.0 ** -9
+    assert vals[0x07] == 7 * 2.0 ** -9
+    assert vals[0x38] == 1.0
+    assert vals[0x00] == 0.0 and math.copysign(1, vals[0x80]) == -1.0
+    assert np.isnan(vals[0x7F]) and np.isnan(vals[0xFF])
+    assert np.sum(np.isnan(vals)) == 2
+    np.testing.assert_array_equal(vals[0x80:0xFF], -vals[0x00:0x7F])
+    assert np.all(np.diff(vals[0:0x7F]) > 0)  # strictly increasing magnitude over the positive codes
+
+
+def test_fp8_matches_torch_float8_e4m3fn():
+    codes = torch.arange(256, dtype=torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    ours = np.array([oracle.fp8_e4m3_value(c) for c in range(256)])
+    np.testing.assert_array_equal(np.isnan(ours), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    np.testing.assert_array_equal(ours[ok], ref[ok])
+
+
+def test_bf16_matches_torch():
+    rng = np.random.default_rng(0)
+    bits = rng.integers(0, 2 ** 16, 4096, dtype=np.uint16)
+    bits = bits[(bits & 0x7F80) != 0x7F80]  # finite patterns
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    ours = np.array([oracle.bf16_value(b) for b in bits])
+    np.testing.assert_array_equal(ours, ref)
+
+
+# ------------------------------------------------------- helpers for brute force
+
+def _fp8_to_f64(codes):
+    return torch.from_numpy(np.ascontiguousarray(codes)).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def _bf16_to_f64(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+
+
+def _values(arr, scale=None):
+    """Library-routine decode of a storage array to float64 (torch casts)."""
+    if arr.dtype == np.float32:
+        v = arr.astype(np.float64)
+    elif arr.dtype == np.uint16:
+        v = _bf16_to_f64(arr)
+    else:
+        v = _fp8_to_f64(arr) * scale.astype(np.float64)[..., None]
+    return v
+
+
+def _logical_rows(inp, pool, scale, b):
+    """Rows of request b from an un-shuffled (contiguous) pool: a plain slice."""
+    first = int(inp.block_table[b, 0])
+    L = int(inp.lens[b])
+    P = inp.cfg.page_size
+    flat = _values(pool, scale).reshape(-1, pool.shape[-1])
+    return flat[first * P: first * P + L]
+
+
+@pytest.fixture(scope="module")
+def c1_contig():
+    return gen.make_inputs("c1", shuffle=False)
+
+
+@pytest.fixture(scope="module")
+def c1():
+    return gen.make_inputs("c1")
+
+
+def _fp8_small():
+    cfg = gen.CONFIGS["c1"].with_(cache_dtype=gen.FP8, idx_dtype=gen.FP8, q_dtype=gen.BF16, name="c1f8")
+    return cfg
+
+
+# ------------------------------------------------------------------- indexer
+
+def _brute_scores(inp, b):
+    K = _logical_rows(inp, inp.k_idx, inp.k_idx_scale, b)           # [L, d]
+    q = _values(inp.q_idx[b])                                         # [H, d]
+    w = inp.w[b].astype(np.float64)                                   # [H]
+    dots = np.einsum("hd,td->ht", q, K)
+    return np.einsum("h,ht->t", w, np.maximum(dots, 0.0))
+
+
+@pytest.mark.parametrize("cfg", ["c1", "c1f8"])
+def test_indexer_matches_einsum_brute_force(cfg):
+    c = gen.CONFIGS["c1"] if cfg == "c1" else _fp8_small()
+    inp = gen.make_inputs(c, shuffle=False)
+    s, a, st = oracle.indexer_scores(inp.q_idx, inp.w, inp.k_idx, inp.k_idx_scale, inp.block_table, inp.lens)
+    assert not st.any()
+    for b in range(inp.cfg.batch):
+        L = inp.lens[b]
+        ref = _brute_scores(inp, b)
+        np.testing.assert_allclose(s[b, :L], ref, rtol=1e-12, atol=1e-12)
+        assert np.all(a[b, :L] >= np.abs(s[b, :L]) - 1e-12)
+
+
+def test_indexer_page_permutation_invariant(c1, c1_contig):
+    s1, _, _ = oracle.indexer_scores(c1.q_idx, c1.w, c1.k_idx, c1.k_idx_scale, c1.block_table, c1.lens)
+    s2, _, _ = oracle.indexer_scores(c1_contig.q_idx, c1_contig.w, c1_contig.k_idx, c1_contig.k_idx_scale,
+                                     c1_contig.block_table, c1_contig.lens)
+    for b in range(2):
+        L = c1.lens[b]
+        np.testing.assert_array_equal(s1[b, :L], s2[b, :L])
+
+
+def test_indexer_special_cases(c1_contig):
+    inp = c1_contig
+    # w = 0 => every score is 0.
+    s, _, _ = oracle.indexer_scores(inp.q_idx, np.zeros_like(inp.w), inp.k_idx, None, inp.block_table, inp.lens)
+    for b in range(2):
+        assert np.all(s[b, :inp.lens[b]] == 0.0)
+    # One head, w = 1 => ReLU of the plain dot product.
+    q1 = np.ascontiguousarray(inp.q_idx[:, :1, :])
+    s, _, _ = oracle.indexer_scores(q1, np.ones((2, 1), np.float32), inp.k_idx, None, inp.block_table, inp.lens)
+    for b in range(2):
+        K = _logical_rows(inp, inp.k_idx, None, b)
+        np.testing.assert_allclose(s[b, :inp.lens[b]], np.maximum(K @ q1[b, 0].astype(np.float64), 0), rtol=1e-13)
+    # q_h = e_j for every head => sum_h w_h * ReLU(k_t[j]); negative w flips the sign of the sum.
+    j = 5
+    qe = np.zeros_like(inp.q_idx)
+    qe[:, :, j] = 1.0
+    w = np.array([[0.5, -2.0], [3.0, 1.0]], np.float32)
+    s, _, _ = oracle.indexer_scores(qe, w, inp.k_idx, None, inp.block_table, inp.lens)
+    for b in range(2):
+        K = _logical_rows(inp, inp.k_idx, None, b)
+        np.testing.assert_allclose(s[b, :inp.lens[b]], w[b].sum() * np.maximum(K[:, j], 0), rtol=1e-13)
+
+
+def test_indexer_sampled_equals_full(c1):
+    s, a, _ = oracle.indexer_scores(c1.q_idx, c1.w, c1.k_idx, c1.k_idx_scale, c1.block_table, c1.lens)
+    sb = np.array([0, 0, 1, 1, 1], np.int32)
+    stk = np.array([0, 36, 0, 50, 99], np.int64)
+    s2, a2 = oracle.indexer_scores_at(c1.q_idx, c1.w, c1.k_idx, c1.k_idx_scale, c1.block_table, sb, stk)
+    np.testing.assert_array_equal(s2, s[sb, stk])
+    np.testing.assert_array_equal(a2, a[sb, stk])
+
+
+def test_indexer_status_flags(c1):
+    bt = c1.block_table.copy()
+    bt[1, 3] = c1.num_pages  # out of range page used by request 1
+    s, _, st = oracle.indexer_scores(c1.q_idx, c1.w, c1.k_idx, c1.k_idx_scale, bt, c1.lens)
+    assert st[0] == 0 and st[1] == oracle.BAD_PAGE
+    assert np.all(np.isnan(s[1, :100])) and not np.isnan(s[0, :37]).any()
+    lens = c1.lens.copy()
+    lens[0] = 200  # beyond its mapped pages (bt_stride * P = 112)
+    _, _, st = oracle.indexer_scores(c1.q_idx, c1.w, c1.k_idx, c1.k_idx_scale, c1.block_table, lens)
+    assert st[0] == oracle.BAD_LEN and st[1] == 0
+
+
+# --------------------------------------------------------------------- top-k
+
+def _brute_topk(s, L, k):
+    def key(t):
+        v = s[t]
+        return (1, 0.0, t) if np.isnan(v) else (0, -float(v), t)
+    order = sorted(range(L), key=key)
+    sel = sorted(order[:min(k, L)])
+    return sel + [-1] * (k - len(sel))
+
+
+def test_topk_brute_force_with_ties_nan_negzero():
+    rng = np.random.default_rng(1)
+    for trial in range(200):
+        L = int(rng.integers(1, 60))
+        k = int(rng.integers(1, 70))
+        s = rng.integers(-3, 4, L).astype(np.float64)  # many exact ties
+        if trial % 3 == 0:
+            s[rng.random(L) < 0.2] = np.nan
+        if trial % 4 == 0:
+            s[s == 0] = -0.0
+        if trial % 5 == 0:
+            s[rng.random(L) < 0.2] = -np.inf
+        got = oracle.topk(s[None, :], np.array([L]), k)[0]
+        assert list(got) == _brute_topk(s, L, k), (trial, s, k)
+
+
+def test_topk_invariants_large():
+    rng = np.random.default_rng(2)
+    L, k = 50000, 2048
+    s = np.round(rng.standard_normal(L) * 50) / 4  # coarse grid -> ties at the threshold
+    idx = oracle.topk(s[None, :], np.array([L]), k)[0]
+    assert np.all(np.diff(idx) > 0) and len(idx) == k
+    sel = np.zeros(L, bool)
+    sel[idx] = True
+    assert s[sel].min() >= s[~sel].max()
+    thr = s[sel].min()
+    tied_sel = np.where(sel & (s == thr))[0]
+    tied_un = np.where(~sel & (s == thr))[0]
+    assert len(tied_un) == 0 or tied_un.min() > tied_sel.max()
+
+
+def test_topk_degenerate():
+    L, k = 300, 64
+    idx = oracle.topk(np.full((1, L), 1.5), np.array([L]), k)[0]
+    np.testing.assert_array_equal(idx, np.arange(k))
+    s = np.random.default_rng(3).standard_normal((1, 40))
+    idx = oracle.topk(s, np.array([40]), 64)[0]
+    np.testing.assert_array_equal(idx, np.r_[np.arange(40), -np.ones(24)])
+    idx = oracle.topk(s, np.array([0]), 8)[0]
+    assert np.all(idx == -1)
+    s = np.array([[-0.0, 0.0, -0.0, 1.0]])
+    np.testing.assert_array_equal(oracle.topk(s, np.array([4]), 2)[0], [0, 3])
+
+
+# ----------------------------------------------------------------- attention
+
+def _brute_attention(inp, b, tokens=None):
+    """Dense softmax without the max trick (fine for N(0,1) data at tiny sizes), library softmax."""
+    cfg = inp.cfg
+    C = _logical_rows(inp, inp.kv, inp.kv_scale, b)
+    if tokens is not None:
+        C = C[tokens]
+    q = _values(inp.q[b])                                            # [H, D]
+    z = cfg.softmax_scale * (q @ C.T)                                 # [H, n]
+    p = np.exp(z) / np.exp(z).sum(axis=1, keepdims=True)
+    o = p @ C[:, :cfg.d_latent]
+    lse = np.log(np.exp(z).sum(axis=1))
+    # cross-check the hand softmax with the library's
+    np.testing.assert_allclose(p, softmax(z, axis=1), rtol=1e-12)
+    np.testing.assert_allclose(lse, logsumexp(z, axis=1), rtol=1e-12)
+    return o, lse
+
+
+def _att(inp, idx=None, q=None, kv=None, kv_scale=None, bt=None, lens=None):
+    c = inp.cfg
+    return oracle.mla_attention(inp.q if q is None else q, inp.kv if kv is None else kv,
+                                inp.kv_scale if kv_scale is None else kv_scale,
+                                inp.block_table if bt is None else bt, inp.lens if lens is None else lens,
+                                idx, c.n_heads, c.d_latent, c.d_rope, c.softmax_scale)
+
+
+@pytest.mark.parametrize("cfg", ["c1", "c1f8"])
+def test_attention_dense_matches_brute_force(cfg):
+    c = gen.CONFIGS["c1"] if cfg == "c1" else _fp8_small()
+    inp = gen.make_inputs(c, shuffle=False)
+    o, lse, st = _att(inp)
+    assert not st.any()
+    for b in range(2):
+        ro, rl = _brute_attention(inp, b)
+        np.testing.assert_allclose(o[b], ro, rtol=1e-11, atol=1e-12)
+        np.testing.assert_allclose(lse[b], rl, rtol=1e-12)
+
+
+def test_attention_sparse_matches_brute_force(c1_contig):
+    inp = c1_contig
+    rng = np.random.default_rng(4)
+    k = 20
+    idx = np.full((2, k), -1, np.int32)
+    sets = []
+    for b in range(2):
+        sel = np.sort(rng.choice(inp.lens[b], size=12 + 5 * b, replace=False))
+        idx[b, :len(sel)] = sel
+        rng.shuffle(idx[b])  # order and padding position must not matter
+        sets.append(sel)
+    o, lse, _ = _att(inp, idx)
+    for b in range(2):
+        ro, rl = _brute_attention(inp, b, sets[b])
+        np.testing.assert_allclose(o[b], ro, rtol=1e-11, atol=1e-12)
+        np.testing.assert_allclose(lse[b], rl, rtol=1e-12)
+
+
+def test_attention_page_permutation_invariant(c1, c1_contig):
+    o1, l1, _ = _att(c1)
+    o2, l2, _ = _att(c1_contig)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(l1, l2)
+
+
+def test_attention_closed_forms(c1_contig):
+    inp = c1_contig
+    c = inp.cfg
+    # q = 0 => uniform weights: o = mean of the value rows, lse = ln |S|.
+    o, lse, _ = _att(inp, q=np.zeros_like(inp.q))
+    for b in range(2):
+        C = _logical_rows(inp, inp.kv, None, b)
+        np.testing.assert_allclose(o[b], np.broadcast_to(C[:, :c.d_latent].mean(0), o[b].shape), rtol=1e-12,
+                                   atol=1e-14)
+        np.testing.assert_allclose(lse[b], np.log(inp.lens[b]), rtol=1e-14)
+    # Every row equal to one vector => o = its latent part, lse = z + ln |S|.
+    row = gen.normals32(9, 0, 0, c.dim)
+    kv = np.broadcast_to(row, inp.kv.shape).copy()
+    o, lse, _ = _att(inp, kv=kv)
+    for b in range(2):
+        z = c.softmax_scale * (inp.q[b].astype(np.float64) @ row.astype(np.float64))
+        np.testing.assert_allclose(o[b], np.broadcast_to(row[:c.d_latent], o[b].shape), rtol=1e-12)
+        np.testing.assert_allclose(lse[b], z + np.log(inp.lens[b]), rtol=1e-12)
+
+
+def test_topk_k_ge_len_equals_dense(c1):
+    dense_o, dense_l, _ = _att(c1)
+    s, _, _ = oracle.indexer_scores(c1.q_idx, c1.w, c1.k_idx, c1.k_idx_scale, c1.block_table, c1.lens)
+    idx = oracle.topk(s, c1.lens, 128)
+    o, l, _ = _att(c1, idx=idx)
+    np.testing.assert_allclose(o, dense_o, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(l, dense_l, rtol=1e-12)
+
+
+def test_attention_status(c1):
+    idx = np.tile(np.arange(32, dtype=np.int32), (2, 1))
+    idx[0, 5] = 37  # == L_0: out of range
+    o, lse, st = _att(c1, idx=idx)
+    assert st[0] == oracle.BAD_INDEX and st[1] == 0
+    assert np.isnan(o[0]).all() and np.isnan(lse[0]).all() and not np.isnan(o[1]).any()
+    bt = c1.block_table.copy()
+    bt[0, 1] = -5
+    _, _, st = _att(c1, bt=bt)
+    assert st[0] == oracle.BAD_PAGE and st[1] == 0
+    empty = np.full((2, 4), -1, np.int32)
+    o, lse, st = _att(c1, idx=empty)
+    assert not st.any() and np.all(o == 0) and np.all(lse == -np.inf)
+
+
+# --------------------------------------------------------------------- merge
+
+def test_merge_partition_equals_unsplit(c1):
+    rng = np.random.default_rng(5)
+    full_o, full_l, _ = _att(c1)
+    for S in (1, 2, 3, 7):
+        parts_o, parts_l = [], []
+        assign = [rng.integers(0, S, int(L)) for L in c1.lens]
+        for j in range(S):
+            k = int(max(c1.lens))
+            idx = np.full((2, k), -1, np.int32)
+            for b in range(2):
+                sel = np.where(assign[b] == j)[0]
+                idx[b, :len(sel)] = sel
+            o, l, _ = _att(c1, idx=idx)
+            parts_o.append(o)
+            parts_l.append(l)
+        o, l = oracle.lse_merge(np.stack(parts_o, 1), np.stack(parts_l, 1))
+        np.testing.assert_allclose(o, full_o, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(l, full_l, rtol=1e-13)
+
+
+def test_merge_algebra():
+    rng = np.random.default_rng(6)
+    B, H, d = 3, 4, 8
+    parts = [(rng.standard_normal((B, 1, H, d)), rng.standard_normal((B, 1, H)) * 3) for _ in range(3)]
+    a, b, c = parts
+
+    def m(*xs):
+        o, l = oracle.lse_merge(np.concatenate([x[0] for x in xs], 1), np.concatenate([x[1] for x in xs], 1))
+        return o[:, None], l[:, None]
+    left = m(m(a, b), c)
+    right = m(a, m(b, c))
+    np.testing.assert_allclose(left[0], right[0], atol=1e-12)
+    np.testing.assert_allclose(left[1], right[1], atol=1e-12)
+    comm = m(c, a, b)
+    np.testing.assert_allclose(comm[0], left[0], atol=1e-12)
+    # Equal LSEs: plain average, lse + ln(m).
+    lse_eq = np.broadcast_to(a[1], (B, 3, H)).copy()
+    os_ = np.concatenate([a[0], b[0], c[0]], 1)
+    o, l = oracle.lse_merge(os_, lse_eq)
+    np.testing.assert_allclose(o, os_.mean(1), atol=1e-13)
+    np.testing.assert_allclose(l, a[1][:, 0] + np.log(3), atol=1e-13)
+    # An empty split (-inf) is the identity; all empty gives o = 0, lse = -inf.
+    empty = (np.zeros((B, 1, H, d)), np.full((B, 1, H), -np.inf))
+    o, l = m(a, empty)
+    np.testing.assert_allclose(o[:, 0], a[0][:, 0], atol=1e-14)
+    np.testing.assert_allclose(l[:, 0], a[1][:, 0], atol=1e-14)
+    o, l = m(empty, empty)
+    assert np.all(o == 0) and np.all(l == -np.inf)
+    # Weights use lse differences: a shift of every lse by c leaves o unchanged and shifts lse by c.
+    o1, l1 = m(a, b)
+    o2, l2 = m((a[0], a[1] + 7.5), (b[0], b[1] + 7.5))
+    np.testing.assert_allclose(o1, o2, atol=1e-13)
+    np.testing.assert_allclose(l2, l1 + 7.5, atol=1e-12)
+
+
+# --------------------------------------------------------- cache accounting
+
+def test_kv_size_closed_form_matches_pages():
+    g = json.load(open(os.path.join(GOLDEN, "kv_cache_size.json")))
+    e = g["mha_fp16_example"]
+    per_tok = oracle.kv_bytes_per_token(e["layers"], e["kv_heads"], e["head_dim"], e["bytes_per_elem"])
+    assert per_tok == 1474560.0
+    assert round(per_tok / 1e6, 2) == e["bytes_per_token_MB"]
+    assert round(per_tok * 8192 / 1e9) == e["seq_8k_GB"]
+    assert round(per_tok * 16384 / 1e9) == e["seq_16k_GB"]
+    s = g["ledger_snippet"]
+    per_tok = oracle.kv_bytes_per_token(s["layers"], s["kv_heads"], s["head_dim"], s["bytes_per_elem"])
+    assert round(per_tok / 1024, 1) == s["kv_per_token_KiB"]
+    gib_8k = per_tok * 8192 / 1024 ** 3
+    assert round(gib_8k, 2) == s["seq_8k_GiB"]
+    usable = s["gpu_total_gb"] * (1 - s["reserved_ratio"]) - s["weights_gb"]
+    assert int(usable // gib_8k) == s["max_seqs_at_8k"]
+    # FP8 halves the per-element bytes, which doubles the tokens a fixed budget holds.
+    f = g["fp8_capacity"]
+    ratio = oracle.kv_bytes_per_token(1, 1, 1, 2) / oracle.kv_bytes_per_token(1, 1, 1, 1)
+    assert abs(f["fp8_tokens"] / f["bf16_tokens"] - ratio) < 0.01
+
+
+def test_mla_pool_accounting_matches_generator_layout():
+    assert oracle.mla_bytes_per_token(512, 64, 2) == 1152.0
+    assert oracle.mla_bytes_per_token(512, 64, 1, 4) == 580.0
+    for name in ("c1", "c1f8"):
+        c = gen.CONFIGS["c1"] if name == "c1" else _fp8_small()
+        inp = gen.make_inputs(c)
+        slots = inp.num_pages * c.page_size
+        nbytes = inp.kv.nbytes + (inp.kv_scale.nbytes if inp.kv_scale is not None else 0)
+        elem = inp.kv.itemsize
+        assert nbytes / slots == oracle.mla_bytes_per_token(c.d_latent, c.d_rope, elem, 4 if elem == 1 else 0)
