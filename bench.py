@@ -1,0 +1,239 @@
+"""Decode-step benchmark of the sparse paged MLA layer on one MI355X.
+
+One step = dsa_indexer_scores -> topk_select -> mla_paged_decode -> lse_merge
+(dense workloads: decode -> merge) on one HIP stream, every input resident in
+HBM.  The default workload is the 64-request 32K-128K FP8 decode (c3f).
+
+Timing: W untimed warm-up steps, then exactly K timed steps.  Before each
+timed step a 512 MiB buffer is overwritten (outside the timed events) so the
+step starts with cold L2 and MALL.  Each kernel is bracketed by HIP events on
+the stream it runs on; the step time is the sum of its kernels' spans (start
+of the first to end of the last).  `value` = requests / mean step time.
+A warm number (K steps back to back, no flush) is reported beside it.
+
+Prints ONE JSON line (rank 0).  Other workloads: --config c2|c3|c4|c5.
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="c3f")
+    ap.add_argument("--splits", type=int, default=0, help="KV splits (0: per-workload default)")
+    ap.add_argument("--no-flush", action="store_true")
+    ap.add_argument("--cpu-requests", type=int, default=-1,
+                    help="requests in the CPU-oracle sample (-1: auto, 0: skip)")
+    ap.add_argument("--profile-only", action="store_true", help="no CPU baseline, fewer extras (for rocprofv3)")
+    return ap.parse_args()
+
+
+def algorithmic(cfg, lens):
+    """Per-kernel algorithmic bytes and FLOPs of one step (what the method must move / compute)."""
+    B, H, D, dc = cfg.batch, cfg.n_heads, cfg.dim, cfg.d_latent
+    sumL = int(lens.sum())
+    e_c = {0: 4, 1: 2, 2: 1}[cfg.cache_dtype]
+    s_c = 4 if cfg.cache_dtype == 2 else 0
+    e_q = {0: 4, 1: 2}[cfg.q_dtype]
+    out = {}
+    if cfg.dense:
+        n_sel = sumL
+        k = 0
+    else:
+        k = cfg.topk
+        HI, dI = cfg.idx_heads, cfg.idx_dim
+        e_k = {0: 4, 1: 2, 2: 1}[cfg.idx_dtype]
+        s_k = 4 if cfg.idx_dtype == 2 else 0
+        out["indexer"] = dict(bytes=sumL * (dI * e_k + s_k) + B * HI * (dI * e_q + 4) + 4 * sumL,
+                              flops=2 * HI * dI * sumL)
+        out["topk"] = dict(bytes=4 * sumL + 4 * B * k, flops=0)
+        n_sel = int(sum(min(k, int(L)) for L in lens))
+    out["decode"] = dict(bytes=n_sel * (D * e_c + s_c) + B * H * D * e_q + 4 * B * H * (dc + 1) + 4 * B * k,
+                         flops=2 * H * (D + dc) * n_sel)
+    out["merge"] = dict(bytes=0, flops=0)
+    return out
+
+
+def roofline_time_s(a):
+    return sum(max(v["bytes"] / (HBM_PEAK_GBS * 1e9), v["flops"] / (BF16_PEAK_TFLOPS * 1e12)) for v in a.values())
+
+
+def kernel_source_sha(name):
+    p = os.path.join(ROOT, "sparse_paged_mla_amd", "csrc", name)
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel_file, workload):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if taken on this kernel source."""
+    p = os.path.join(ROOT, "profiles", "counters.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        rec = json.load(open(p)).get(workload, {}).get(kernel_file)
+    except (ValueError, OSError):
+        return None
+    if not rec or rec.get("source_sha") != kernel_source_sha(kernel_file):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(inp, n_req):
+    """The fp64 oracle, as it stands, on the first n_req requests of the same inputs (one thread)."""
+    import numpy as np
+    import oracle
+    cfg = inp.cfg
+    sl = slice(0, n_req)
+    t0 = time.perf_counter()
+    idx = None
+    if not cfg.dense:
+        s, _, _ = oracle.indexer_scores(inp.q_idx[sl], inp.w[sl], inp.k_idx, inp.k_idx_scale, inp.block_table[sl],
+                                        inp.lens[sl], max_len=inp.max_len, score_stride=int(inp.lens[sl].max()))
+        idx = oracle.topk(s, inp.lens[sl], cfg.topk)
+    oracle.mla_attention(inp.q[sl], inp.kv, inp.kv_scale, inp.block_table[sl], inp.lens[sl], idx, cfg.n_heads,
+                         cfg.d_latent, cfg.d_rope, cfg.softmax_scale, max_len=inp.max_len)
+    dt = time.perf_counter() - t0
+    return dict(value=n_req / dt, unit="decode tokens/s", cores=1, kind="oracle",
+                sample=f"first {n_req} of {cfg.batch} requests of {cfg.name} "
+                       f"({int(np.sum(inp.lens[sl]))} context tokens), full step: indexer + top-k + attention "
+                       f"in fp64, one thread, {dt:.1f} s")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    import spmla_gen as gen
+    from spmla_gen.torch_io import device_batch
+    from sparse_paged_mla_amd.step import DecodeStep
+    import sparse_paged_mla_amd as spm
+
+    spm.load_library()
+    cfg = gen.CONFIGS[args.config]
+    t_gen = time.perf_counter()
+    inp = gen.make_inputs(cfg)
+    db = device_batch(inp, "cuda")
+    torch.cuda.synchronize()
+    print(f"[bench] {cfg.name}: inputs ready in {time.perf_counter() - t_gen:.1f} s "
+          f"(sum L = {int(inp.lens.sum())}, pool {inp.num_pages} pages)", file=sys.stderr, flush=True)
+    default_splits = {"c1": 1, "c2": 4, "c3": 2, "c3f": 2, "c4": 2, "c5": 8}
+    splits = args.splits or default_splits.get(cfg.name, 1)
+    step = DecodeStep(db, num_splits=splits)
+    stages = ["indexer", "select", "attend", "merge"] if step.sparse else ["attend", "merge"]
+    if splits == 1:
+        stages.remove("merge")
+    flush_buf = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
+
+    def run_timed(flush):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
+        if flush:
+            flush_buf.fill_(1.0)
+        evs[0].record()
+        for i, name in enumerate(stages):
+            getattr(step, name)()
+            evs[i + 1].record()
+        return evs
+
+    for _ in range(args.warmup):
+        run_timed(False)
+    torch.cuda.synchronize()
+    assert not step.status.cpu().numpy().any(), "device status flags set on clean inputs"
+
+    flush = not args.no_flush
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    recs = [run_timed(flush) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    per_stage = {n: [] for n in stages}
+    step_ms = []
+    for evs in recs:
+        step_ms.append(evs[0].elapsed_time(evs[-1]))
+        for i, n in enumerate(stages):
+            per_stage[n].append(evs[i].elapsed_time(evs[i + 1]))
+    mean_ms = statistics.fmean(step_ms)
+
+    # Warm: K steps back to back.
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        step.run()
+    e1.record()
+    torch.cuda.synchronize()
+    warm_ms = e0.elapsed_time(e1) / args.steps
+
+    alg = algorithmic(cfg, inp.lens)
+    t_star = roofline_time_s(alg)
+    kname = {"indexer": "indexer", "select": "topk", "attend": "decode", "merge": "merge"}
+    kernel_ms = {kname[n]: statistics.fmean(v) for n, v in per_stage.items()}
+    # Dominant kernel: the one with the largest roofline time.
+    dom = max((k for k in kernel_ms if k in alg),
+              key=lambda k: max(alg[k]["bytes"] / HBM_PEAK_GBS, alg[k]["flops"] / BF16_PEAK_TFLOPS * 1e-3))
+    dk = alg[dom]
+    t_dom = kernel_ms[dom] * 1e-3
+    hbm_bound = dk["bytes"] / (HBM_PEAK_GBS * 1e9) >= dk["flops"] / (BF16_PEAK_TFLOPS * 1e12)
+    src = {"indexer": "indexer.hip", "topk": "topk.hip", "decode": "mla_decode.hip", "merge": "lse_merge.hip"}[dom]
+    traffic = measured_traffic(src, cfg.name)
+    if hbm_bound:
+        achieved = dk["bytes"] / t_dom / 1e9
+        roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic, kernel=dom,
+                    algorithmic_bytes=int(dk["bytes"]), avg_launch_us=round(t_dom * 1e6, 2))
+    else:
+        achieved = dk["flops"] / t_dom / 1e12
+        roof = dict(bound="mfma", achieved=round(achieved, 2), peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
+                    frac=round(achieved / BF16_PEAK_TFLOPS, 4), traffic=traffic, kernel=dom,
+                    algorithmic_flops=int(dk["flops"]), avg_launch_us=round(t_dom * 1e6, 2))
+
+    n_cpu = args.cpu_requests
+    if n_cpu < 0:
+        n_cpu = {"c1": 2, "c2": 32, "c3": 6, "c3f": 6, "c4": 32, "c5": 1}.get(cfg.name, 1)
+    cpu = None if (args.profile_only or n_cpu == 0) else cpu_baseline(inp, min(n_cpu, cfg.batch))
+
+    value = cfg.batch / (mean_ms * 1e-3)
+    line = {
+        "metric": "decode tokens/s for sparse paged MLA attention (one layer, one decode step)",
+        "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(mean_ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded generator)",
+        "config": {
+            "workload": f"{cfg.name}: {cfg.batch} requests, context {cfg.lens}, sum L {int(inp.lens.sum())}, "
+                        f"{cfg.n_heads} heads, latent {cfg.d_latent}+{cfg.d_rope}, "
+                        + ("dense attention" if cfg.dense else
+                           f"indexer {cfg.idx_heads}x{cfg.idx_dim} {gen.DTYPE_NAMES[cfg.idx_dtype]}, top-k {cfg.topk}")
+                        + f", cache {gen.DTYPE_NAMES[cfg.cache_dtype]}, page {cfg.page_size}",
+            "global_batch": cfg.batch, "seq_len": int(inp.max_len), "num_splits": splits,
+            "parallelism": "single GPU", "cache_flush_between_steps": flush},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "step_roofline": {"t_star_us": round(t_star * 1e6, 2), "t_step_us": round(mean_ms * 1e3, 2),
+                          "frac": round(t_star / (mean_ms * 1e-3), 4)},
+        "kernel_us": {k: round(v * 1e3, 2) for k, v in kernel_ms.items()},
+        "step_ms_median_min_max": [round(statistics.median(step_ms), 4), round(min(step_ms), 4),
+                                   round(max(step_ms), 4)],
+        "warm_ms_per_step": round(warm_ms, 4), "warm_value": round(cfg.batch / (warm_ms * 1e-3), 1),
+        "wall_ms_per_step_incl_flush": round(wall / args.steps * 1e3, 4),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

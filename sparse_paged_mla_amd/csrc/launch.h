@@ -1,0 +1,42 @@
+// Internal launcher declarations (host side).  Arguments are validated by the
+// C-ABI layer before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace spmla {
+
+struct IndexerArgs {
+  const void* q_idx; int q_dtype; const float* w;
+  const void* k_pool; const float* k_scale; int k_dtype;
+  int32_t num_pages, page_size; const int32_t* bt; int32_t bt_stride;
+  const int32_t* lens; int32_t batch; int64_t max_len; int32_t n_heads, d;
+  float* scores; int64_t score_stride; int32_t* status;
+};
+// Returns 0 on success, -2 unsupported combination, -3 launch failure.
+int launch_indexer(const IndexerArgs& a, hipStream_t stream);
+
+struct TopkArgs {
+  const float* scores; int64_t score_stride; const int32_t* lens; int32_t batch; int64_t max_len;
+  int32_t k; int32_t* out_idx; void* workspace; int32_t* status;
+};
+size_t topk_workspace_size(int32_t batch, int64_t max_len, int32_t k);
+int launch_topk(const TopkArgs& a, hipStream_t stream);
+
+struct DecodeArgs {
+  const void* q; int q_dtype; const void* kv; const float* kv_scale; int kv_dtype;
+  int32_t num_pages, page_size; const int32_t* bt; int32_t bt_stride;
+  const int32_t* lens; int32_t batch; int64_t max_len; const int32_t* indices; int32_t k;
+  int32_t n_heads, d_latent, d_rope; float sm_scale; int32_t num_splits;
+  float* o_part; float* lse_part; int32_t* status;
+};
+int launch_decode(const DecodeArgs& a, hipStream_t stream);
+
+struct MergeArgs {
+  const float* o_part; const float* lse_part; int32_t batch, num_splits, n_heads, d; float* o; float* lse;
+};
+int launch_merge(const MergeArgs& a, hipStream_t stream);
+
+}  // namespace spmla

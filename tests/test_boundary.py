@@ -1,0 +1,142 @@
+"""The C ABI without a GPU: the library loads, exports every entry point the
+header declares, and rejects bad arguments on the host with the documented
+status codes before anything is enqueued (no call here reaches a kernel)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sparse_mla.h")
+LIB = os.path.join(ROOT, "sparse_paged_mla_amd", "libsparse_mla.so")
+
+OK, EINVAL, EUNSUPPORTED, ELAUNCH, EWORKSPACE = 0, -1, -2, -3, -4
+F32, BF16, FP8 = 0, 1, 2
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\**\s+\**([a-z_0-9]+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail("libsparse_mla.so is not built (run __graft_entry__.build())")
+    import sparse_paged_mla_amd as spm
+    return spm.load_library()
+
+
+def test_header_declares_the_four_operations():
+    names = _declared()
+    for n in ("dsa_indexer_scores", "topk_select", "mla_paged_decode", "lse_merge", "topk_workspace_bytes",
+              "spmla_last_error"):
+        assert n in names, names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for n in _declared():
+        assert hasattr(lib, n), f"{n} not exported"
+
+
+def test_product_never_loads_the_oracle():
+    for dirpath, _, files in os.walk(os.path.join(ROOT, "sparse_paged_mla_amd")):
+        for f in files:
+            if f.endswith((".py", ".cpp", ".hip", ".h")):
+                text = open(os.path.join(dirpath, f), errors="ignore").read()
+                assert "oracle" not in text.replace("oracle-free", ""), f"{f} mentions the oracle"
+
+
+FAKE = ctypes.c_void_p(0x1000)   # a non-null 16-byte-aligned value; never dereferenced by rejected calls
+MIS = ctypes.c_void_p(0x1004)    # misaligned
+
+
+def _idx(lib, **kw):
+    a = dict(q_idx=FAKE, q_dtype=BF16, w=FAKE, k_pool=FAKE, k_scale=FAKE, k_dtype=FP8, num_pages=10, page_size=64,
+             bt=FAKE, bt_stride=4, lens=FAKE, batch=2, max_len=256, n_heads=64, d=128, scores=FAKE,
+             score_stride=256, status=None, stream=None)
+    a.update(kw)
+    return lib.dsa_indexer_scores(*a.values())
+
+
+def _dec(lib, **kw):
+    a = dict(q=FAKE, q_dtype=BF16, kv=FAKE, kv_scale=FAKE, kv_dtype=FP8, num_pages=10, page_size=64, bt=FAKE,
+             bt_stride=4, lens=FAKE, batch=2, max_len=256, indices=FAKE, k=2048, n_heads=128, d_latent=512,
+             d_rope=64, sm_scale=1 / 24, splits=1, o_part=FAKE, lse_part=FAKE, status=None, stream=None)
+    a.update(kw)
+    return lib.mla_paged_decode(*a.values())
+
+
+def test_indexer_rejects(lib):
+    assert _idx(lib, page_size=48) == EUNSUPPORTED
+    assert _idx(lib, q_dtype=FP8) == EUNSUPPORTED
+    assert _idx(lib, q_dtype=BF16, k_dtype=F32) == EUNSUPPORTED
+    assert _idx(lib, k_dtype=7) == EINVAL
+    assert _idx(lib, n_heads=129) == EUNSUPPORTED
+    assert _idx(lib, d=96) == EUNSUPPORTED
+    assert _idx(lib, q_dtype=BF16, d=16) == EUNSUPPORTED
+    assert _idx(lib, score_stride=255) == EINVAL
+    assert b"score_stride" in lib.spmla_last_error()
+    assert _idx(lib, q_idx=None) == EINVAL
+    assert _idx(lib, k_scale=None) == EINVAL
+    assert _idx(lib, k_pool=MIS) == EINVAL
+    assert _idx(lib, batch=-1) == EINVAL
+    assert _idx(lib, num_pages=0) == EINVAL
+    assert _idx(lib, max_len=-5) == EINVAL
+    assert _idx(lib, batch=0, q_idx=None, scores=None) == OK  # empty batch: nothing to do
+
+
+def test_topk_rejects(lib):
+    lib.topk_workspace_bytes.restype = ctypes.c_size_t
+    need = lib.topk_workspace_bytes(4, 1000, 2048)
+    assert need >= 4 * 1000 * 8
+    assert lib.topk_workspace_bytes(4, 1000, 5000) == 0
+    assert lib.topk_workspace_bytes(-1, 1000, 8) == 0
+    f = lib.topk_select
+    assert f(FAKE, 1000, FAKE, 4, 1000, 0, FAKE, FAKE, need, None, None) == EUNSUPPORTED
+    assert f(FAKE, 1000, FAKE, 4, 1000, 4097, FAKE, FAKE, need, None, None) == EUNSUPPORTED
+    assert f(FAKE, 999, FAKE, 4, 1000, 2048, FAKE, FAKE, need, None, None) == EINVAL
+    assert f(FAKE, 1000, FAKE, 4, 1000, 2048, FAKE, FAKE, need - 1, None, None) == EWORKSPACE
+    assert f(FAKE, 1000, FAKE, 4, 1000, 2048, FAKE, None, need, None, None) == EWORKSPACE
+    assert f(FAKE, 1000, FAKE, 4, 1000, 2048, FAKE, ctypes.c_void_p(0x1010), need, None, None) == EINVAL
+    assert f(None, 1000, FAKE, 4, 1000, 2048, FAKE, FAKE, need, None, None) == EINVAL
+    assert f(FAKE, 1000, FAKE, 4, 1000, 2048, FAKE, FAKE, 0, None, None) == EWORKSPACE
+    assert b"workspace" in lib.spmla_last_error()
+    assert f(None, 1000, None, 0, 1000, 2048, None, None, 0, None, None) == OK
+
+
+def test_decode_rejects(lib):
+    lib.mla_paged_decode.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                                     ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                     ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
+                                     ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                     ctypes.c_int32, ctypes.c_float, ctypes.c_int32, ctypes.c_void_p,
+                                     ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    assert _dec(lib, d_latent=256) == EUNSUPPORTED
+    assert _dec(lib, q_dtype=FP8) == EUNSUPPORTED
+    assert _dec(lib, kv_dtype=F32) == EUNSUPPORTED          # bf16 queries need a bf16/FP8 cache
+    assert _dec(lib, splits=0) == EUNSUPPORTED
+    assert _dec(lib, splits=65) == EUNSUPPORTED
+    assert _dec(lib, sm_scale=0.0) == EINVAL
+    assert _dec(lib, sm_scale=float("nan")) == EINVAL
+    assert _dec(lib, n_heads=0) == EUNSUPPORTED
+    assert _dec(lib, k=70000) == EUNSUPPORTED
+    assert _dec(lib, kv_scale=None) == EINVAL
+    assert _dec(lib, o_part=None) == EINVAL
+    assert _dec(lib, q=MIS) == EINVAL
+    assert _dec(lib, page_size=8) == EUNSUPPORTED
+    assert _dec(lib, bt=None) == EINVAL
+    assert _dec(lib, batch=0) == OK
+
+
+def test_merge_rejects(lib):
+    f = lib.lse_merge
+    assert f(FAKE, FAKE, 2, 0, 4, 512, FAKE, FAKE, None) == EUNSUPPORTED
+    assert f(FAKE, FAKE, 2, 65, 4, 512, FAKE, FAKE, None) == EUNSUPPORTED
+    assert f(FAKE, FAKE, 2, 4, 4, 510, FAKE, FAKE, None) == EUNSUPPORTED
+    assert f(None, FAKE, 2, 4, 4, 512, FAKE, FAKE, None) == EINVAL
+    assert f(FAKE, FAKE, 2, 4, 4, 512, MIS, FAKE, None) == EINVAL
+    assert f(FAKE, FAKE, -2, 4, 4, 512, FAKE, FAKE, None) == EINVAL
+    assert f(None, None, 0, 4, 4, 512, None, None, None) == OK

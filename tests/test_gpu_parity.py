@@ -1,0 +1,272 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on the
+same seeded inputs.  Stage by stage, so one stage's error cannot hide
+another's: indexer scores; top-k on the GPU's own scores; attention on the
+GPU-selected tokens; merge.  Tolerances are in tests/parity.py."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import spmla_gen as gen
+from spmla_gen.torch_io import device_batch, tensor
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+
+
+def _lib():
+    import sparse_paged_mla_amd as spm
+    spm.load_library()
+    return spm
+
+
+def _step(inp, splits=1):
+    from sparse_paged_mla_amd.step import DecodeStep
+    db = device_batch(inp)
+    st = DecodeStep(db, num_splits=splits)
+    st.run()
+    torch.cuda.synchronize()
+    return db, st
+
+
+def _check_full(inp, splits=1, what=""):
+    print(f"[parity] {what} B={inp.cfg.batch} lens={list(inp.lens[:8])} splits={splits}", flush=True)
+    cfg = inp.cfg
+    db, st = _step(inp, splits)
+    status = st.status.cpu().numpy()
+    assert not status.any(), status
+    idx = None
+    if not cfg.dense:
+        s_gpu = st.scores.cpu().numpy()
+        s_ref, mags, _ = oracle.indexer_scores(inp.q_idx, inp.w, inp.k_idx, inp.k_idx_scale, inp.block_table,
+                                               inp.lens, score_stride=inp.score_stride)
+        for b in range(cfg.batch):
+            L = inp.lens[b]
+            parity.check_scores(s_gpu[b, :L], s_ref[b, :L], mags[b, :L], f"{what} scores b={b}")
+        idx = st.idx.cpu().numpy()
+        parity.check_topk_exact(idx, s_gpu, inp.lens, cfg.topk, what)
+    o_ref, lse_ref, st_ref = oracle.mla_attention(inp.q, inp.kv, inp.kv_scale, inp.block_table, inp.lens, idx,
+                                                  cfg.n_heads, cfg.d_latent, cfg.d_rope, cfg.softmax_scale)
+    assert not st_ref.any()
+    parity.check_attention(st.o.cpu().numpy(), st.lse.cpu().numpy(), o_ref, lse_ref, what)
+    return db, st
+
+
+# ---------------------------------------------------------------- whole steps
+
+@pytest.mark.parametrize("splits", [1, 2, 3])
+def test_c1_tiny_full_step(splits):
+    _lib()
+    _check_full(gen.make_inputs("c1"), splits, "c1")
+
+
+def test_c1_dense_attention():
+    _lib()
+    inp = gen.make_inputs(gen.CONFIGS["c1"].with_(idx_heads=0, topk=0))
+    _check_full(inp, 2, "c1 dense")
+
+
+SMALL_SPARSE = [
+    ("bf16", gen.CONFIGS["c3"].with_(batch=3), [70, 1000, 5000]),
+    ("fp8", gen.CONFIGS["c3f"].with_(batch=4), [1, 300, 3000, 9000]),
+    ("fp8-p16", gen.CONFIGS["c4"].with_(batch=3, page_size=16, pool_factor=1.25), [2049, 17, 4100]),
+]
+
+
+@pytest.mark.parametrize("name,cfg,lens", SMALL_SPARSE, ids=[s[0] for s in SMALL_SPARSE])
+@pytest.mark.parametrize("splits", [1, 4])
+def test_small_sparse_step(name, cfg, lens, splits):
+    _lib()
+    _check_full(gen.make_inputs(cfg, lens=lens), splits, name)
+
+
+@pytest.mark.parametrize("splits", [1, 3, 8])
+def test_small_dense_bf16(splits):
+    _lib()
+    cfg = gen.CONFIGS["c2"].with_(batch=3)
+    _check_full(gen.make_inputs(cfg, lens=[33, 700, 2500]), splits, "dense bf16")
+
+
+def test_poisoned_tails_are_never_read():
+    _lib()
+    cfg = gen.CONFIGS["c3f"].with_(batch=3)
+    _check_full(gen.make_inputs(cfg, lens=[65, 2100, 3001], poison_tail=True), 2, "poisoned fp8")
+    cfg = gen.CONFIGS["c2"].with_(batch=2)
+    _check_full(gen.make_inputs(cfg, lens=[31, 1000], poison_tail=True), 3, "poisoned dense")
+
+
+# ----------------------------------------------------------------- top-k only
+
+def _gpu_topk(scores, lens, k):
+    spm = _lib()
+    B, stride = scores.shape
+    max_len = int(max(lens)) if len(lens) else 0
+    s = torch.from_numpy(np.ascontiguousarray(scores, np.float32)).cuda()
+    l = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    out = torch.full((B, k), -7, dtype=torch.int32, device="cuda")
+    ws = torch.empty(max(spm.topk_workspace_bytes(B, max_len, k), 256), dtype=torch.uint8, device="cuda")
+    st = torch.zeros(B, dtype=torch.int32, device="cuda")
+    spm.topk_select(s, l, max_len, k, out, ws, st)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), st.cpu().numpy()
+
+
+@pytest.mark.parametrize("k", [1, 32, 2048, 4096])
+def test_topk_ties_nan_negzero(k):
+    rng = np.random.default_rng(k)
+    lens = [0, 1, 31, 2048, 5000, 70000]
+    S = np.zeros((len(lens), 70016), np.float32)
+    S[:] = np.round(rng.standard_normal(S.shape) * 4).astype(np.float32)  # heavy ties
+    S[1, 0] = np.nan
+    S[2, :31] = np.where(rng.random(31) < 0.3, np.float32(-0.0), S[2, :31])
+    S[3, ::7] = np.nan
+    S[4, :] = 1.25                                                         # all equal
+    S[5, ::3] = -0.0
+    idx, st = _gpu_topk(S, lens, k)
+    assert not st.any()
+    parity.check_topk_exact(idx, S, np.array(lens), k, f"ties k={k}")
+
+
+def test_topk_large_continuous():
+    rng = np.random.default_rng(11)
+    lens = [300000, 131072, 2047, 2049]
+    S = rng.standard_normal((4, 300032)).astype(np.float32) * 30 + 144
+    idx, st = _gpu_topk(S, lens, 2048)
+    parity.check_topk_exact(idx, S, np.array(lens), 2048, "continuous")
+
+
+def test_topk_bad_len_flags_request():
+    S = np.random.default_rng(0).standard_normal((3, 256)).astype(np.float32)
+    spm = _lib()
+    s = torch.from_numpy(S).cuda()
+    l = torch.tensor([10, 300, -1], dtype=torch.int32, device="cuda")  # 300 > max_len 256, -1 < 0
+    out = torch.empty((3, 8), dtype=torch.int32, device="cuda")
+    ws = torch.empty(spm.topk_workspace_bytes(3, 256, 8), dtype=torch.uint8, device="cuda")
+    st = torch.zeros(3, dtype=torch.int32, device="cuda")
+    spm.topk_select(s, l, 256, 8, out, ws, st)
+    torch.cuda.synchronize()
+    assert list(st.cpu().numpy()) == [0, spm.BAD_LEN, spm.BAD_LEN]
+    o = out.cpu().numpy()
+    assert np.all(o[1:] == -1)
+    parity.check_topk_exact(o[:1], S[:1], np.array([10]), 8, "bad-len neighbour")
+
+
+# ------------------------------------------------------------ fault handling
+
+def test_device_faults_flag_only_the_offending_request():
+    spm = _lib()
+    cfg = gen.CONFIGS["c3f"].with_(batch=4)
+    inp = gen.make_inputs(cfg, lens=[500, 600, 700, 800])
+    bt = inp.block_table.copy()
+    bt[1, 2] = inp.num_pages + 5      # request 1: page id out of range
+    lens = inp.lens.copy()
+    lens[2] = bt.shape[1] * cfg.page_size + 1  # request 2: longer than its mapped pages
+    inp.block_table, inp.lens = bt, lens
+    inp.max_len = int(lens.max())
+    inp.score_stride = (inp.max_len + 63) // 64 * 64
+    from sparse_paged_mla_amd.step import DecodeStep
+    db = device_batch(inp)
+    st = DecodeStep(db, num_splits=2)
+    st.indexer()
+    st.select()
+    idx = st.idx.clone()
+    idx[3, 5] = 800                  # request 3: index == L
+    st.idx.copy_(idx)
+    st.attend()
+    st.merge()
+    torch.cuda.synchronize()
+    status = st.status.cpu().numpy()
+    assert status[0] == 0
+    assert status[1] & spm.BAD_PAGE
+    assert status[2] & spm.BAD_LEN
+    assert status[3] == spm.BAD_INDEX
+    o = st.o.cpu().numpy()
+    assert np.isnan(o[1]).all() and np.isnan(o[2]).all() and np.isnan(o[3]).all()
+    # Request 0 is untouched: compare with the oracle on its own selection.
+    s_gpu = st.scores.cpu().numpy()
+    parity.check_topk_exact(st.idx.cpu().numpy()[:1], s_gpu[:1], lens[:1], cfg.topk, "fault neighbour")
+    o_ref, lse_ref, _ = oracle.mla_attention(inp.q[:1], inp.kv, inp.kv_scale, bt[:1], lens[:1],
+                                             st.idx.cpu().numpy()[:1], cfg.n_heads, cfg.d_latent, cfg.d_rope,
+                                             cfg.softmax_scale)
+    parity.check_attention(o[:1], st.lse.cpu().numpy()[:1], o_ref, lse_ref, "fault neighbour")
+    _, _, st_ref = oracle.indexer_scores(inp.q_idx, inp.w, inp.k_idx, inp.k_idx_scale, bt, lens)
+    assert (st_ref[:3] == status[:3]).all()
+
+
+# ----------------------------------------------------------- metamorphic checks
+
+def test_page_permutation_and_determinism():
+    _lib()
+    cfg = gen.CONFIGS["c3f"].with_(batch=3)
+    a = gen.make_inputs(cfg, lens=[3000, 5000, 4097])
+    b = gen.make_inputs(cfg, lens=[3000, 5000, 4097], shuffle=False)
+    _, s1 = _step(a, 2)
+    _, s2 = _step(b, 2)
+    _, s3 = _step(a, 2)
+    for name in ("scores", "idx", "o", "lse"):
+        x1, x2, x3 = (getattr(s, name).cpu().numpy() for s in (s1, s2, s3))
+        if name == "scores":
+            x1, x2, x3 = (np.concatenate([x[i, :L] for i, L in enumerate(a.lens)]) for x in (x1, x2, x3))
+        assert np.array_equal(x1, x3), f"{name} not deterministic"
+        assert np.array_equal(x1, x2), f"{name} changes under a page permutation"
+
+
+# Different split boundaries change the running max each probability is taken
+# against before it is rounded to bf16 for the value contraction, so outputs
+# agree to the bf16 rounding of the weights (relative 2^-9 each), not bit for
+# bit: |do| <= 2^-8 * max|v| is the bound; 2e-3 is used.  lse is formed in
+# fp32 from unrounded weights.
+SPLIT_O_ATOL = 2e-3
+SPLIT_LSE_ATOL = 2e-5
+
+
+def test_splits_agree():
+    _lib()
+    cfg = gen.CONFIGS["c3f"].with_(batch=2)
+    inp = gen.make_inputs(cfg, lens=[6000, 9000])
+    outs = [_step(inp, s)[1] for s in (1, 2, 7, 32)]
+    for st in outs[1:]:
+        assert np.abs(st.o.cpu().numpy() - outs[0].o.cpu().numpy()).max() < SPLIT_O_ATOL
+        assert np.abs(st.lse.cpu().numpy() - outs[0].lse.cpu().numpy()).max() < SPLIT_LSE_ATOL
+        assert np.array_equal(st.idx.cpu().numpy(), outs[0].idx.cpu().numpy())
+
+
+def test_k_ge_len_equals_dense():
+    _lib()
+    cfg = gen.CONFIGS["c3"].with_(batch=2, topk=4096)
+    inp = gen.make_inputs(cfg, lens=[1000, 4096])
+    _, sp = _step(inp, 2)
+    dense = gen.make_inputs(cfg.with_(idx_heads=0, topk=0), lens=[1000, 4096])
+    _, dn = _step(dense, 2)
+    assert np.abs(sp.o.cpu().numpy() - dn.o.cpu().numpy()).max() < SPLIT_O_ATOL
+    assert np.abs(sp.lse.cpu().numpy() - dn.lse.cpu().numpy()).max() < SPLIT_LSE_ATOL
+    # With one split both paths attend the same tokens in the same order: bit-identical.
+    _, sp1 = _step(inp, 1)
+    _, dn1 = _step(dense, 1)
+    assert np.array_equal(sp1.o.cpu().numpy(), dn1.o.cpu().numpy())
+    assert np.array_equal(sp1.lse.cpu().numpy(), dn1.lse.cpu().numpy())
+
+
+# --------------------------------------------------------------- lse merge only
+
+def test_merge_matches_oracle_on_random_partials():
+    spm = _lib()
+    rng = np.random.default_rng(3)
+    B, S, H, d = 3, 5, 16, 512
+    op = rng.standard_normal((B, S, H, d)).astype(np.float32)
+    lp = (rng.standard_normal((B, S, H)) * 4).astype(np.float32)
+    lp[0, 1:, :] = -np.inf                 # only split 0 non-empty
+    lp[1, :, 3] = -np.inf                  # a fully empty row
+    lp[2, 2, 5] = np.nan                   # NaN propagates
+    o = torch.empty(B, H, d, device="cuda")
+    l = torch.empty(B, H, device="cuda")
+    spm.lse_merge(torch.from_numpy(op).cuda(), torch.from_numpy(lp).cuda(), o, l)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.lse_merge(op, lp)
+    og, lg = o.cpu().numpy(), l.cpu().numpy()
+    assert np.array_equal(np.isnan(lg), np.isnan(l_ref))
+    ok = ~np.isnan(l_ref)
+    assert np.array_equal(lg[ok] == -np.inf, l_ref[ok] == -np.inf)
+    fin = np.isfinite(l_ref)
+    assert np.abs(lg[fin] - l_ref[fin]).max() < 1e-5
+    assert np.abs(og[ok] - o_ref[ok]).max() < 1e-5
