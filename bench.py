@@ -5,8 +5,10 @@ One step = dsa_indexer_scores -> topk_select -> mla_paged_decode -> lse_merge
 HBM.  The default workload is the 64-request 32K-128K FP8 decode (c3f).
 
 Timing: W untimed warm-up steps, then exactly K timed steps.  Before each
-timed step a 512 MiB buffer is overwritten (outside the timed events) so the
-step starts with cold L2 and MALL.  Each kernel is bracketed by HIP events on
+timed step a 512 MiB buffer is read (outside the timed events) so the step
+starts with L2 and MALL holding unrelated clean lines, as after the other
+layers of a model.  (An overwriting flush would leave dirty lines whose
+write-back competes with the timed step.)  Each kernel is bracketed by HIP events on
 the stream it runs on; the step time is the sum of its kernels' spans (start
 of the first to end of the last).  `value` = requests / mean step time.
 A warm number (K steps back to back, no flush) is reported beside it.
@@ -140,12 +142,13 @@ def main():
     stages = ["indexer", "select", "attend", "merge"] if step.sparse else ["attend", "merge"]
     if splits == 1:
         stages.remove("merge")
-    flush_buf = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
+    flush_buf = torch.ones(512 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
+    flush_sink = torch.zeros((), dtype=torch.float32, device="cuda")
 
     def run_timed(flush):
         evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
         if flush:
-            flush_buf.fill_(1.0)
+            flush_sink.copy_(flush_buf.amax())
         evs[0].record()
         for i, name in enumerate(stages):
             getattr(step, name)()

@@ -18,6 +18,7 @@ typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
+typedef __bf16 v4bf16_t __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 
@@ -72,6 +73,14 @@ __device__ __forceinline__ void load_raw(const uint8_t* __restrict__ p, uint32_t
     static_assert(BYTES == 1, "unsupported raw width");
     out[0] = *p;
   }
+}
+
+typedef uint32_t u32x4_ev __attribute__((ext_vector_type(4)));
+
+// 16-byte streaming load that does not allocate in the caches (data read once).
+__device__ __forceinline__ void load_nt16(const uint8_t* __restrict__ p, uint32_t* out) {
+  const u32x4_ev v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_ev*>(p));
+  out[0] = v.x; out[1] = v.y; out[2] = v.z; out[3] = v.w;
 }
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }

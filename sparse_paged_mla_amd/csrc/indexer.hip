@@ -4,8 +4,13 @@
 // score(b, t) = sum_h w[b,h] * max(0, q_idx[b,h,:] . key(b,t)) (times the
 // token's FP8 scale, which is positive and so commutes with the ReLU).
 //
-// Work split: one workgroup (4 waves) per (request, chunk of kChunk tokens).
-// A wave scores 16 tokens per step: S[heads x 16 tokens] = Q[heads x d] .
+// Work split: one workgroup (4 waves) per (request, chunk of kIdxChunk
+// tokens); the chunk's page ids are resolved into LDS first, so the key loads
+// never wait on a block-table load.  Each wave streams 64 tokens per step with
+// fully coalesced 16-byte loads (one page of 64 FP8 keys is 8 KiB of
+// consecutive bytes), always one step ahead (two register buffers), and
+// transposes them into MFMA operand order through its own LDS rows.  The math
+// is done in 16-token sub-blocks: S[heads x 16 tokens] = Q[heads x d] .
 // K^T[d x 16 tokens] with the heads on the MFMA's M side (the query stays in
 // registers for the whole chunk) and the tokens on N, so each lane loads a
 // contiguous slice of one key row straight from HBM.  Because a dot product
@@ -19,7 +24,23 @@
 namespace spmla {
 
 constexpr int kIdxThreads = 256;
-constexpr int kIdxChunk = 4096;  // tokens per workgroup
+constexpr int kIdxChunk = 4096;         // tokens per workgroup
+constexpr int kIdxStepBytes = 8192;     // key bytes a wave fetches per step
+
+// Tokens a wave handles per step: 8 KiB of keys, at least one 16-token MFMA block.
+template <int ROW_BYTES>
+struct IdxStep {
+  static constexpr int tok = ROW_BYTES * 64 <= kIdxStepBytes ? 64 : ROW_BYTES * 32 <= kIdxStepBytes ? 32 : 16;
+};
+
+// Flat workgroup id -> logical id such that consecutive logical ids share an
+// XCD (the dispatcher deals workgroups round-robin over the 8 XCDs, each with
+// its own L2), so the chunks of one request reuse its query in one L2.
+__device__ __forceinline__ int xcd_remap(int bid, int n) {
+  const int q = n >> 3, r = n & 7;
+  const int xcd = bid & 7, slot = bid >> 3;
+  return xcd < r ? xcd * (q + 1) + slot : r * (q + 1) + (xcd - r) * q + slot;
+}
 
 template <class Op, int KDT, int KSTEPS, int MT>
 __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(
@@ -30,14 +51,29 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(
     int32_t chunks_per_req) {
   constexpr int KPL = Op::KPL;
   constexpr int D = KSTEPS * 4 * KPL;            // key dim
-  constexpr int GROUP_ELEMS = D / 4;             // contiguous elements a lane group loads
+  constexpr int GROUP_ELEMS = D / 4;             // contiguous elements a lane group owns
   constexpr int ROW_BYTES = D * Storage<KDT>::bytes;
   constexpr int GROUP_BYTES = GROUP_ELEMS * Storage<KDT>::bytes;
   constexpr int RAW_DW = (GROUP_BYTES + 3) / 4;
+  constexpr bool kBf = std::is_same<Op, OpBF16>::value;
+  constexpr int QE = kBf ? 2 : 4;                // query element bytes
+  constexpr int STEP_TOK = IdxStep<ROW_BYTES>::tok;  // tokens per wave step
+  constexpr int SUBS = STEP_TOK / 16;                // 16-token MFMA blocks per step
+  constexpr int WG_STEP = 4 * STEP_TOK;              // tokens per workgroup step
+  constexpr int STEP_BYTES = STEP_TOK * ROW_BYTES;
+  static_assert(ROW_BYTES % 16 == 0 && GROUP_BYTES % 4 == 0, "key rows must be whole 16-byte pieces");
+  constexpr int PIECES = STEP_BYTES / 16;        // 16-byte pieces per wave step
+  constexpr int LOADS = (PIECES + 63) / 64;      // coalesced 16-byte loads per lane per step
+  constexpr int ROW_PIECES = ROW_BYTES / 16;
+  constexpr int LROW = ROW_BYTES + 16;           // padded LDS row (conflict-free slice reads)
   const int page_size = 1 << page_shift;
 
-  const int b = blockIdx.x / chunks_per_req;
-  const int chunk = blockIdx.x % chunks_per_req;
+  __shared__ int32_t pg[kIdxChunk / 16 + 1];     // page ids of the chunk (-1: bad)
+  __shared__ __attribute__((aligned(16))) uint8_t stage[4][STEP_TOK * LROW];
+
+  const int logical = xcd_remap(blockIdx.x, gridDim.x);
+  const int b = logical / chunks_per_req;
+  const int chunk = logical % chunks_per_req;
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
   const int g = lane >> 4;
@@ -52,24 +88,31 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(
   if (t_begin >= L) return;
   const int64_t t_end = min((int64_t)L, t_begin + kIdxChunk);
 
-  // Query fragments (A operand: rows = heads), permuted like the key loads.
+  // Resolve the chunk's pages once (t_begin is a multiple of the page size).
+  const int64_t pg0 = t_begin >> page_shift;
+  const int n_pg = (int)(((t_end - 1) >> page_shift) - pg0 + 1);
+  bool flagged = false;
+  for (int i = threadIdx.x; i < n_pg; i += kIdxThreads) {
+    int32_t p = bt[(int64_t)b * bt_stride + pg0 + i];
+    if (p < 0 || p >= num_pages) {
+      p = -1;
+      flagged = true;
+    }
+    pg[i] = p;
+  }
+  if (flagged && status) atomicOr(status + b, kBadPage);
+
+  // Query fragments (A operand: rows = heads), permuted like the key slices.
   typename Op::frag qa[MT][KSTEPS];
   float wr[MT][4];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     const int h = mt * 16 + r16;
     if (h < n_heads) {
-      uint32_t raw[(GROUP_ELEMS * (std::is_same<Op, OpBF16>::value ? 2 : 4) + 3) / 4];
-      const uint8_t* qp = reinterpret_cast<const uint8_t*>(q_idx) +
-                          (((int64_t)b * n_heads + h) * D + g * GROUP_ELEMS) *
-                              (std::is_same<Op, OpBF16>::value ? 2 : 4);
-      if constexpr (std::is_same<Op, OpBF16>::value) {
-        load_raw<GROUP_ELEMS * 2>(qp, raw);
-        raw_to_frags<Op, kBF16, KSTEPS>(raw, qa[mt]);
-      } else {
-        load_raw<GROUP_ELEMS * 4>(qp, raw);
-        raw_to_frags<Op, kF32, KSTEPS>(raw, qa[mt]);
-      }
+      uint32_t raw[(GROUP_ELEMS * QE + 3) / 4];
+      const uint8_t* qp = reinterpret_cast<const uint8_t*>(q_idx) + (((int64_t)b * n_heads + h) * D + g * GROUP_ELEMS) * QE;
+      load_raw<GROUP_ELEMS * QE>(qp, raw);
+      raw_to_frags<Op, kBf ? kBF16 : kF32, KSTEPS>(raw, qa[mt]);
     } else {
 #pragma unroll
       for (int s = 0; s < KSTEPS; ++s) qa[mt][s] = zero_frag<Op>();
@@ -80,80 +123,102 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(
       wr[mt][i] = hh < n_heads ? w[(int64_t)b * n_heads + hh] : 0.f;
     }
   }
+  __syncthreads();  // pg[] ready
 
-  const int32_t* btb = bt + (int64_t)b * bt_stride;
   float* sc_out = scores + (int64_t)b * score_stride;
-  bool flagged = false;
+  uint8_t* my_stage = stage[wv];
 
-  // Per-lane token of a step; resolve its row (or -1 if masked, -2 if bad page).
-  auto row_of = [&](int64_t t0) -> int64_t {
-    const int64_t t = t0 + wv * 16 + r16;
+  // Row of token t of the chunk (>= 0), -1 past the end, -2 on a bad page.
+  auto row_of = [&](int64_t t) __attribute__((always_inline)) -> int64_t {
     if (t >= t_end) return -1;
-    const int32_t page = btb[t >> page_shift];
-    if (page < 0 || page >= num_pages) return -2;
+    const int32_t page = pg[(int)((t >> page_shift) - pg0)];
+    if (page < 0) return -2;
     return ((int64_t)page << page_shift) + (t & (page_size - 1));
   };
-  auto load_row = [&](int64_t row, uint32_t* raw) {
-    if (row >= 0) {
-      load_raw<GROUP_BYTES>(k_pool + row * ROW_BYTES + g * GROUP_BYTES, raw);
-    } else {
+
+  // A wave step covers tokens [t0 + STEP_TOK wv, +STEP_TOK).  Its key bytes are fetched as
+  // 16-byte pieces in token-major order, lane l taking piece 64 i + l of load
+  // i, so every load instruction reads 1 KiB of consecutive row bytes (a page
+  // is contiguous), with non-temporal loads since every key is read once per
+  // step.  The loads are unconditional (a piece past the end reads
+  // row 0, which always exists, and is never used), so the compiler can count
+  // them and keep the next step's loads in flight during this step's math.
+  uint32_t raw_a[LOADS][4], raw_b[LOADS][4];
+  float sc_a = 1.f, sc_b = 1.f;
+  auto issue = [&](int64_t t0, uint32_t (*raw)[4], float& sc) __attribute__((always_inline)) {
+    const int64_t tw = t0 + wv * STEP_TOK;
 #pragma unroll
-      for (int i = 0; i < RAW_DW; ++i) raw[i] = 0u;
+    for (int i = 0; i < LOADS; ++i) {
+      const int piece = min(i * 64 + lane, PIECES - 1);
+      const int64_t row = row_of(tw + piece / ROW_PIECES);
+      const int64_t safe = row >= 0 ? row : 0;
+      load_nt16(k_pool + safe * ROW_BYTES + (piece % ROW_PIECES) * 16, raw[i]);
+    }
+    if constexpr (KDT == kFP8) {
+      const int64_t row = row_of(tw + min(lane, STEP_TOK - 1));
+      sc = k_scale[row >= 0 ? row : 0];
     }
   };
-
-  int64_t row_cur = row_of(t_begin);
-  uint32_t raw_cur[RAW_DW];
-  load_row(row_cur, raw_cur);
-  float scale_cur = (KDT == kFP8 && row_cur >= 0) ? k_scale[row_cur] : 1.f;
-
-  for (int64_t t0 = t_begin; t0 < t_end; t0 += 64) {
-    // Prefetch the next step's row while this one is on the matrix cores.
-    const int64_t t0n = t0 + 64;
-    int64_t row_nxt = -1;
-    uint32_t raw_nxt[RAW_DW];
-    float scale_nxt = 1.f;
-    if (t0n < t_end) {
-      row_nxt = row_of(t0n);
-      load_row(row_nxt, raw_nxt);
-      if (KDT == kFP8 && row_nxt >= 0) scale_nxt = k_scale[row_nxt];
-    } else {
+  auto consume = [&](int64_t t0, const uint32_t (*raw)[4], float sc) __attribute__((always_inline)) {
+    const int64_t tw = t0 + wv * STEP_TOK;
+    // Transpose through the wave's own LDS rows (padded by 16 bytes).
 #pragma unroll
-      for (int i = 0; i < RAW_DW; ++i) raw_nxt[i] = 0u;
+    for (int i = 0; i < LOADS; ++i) {
+      const int piece = i * 64 + lane;
+      if (piece < PIECES)
+        *reinterpret_cast<uint4*>(my_stage + (piece / ROW_PIECES) * LROW + (piece % ROW_PIECES) * 16) =
+            make_uint4(raw[i][0], raw[i][1], raw[i][2], raw[i][3]);
     }
-
-    typename Op::frag kb[KSTEPS];
-    raw_to_frags<Op, KDT, KSTEPS>(raw_cur, kb);
-    f32x4 acc[MT];
+    __builtin_amdgcn_wave_barrier();
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < SUBS; ++j) {
+      const int tok = j * 16 + r16;  // token of this lane's MFMA column
+      uint32_t sl[RAW_DW];
+      const uint8_t* src = my_stage + tok * LROW + g * GROUP_BYTES;
 #pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) {
+      for (int x = 0; x < RAW_DW; x += 4) {
+        if (x + 4 <= RAW_DW) {
+          const uint4 v = *reinterpret_cast<const uint4*>(src + 4 * x);
+          sl[x] = v.x; sl[x + 1] = v.y; sl[x + 2] = v.z; sl[x + 3] = v.w;
+        } else {
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) acc[mt] = Op::mma(qa[mt][s], kb[s], acc[mt]);
-    }
-    float v = 0.f;
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) v += wr[mt][i] * fmaxf(acc[mt][i], 0.f);
-    }
-    v = wave_sum_xor16_32(v);
-    const int64_t t = t0 + wv * 16 + r16;
-    if (g == 0 && t < t_end) {
-      float outv = v * scale_cur;
-      if (row_cur == -2) {
-        outv = __uint_as_float(0x7FC00000u);
-        flagged = true;
+          for (int y = x; y < RAW_DW; ++y) sl[y] = *reinterpret_cast<const uint32_t*>(src + 4 * y);
+        }
       }
-      sc_out[t] = outv;
-    }
-    row_cur = row_nxt;
-    scale_cur = scale_nxt;
+      typename Op::frag kb[KSTEPS];
+      raw_to_frags<Op, KDT, KSTEPS>(sl, kb);
+      f32x4 acc[MT];
 #pragma unroll
-    for (int i = 0; i < RAW_DW; ++i) raw_cur[i] = raw_nxt[i];
+      for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[mt] = Op::mma(qa[mt][s], kb[s], acc[mt]);
+      }
+      float v = 0.f;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v += wr[mt][i] * fmaxf(acc[mt][i], 0.f);
+      }
+      v = wave_sum_xor16_32(v);
+      const float tsc = __shfl(sc, tok);
+      const int64_t t = tw + tok;
+      if (g == 0 && t < t_end) sc_out[t] = row_of(t) == -2 ? __uint_as_float(0x7FC00000u) : v * tsc;
+    }
+    __builtin_amdgcn_wave_barrier();
+  };
+
+  issue(t_begin, raw_a, sc_a);
+  for (int64_t t0 = t_begin; t0 < t_end; t0 += 2 * WG_STEP) {
+    // Issued unconditionally so that the wait before consume() only covers
+    // the older buffer.
+    issue(t0 + WG_STEP, raw_b, sc_b);
+    consume(t0, raw_a, sc_a);
+    if (t0 + WG_STEP >= t_end) break;
+    issue(t0 + 2 * WG_STEP, raw_a, sc_a);
+    consume(t0 + WG_STEP, raw_b, sc_b);
   }
-  if (flagged && status) atomicOr(status + b, kBadPage);
 }
 
 template <class Op, int KDT, int KSTEPS, int MT>

@@ -1,27 +1,30 @@
 // topk_select kernels: exact per-request Top-k by radix selection on an
-// order-preserving 32-bit key, with ties broken toward the lower token index.
+// order-preserving 32-bit key, ties broken toward the lower token index.
 //
-// Key: NaN -> 0 (below everything), -0.0 -> +0.0, then the usual sign-flip so
+// Key: NaN -> 0 (below everything), -0.0 -> +0.0, then the usual sign flip so
 // that unsigned order equals numeric order.  The selection is the k_eff best
 // entries under (key desc, index asc), a total order, so the result is unique
-// and does not depend on the order atomics land in.
+// whatever order atomics land in.
 //
-// Launches per call (all on the caller's stream):
-//  1. clear:  zero the per-request histogram and counters in the workspace.
-//  2. hist:   (request, chunk) workgroups histogram the top 11 key bits in LDS
-//             and add them into the request's global histogram.
-//  3. filter: every workgroup finds the bin b0 holding the k-th best key (a
-//             block scan of the 2048 bins), then streams its chunk again:
-//             keys in bins above b0 are selected outright (their index goes to
-//             the output row at an atomically reserved slot), keys in b0 go to
-//             a candidate list.  Atomics are aggregated per wave with ballot +
-//             mbcnt.
-//  4. finish: one workgroup per request resolves the candidates: two more
-//             histogram rounds over the low 21 key bits find the exact
-//             threshold key T; keys above T are taken, and among keys equal to
-//             T the lowest indices are taken (a radix select on the index when
-//             there are more ties than places).  The k_eff indices are then
-//             sorted ascending in LDS (bitonic) and written with -1 padding.
+// Launches per call (all on the caller's stream), over (request, chunk)
+// workgroups except the last:
+//  1. range:  each chunk's min and max key go to the workspace, and the chunk
+//             clears its share of the request's histogram and counters.
+//  2. hist:   every chunk folds the per-chunk ranges into the request's key
+//             range, picks the 11-bit digit that starts at the highest bit in
+//             which the request's keys differ (so the digit spreads whatever
+//             the score scale), histograms it in LDS and adds the histogram
+//             into the request's global one.
+//  3. filter: every chunk finds the bin b0 holding the k-th best key and
+//             streams its keys again: keys above b0 are selected outright,
+//             keys in b0 become candidates.  Both are compacted in LDS first,
+//             so each workgroup reserves its output range with one atomic.
+//  4. finish: one workgroup per request resolves the candidates in LDS
+//             (further 11-bit rounds on the remaining key bits, then on the
+//             token index for exact ties) and writes the k_eff indices in
+//             ascending order: they are set in an LDS bitmap over [0, L) and
+//             read back with a prefix popcount (bitonic sort when L exceeds
+//             the bitmap).
 #include "common.h"
 #include "launch.h"
 
@@ -30,39 +33,49 @@
 namespace spmla {
 
 constexpr int kTkThreads = 256;
-constexpr int kTkChunk = 4096;       // tokens per hist/filter workgroup
-constexpr int kBins0 = 2048;         // top 11 key bits
-constexpr int kFinThreads = 512;
+constexpr int kTkPer = 16;                       // keys per thread per chunk
+constexpr int kTkChunk = kTkThreads * kTkPer;    // 4096 keys per workgroup
+constexpr int kBins = 2048;
+constexpr int kFinThreads = 1024;
 constexpr int kMaxK = 4096;
-constexpr int kCtrlWords = 8;        // out_count, cand_count, pad
+constexpr int kCtrl = 8;                         // out_count, cand_count
+constexpr int kFinLdsWords = 32768;              // 128 KiB: candidates, then the bitmap
+constexpr int kCandLds = kFinLdsWords / 2;       // candidates that fit in LDS (uint2 each)
+constexpr int64_t kBitmapBits = (int64_t)kFinLdsWords * 32;
 
 struct TopkWs {
-  uint32_t* hist;   // [B, 2048]
-  uint32_t* ctrl;   // [B, 8]
+  uint32_t* hist;   // [B, kBins]
+  uint32_t* ctrl;   // [B, kCtrl]
+  uint2* range;     // [B, chunks] (min key, max key)
   uint2* cand;      // [B, cap] (key, index)
   int64_t cap;
+  int32_t chunks;
 };
 
 static inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+static inline int32_t n_chunks(int64_t max_len) { return (int32_t)std::max<int64_t>(1, (max_len + kTkChunk - 1) / kTkChunk); }
 
 size_t topk_workspace_size(int32_t batch, int64_t max_len, int32_t k) {
   (void)k;
   if (batch <= 0 || max_len < 0) return 0;
-  size_t hist = align_up((size_t)batch * kBins0 * 4, 256);
-  size_t ctrl = align_up((size_t)batch * kCtrlWords * 4, 256);
-  size_t cand = align_up((size_t)batch * (size_t)(max_len > 0 ? max_len : 1) * 8, 256);
-  return hist + ctrl + cand;
+  const size_t b = (size_t)batch;
+  return align_up(b * kBins * 4, 256) + align_up(b * kCtrl * 4, 256) + align_up(b * n_chunks(max_len) * 8, 256) +
+         align_up(b * (size_t)std::max<int64_t>(max_len, 1) * 8, 256);
 }
 
 static TopkWs carve(void* ws, int32_t batch, int64_t max_len) {
   TopkWs w;
+  const size_t b = (size_t)batch;
   uint8_t* p = reinterpret_cast<uint8_t*>(ws);
+  w.chunks = n_chunks(max_len);
   w.hist = reinterpret_cast<uint32_t*>(p);
-  p += align_up((size_t)batch * kBins0 * 4, 256);
+  p += align_up(b * kBins * 4, 256);
   w.ctrl = reinterpret_cast<uint32_t*>(p);
-  p += align_up((size_t)batch * kCtrlWords * 4, 256);
+  p += align_up(b * kCtrl * 4, 256);
+  w.range = reinterpret_cast<uint2*>(p);
+  p += align_up(b * w.chunks * 8, 256);
   w.cand = reinterpret_cast<uint2*>(p);
-  w.cap = max_len > 0 ? max_len : 1;
+  w.cap = std::max<int64_t>(max_len, 1);
   return w;
 }
 
@@ -75,175 +88,265 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 
 __device__ __forceinline__ bool len_ok(int32_t L, int64_t max_len) { return L >= 0 && (int64_t)L <= max_len; }
 
-__global__ void topk_clear_kernel(uint32_t* __restrict__ hist, uint32_t* __restrict__ ctrl, int64_t n_hist,
-                                  int64_t n_ctrl) {
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_hist; i += stride) hist[i] = 0u;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_ctrl; i += stride) ctrl[i] = 0u;
+__device__ __forceinline__ int xcd_remap(int bid, int n) {
+  const int q = n >> 3, r = n & 7;
+  const int xcd = bid & 7, slot = bid >> 3;
+  return xcd < r ? xcd * (q + 1) + slot : r * (q + 1) + (xcd - r) * q + slot;
+}
+
+// Block reduction helpers (any block size that is a multiple of 64).
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  for (int o = 32; o > 0; o >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, o));
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o));
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+  const int lane = threadIdx.x & 63;
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t t = (uint32_t)__shfl_up((int)v, o);
+    if (lane >= o) v += t;
+  }
+  return v;
+}
+// Inclusive block scan; `tmp` holds one word per wave.  Contains barriers.
+template <int NT>
+__device__ __forceinline__ uint32_t block_incl_scan(uint32_t v, uint32_t* tmp) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  v = wave_incl_scan(v);
+  if (lane == 63) tmp[wid] = v;
+  __syncthreads();
+  uint32_t pre = 0;
+  for (int i = 0; i < wid; ++i) pre += tmp[i];
+  __syncthreads();
+  return v + pre;
+}
+
+// The digit that starts at the highest bit where the request's keys differ.
+__device__ __forceinline__ int digit_shift(uint32_t kmin, uint32_t kmax) {
+  const uint32_t diff = kmin ^ kmax;
+  const int hb = diff ? 31 - __clz(diff) : 0;
+  return max(hb + 1 - 11, 0);
+}
+
+__device__ __forceinline__ void request_range(const uint2* rng, int n, uint32_t* s_mm) {
+  // Called by all threads; result in s_mm[0..1] after the trailing barrier.
+  uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+  for (int i = threadIdx.x; i < n; i += blockDim.x) {
+    const uint2 r = rng[i];
+    lo = min(lo, r.x);
+    hi = max(hi, r.y);
+  }
+  lo = wave_min_u32(lo);
+  hi = wave_max_u32(hi);
+  if (threadIdx.x == 0) { s_mm[0] = 0xFFFFFFFFu; s_mm[1] = 0u; }
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) { atomicMin(&s_mm[0], lo); atomicMax(&s_mm[1], hi); }
+  __syncthreads();
+}
+
+// Thread-to-key mapping of a chunk: key j of thread tid is t0 + j*256 + tid
+// (coalesced loads, all issued before any use).
+__device__ __forceinline__ void load_chunk(const float* s, int64_t t0, int64_t t1, uint32_t* key, bool* in) {
+  float v[kTkPer];
+#pragma unroll
+  for (int j = 0; j < kTkPer; ++j) {
+    const int64_t t = t0 + (int64_t)j * kTkThreads + threadIdx.x;
+    in[j] = t < t1;
+    v[j] = s[in[j] ? t : t1 - 1];  // unconditional load (t1 - 1 is in range)
+  }
+#pragma unroll
+  for (int j = 0; j < kTkPer; ++j) key[j] = order_key(v[j]);
+}
+
+__global__ __launch_bounds__(kTkThreads) void topk_range_kernel(const float* __restrict__ scores, int64_t stride,
+                                                                const int32_t* __restrict__ lens, int64_t max_len,
+                                                                int32_t k, TopkWs ws) {
+  __shared__ uint32_t s_mm[2];
+  const int logical = xcd_remap(blockIdx.x, gridDim.x);
+  const int b = logical / ws.chunks, chunk = logical % ws.chunks;
+  const int32_t L = lens[b];
+  if (!len_ok(L, max_len) || L <= k) return;
+  const int n_act = (int)((L + kTkChunk - 1) / kTkChunk);
+  if (chunk >= n_act) return;
+  // This chunk's share of the request's histogram (and the counters, chunk 0).
+  const int per = (kBins + n_act - 1) / n_act;
+  for (int i = chunk * per + threadIdx.x; i < min(kBins, (chunk + 1) * per); i += kTkThreads)
+    ws.hist[(int64_t)b * kBins + i] = 0u;
+  if (chunk == 0 && threadIdx.x < kCtrl) ws.ctrl[(int64_t)b * kCtrl + threadIdx.x] = 0u;
+  const int64_t t0 = (int64_t)chunk * kTkChunk, t1 = min((int64_t)L, t0 + kTkChunk);
+  uint32_t key[kTkPer];
+  bool in[kTkPer];
+  load_chunk(scores + (int64_t)b * stride, t0, t1, key, in);
+  uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+#pragma unroll
+  for (int j = 0; j < kTkPer; ++j) {
+    if (in[j]) { lo = min(lo, key[j]); hi = max(hi, key[j]); }
+  }
+  lo = wave_min_u32(lo);
+  hi = wave_max_u32(hi);
+  if (threadIdx.x == 0) { s_mm[0] = 0xFFFFFFFFu; s_mm[1] = 0u; }
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) { atomicMin(&s_mm[0], lo); atomicMax(&s_mm[1], hi); }
+  __syncthreads();
+  if (threadIdx.x == 0) ws.range[(int64_t)b * ws.chunks + chunk] = make_uint2(s_mm[0], s_mm[1]);
 }
 
 __global__ __launch_bounds__(kTkThreads) void topk_hist_kernel(const float* __restrict__ scores, int64_t stride,
                                                                const int32_t* __restrict__ lens, int64_t max_len,
-                                                               int32_t k, uint32_t* __restrict__ ghist,
-                                                               int32_t chunks_per_req) {
-  __shared__ uint32_t h[kBins0];
-  const int b = blockIdx.x / chunks_per_req;
-  const int chunk = blockIdx.x % chunks_per_req;
+                                                               int32_t k, TopkWs ws) {
+  __shared__ uint32_t h[kBins];
+  __shared__ uint32_t s_mm[2];
+  const int logical = xcd_remap(blockIdx.x, gridDim.x);
+  const int b = logical / ws.chunks, chunk = logical % ws.chunks;
   const int32_t L = lens[b];
   if (!len_ok(L, max_len) || L <= k) return;
-  const int64_t t0 = (int64_t)chunk * kTkChunk;
-  if (t0 >= L) return;
-  const int64_t t1 = min((int64_t)L, t0 + kTkChunk);
-  for (int i = threadIdx.x; i < kBins0; i += kTkThreads) h[i] = 0u;
+  const int n_act = (int)((L + kTkChunk - 1) / kTkChunk);
+  if (chunk >= n_act) return;
+  const int64_t t0 = (int64_t)chunk * kTkChunk, t1 = min((int64_t)L, t0 + kTkChunk);
+  uint32_t key[kTkPer];
+  bool in[kTkPer];
+  load_chunk(scores + (int64_t)b * stride, t0, t1, key, in);
+  for (int i = threadIdx.x; i < kBins; i += kTkThreads) h[i] = 0u;
+  request_range(ws.range + (int64_t)b * ws.chunks, n_act, s_mm);
+  const int sh = digit_shift(s_mm[0], s_mm[1]);
+#pragma unroll
+  for (int j = 0; j < kTkPer; ++j)
+    if (in[j]) atomicAdd(&h[(key[j] >> sh) & (kBins - 1)], 1u);
   __syncthreads();
-  const float* s = scores + (int64_t)b * stride;
-  for (int64_t t = t0 + threadIdx.x; t < t1; t += kTkThreads) atomicAdd(&h[order_key(s[t]) >> 21], 1u);
-  __syncthreads();
-  uint32_t* gh = ghist + (int64_t)b * kBins0;
-  for (int i = threadIdx.x; i < kBins0; i += kTkThreads) {
+  uint32_t* gh = ws.hist + (int64_t)b * kBins;
+  for (int i = threadIdx.x; i < kBins; i += kTkThreads) {
     const uint32_t c = h[i];
     if (c) atomicAdd(gh + i, c);
   }
 }
 
-// Block-wide search over a histogram in LDS, from the top bin down: returns the
-// bin x with sum_{y > x} h[y] < need <= sum_{y >= x} h[y], and that "above"
-// count.  NB must be a multiple of the block size; `red` is scratch of
-// blockDim.x words; `out` two words.  need >= 1 and <= total is required.
+// Block-wide search over a histogram in LDS from the top bin down: the bin x
+// with sum_{y > x} h[y] < need <= sum_{y >= x} h[y], and that sum above.
+// NB a multiple of NT; need in [1, total].  Result in out[0..1]; barriers inside.
 template <int NB, int NT>
-__device__ void find_bin_desc(const uint32_t* h, uint32_t need, uint32_t* red, uint32_t* out) {
+__device__ void find_bin_desc(const uint32_t* h, uint32_t need, uint32_t* tmp, uint32_t* out) {
   constexpr int PER = NB / NT;
   const int tid = threadIdx.x;
-  if (tid == 0) { out[0] = 0u; out[1] = 0u; }
-  // Thread tid owns bins [NB - (tid+1)*PER, NB - tid*PER): thread 0 owns the top.
-  const int hi = NB - tid * PER;
+  const int hi = NB - tid * PER;  // thread 0 owns the top PER bins
   uint32_t mine = 0;
 #pragma unroll
   for (int j = 1; j <= PER; ++j) mine += h[hi - j];
-  red[tid] = mine;
-  __syncthreads();
-  // Inclusive scan over threads (Hillis-Steele in LDS).
-  for (int off = 1; off < NT; off <<= 1) {
-    uint32_t v = tid >= off ? red[tid - off] : 0u;
-    __syncthreads();
-    red[tid] += v;
-    __syncthreads();
-  }
-  const uint32_t incl = red[tid];
+  if (tid == 0) { out[0] = 0u; out[1] = 0u; }
+  const uint32_t incl = block_incl_scan<NT>(mine, tmp);
   const uint32_t excl = incl - mine;
   if (excl < need && need <= incl) {
     uint32_t run = excl;
     for (int j = 1; j <= PER; ++j) {
       const uint32_t c = h[hi - j];
-      if (run + c >= need) {
-        out[0] = (uint32_t)(hi - j);
-        out[1] = run;
-        break;
-      }
+      if (run + c >= need) { out[0] = (uint32_t)(hi - j); out[1] = run; break; }
       run += c;
     }
   }
   __syncthreads();
 }
 
-// Same, from the lowest bin up (used to take the smallest indices).
+// Same from the lowest bin up (smallest indices first).
 template <int NB, int NT>
-__device__ void find_bin_asc(const uint32_t* h, uint32_t need, uint32_t* red, uint32_t* out) {
+__device__ void find_bin_asc(const uint32_t* h, uint32_t need, uint32_t* tmp, uint32_t* out) {
   constexpr int PER = NB / NT;
   const int tid = threadIdx.x;
-  if (tid == 0) { out[0] = 0u; out[1] = 0u; }
   const int lo = tid * PER;
   uint32_t mine = 0;
 #pragma unroll
   for (int j = 0; j < PER; ++j) mine += h[lo + j];
-  red[tid] = mine;
-  __syncthreads();
-  for (int off = 1; off < NT; off <<= 1) {
-    uint32_t v = tid >= off ? red[tid - off] : 0u;
-    __syncthreads();
-    red[tid] += v;
-    __syncthreads();
-  }
-  const uint32_t incl = red[tid];
+  if (tid == 0) { out[0] = 0u; out[1] = 0u; }
+  const uint32_t incl = block_incl_scan<NT>(mine, tmp);
   const uint32_t excl = incl - mine;
   if (excl < need && need <= incl) {
     uint32_t run = excl;
     for (int j = 0; j < PER; ++j) {
       const uint32_t c = h[lo + j];
-      if (run + c >= need) {
-        out[0] = (uint32_t)(lo + j);
-        out[1] = run;
-        break;
-      }
+      if (run + c >= need) { out[0] = (uint32_t)(lo + j); out[1] = run; break; }
       run += c;
     }
   }
   __syncthreads();
 }
 
-// Wave-aggregated append: lanes with `pred` get consecutive slots starting at
-// a base reserved with one atomic per wave.  Returns the lane's slot.
-__device__ __forceinline__ uint32_t wave_append(bool pred, uint32_t* counter) {
+// Rank of this lane among the lanes of its wave with pred set, and the count.
+__device__ __forceinline__ uint32_t wave_rank(bool pred, uint32_t* count) {
   const uint64_t mask = __ballot(pred);
-  if (mask == 0) return 0u;
-  const uint32_t lane_rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
-                                                       __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
-  const int leader = __ffsll((long long)mask) - 1;
-  uint32_t base = 0;
-  if ((int)(threadIdx.x & 63) == leader) base = atomicAdd(counter, (uint32_t)__popcll(mask));
-  base = __shfl(base, leader);
-  return base + lane_rank;
+  *count = (uint32_t)__popcll(mask);
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
-__global__ __launch_bounds__(kTkThreads) void topk_filter_kernel(
-    const float* __restrict__ scores, int64_t stride, const int32_t* __restrict__ lens, int64_t max_len, int32_t k,
-    const uint32_t* __restrict__ ghist, uint32_t* __restrict__ ctrl, uint2* __restrict__ cand, int64_t cap,
-    int32_t* __restrict__ out_idx, int32_t chunks_per_req) {
-  __shared__ uint32_t h[kBins0];
-  __shared__ uint32_t red[kTkThreads];
+__global__ __launch_bounds__(kTkThreads) void topk_filter_kernel(const float* __restrict__ scores, int64_t stride,
+                                                                 const int32_t* __restrict__ lens, int64_t max_len,
+                                                                 int32_t k, TopkWs ws, int32_t* __restrict__ out_idx) {
+  __shared__ uint32_t h[kBins];
+  __shared__ uint32_t tmp[kTkThreads / 64];
   __shared__ uint32_t res[2];
-  const int b = blockIdx.x / chunks_per_req;
-  const int chunk = blockIdx.x % chunks_per_req;
+  __shared__ uint32_t s_mm[2];
+  __shared__ uint32_t n_sel, n_cnd, base_sel, base_cnd;
+  __shared__ int32_t sel_buf[kTkChunk];
+  __shared__ uint2 cnd_buf[kTkChunk];
+  const int logical = xcd_remap(blockIdx.x, gridDim.x);
+  const int b = logical / ws.chunks, chunk = logical % ws.chunks;
   const int32_t L = lens[b];
   if (!len_ok(L, max_len) || L <= k) return;
-  const int64_t t0 = (int64_t)chunk * kTkChunk;
-  if (t0 >= L) return;
-  const int64_t t1 = min((int64_t)L, t0 + kTkChunk);
-  const uint32_t* gh = ghist + (int64_t)b * kBins0;
-  for (int i = threadIdx.x; i < kBins0; i += kTkThreads) h[i] = gh[i];
-  __syncthreads();
-  find_bin_desc<kBins0, kTkThreads>(h, (uint32_t)k, red, res);
+  const int n_act = (int)((L + kTkChunk - 1) / kTkChunk);
+  if (chunk >= n_act) return;
+  const int64_t t0 = (int64_t)chunk * kTkChunk, t1 = min((int64_t)L, t0 + kTkChunk);
+  uint32_t key[kTkPer];
+  bool in[kTkPer];
+  load_chunk(scores + (int64_t)b * stride, t0, t1, key, in);
+  const uint32_t* gh = ws.hist + (int64_t)b * kBins;
+  for (int i = threadIdx.x; i < kBins; i += kTkThreads) h[i] = gh[i];
+  if (threadIdx.x == 0) { n_sel = 0u; n_cnd = 0u; }
+  request_range(ws.range + (int64_t)b * ws.chunks, n_act, s_mm);
+  const int sh = digit_shift(s_mm[0], s_mm[1]);
+  find_bin_desc<kBins, kTkThreads>(h, (uint32_t)k, tmp, res);
   const uint32_t b0 = res[0];
-  const float* s = scores + (int64_t)b * stride;
-  uint32_t* c = ctrl + (int64_t)b * kCtrlWords;
-  int32_t* out = out_idx + (int64_t)b * k;
-  uint2* cb = cand + (int64_t)b * cap;
-  // Every lane runs the same trip count so the wave-wide ballots stay uniform.
-  for (int64_t base = t0; base < t1; base += kTkThreads) {
-    const int64_t t = base + threadIdx.x;
-    const bool in = t < t1;
-    const uint32_t key = in ? order_key(s[t]) : 0u;
-    const uint32_t bin = key >> 21;
-    const bool sel = in && bin > b0;
-    const bool cnd = in && bin == b0;
-    const uint32_t ps = wave_append(sel, c + 0);
-    if (sel) out[ps] = (int32_t)t;
-    const uint32_t pc = wave_append(cnd, c + 1);
-    if (cnd) cb[pc] = make_uint2(key, (uint32_t)t);
+  // Compact this chunk's selected and candidate keys in LDS (one LDS atomic per wave each).
+#pragma unroll
+  for (int j = 0; j < kTkPer; ++j) {
+    const uint32_t d = (key[j] >> sh) & (kBins - 1);
+    const bool sel = in[j] && d > b0;
+    const bool cnd = in[j] && d == b0;
+    uint32_t cs, cc;
+    const uint32_t rs = wave_rank(sel, &cs);
+    const uint32_t rc = wave_rank(cnd, &cc);
+    uint32_t bs = 0, bc = 0;
+    if ((threadIdx.x & 63) == 0) {
+      if (cs) bs = atomicAdd(&n_sel, cs);
+      if (cc) bc = atomicAdd(&n_cnd, cc);
+    }
+    bs = (uint32_t)__shfl((int)bs, 0);
+    bc = (uint32_t)__shfl((int)bc, 0);
+    const int64_t t = t0 + (int64_t)j * kTkThreads + threadIdx.x;
+    if (sel) sel_buf[bs + rs] = (int32_t)t;
+    if (cnd) cnd_buf[bc + rc] = make_uint2(key[j], (uint32_t)t);
   }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    base_sel = n_sel ? atomicAdd(ws.ctrl + (int64_t)b * kCtrl + 0, n_sel) : 0u;
+    base_cnd = n_cnd ? atomicAdd(ws.ctrl + (int64_t)b * kCtrl + 1, n_cnd) : 0u;
+  }
+  __syncthreads();
+  int32_t* out = out_idx + (int64_t)b * k;
+  uint2* cb = ws.cand + (int64_t)b * ws.cap;
+  for (uint32_t i = threadIdx.x; i < n_sel; i += kTkThreads) out[base_sel + i] = sel_buf[i];
+  for (uint32_t i = threadIdx.x; i < n_cnd; i += kTkThreads) cb[base_cnd + i] = cnd_buf[i];
 }
 
 __global__ __launch_bounds__(kFinThreads) void topk_finish_kernel(const int32_t* __restrict__ lens, int64_t max_len,
-                                                                  int32_t k, const uint32_t* __restrict__ ghist,
-                                                                  const uint32_t* __restrict__ ctrl,
-                                                                  const uint2* __restrict__ cand, int64_t cap,
-                                                                  int32_t* __restrict__ out_idx,
+                                                                  int32_t k, TopkWs ws, int32_t* __restrict__ out_idx,
                                                                   int32_t* __restrict__ status) {
-  __shared__ uint32_t h[kBins0];
-  __shared__ uint32_t red[kFinThreads];
+  __shared__ uint32_t big[kFinLdsWords];   // candidates (uint2), later the bitmap
+  __shared__ uint32_t h[kBins];
+  __shared__ int32_t sel[kMaxK];
+  __shared__ uint32_t tmp[kFinThreads / 64];
   __shared__ uint32_t res[2];
+  __shared__ uint32_t s_mm[2];
   __shared__ uint32_t cnt;
-  __shared__ int32_t sorted[kMaxK];
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
   const int32_t L = lens[b];
@@ -257,115 +360,148 @@ __global__ __launch_bounds__(kFinThreads) void topk_finish_kernel(const int32_t*
     for (int j = tid; j < k; j += kFinThreads) out[j] = j < L ? j : -1;
     return;
   }
-  // Threshold bin of the top 11 bits (as the filter pass found it).
-  const uint32_t* gh = ghist + (int64_t)b * kBins0;
-  for (int i = tid; i < kBins0; i += kFinThreads) h[i] = gh[i];
+  const int n_act = (int)((L + kTkChunk - 1) / kTkChunk);
+  request_range(ws.range + (int64_t)b * ws.chunks, n_act, s_mm);
+  const int sh = digit_shift(s_mm[0], s_mm[1]);
+  const uint32_t* gh = ws.hist + (int64_t)b * kBins;
+  for (int i = tid; i < kBins; i += kFinThreads) h[i] = gh[i];
   __syncthreads();
-  find_bin_desc<kBins0, kFinThreads>(h, (uint32_t)k, red, res);
-  const uint32_t b0 = res[0];
-  const uint32_t n_gt = ctrl[(int64_t)b * kCtrlWords + 0];
-  const uint32_t n_c = ctrl[(int64_t)b * kCtrlWords + 1];
-  const uint2* cb = cand + (int64_t)b * cap;
-  uint32_t need = (uint32_t)k - n_gt;  // >= 1 places left for keys in bin b0
-
-  // Round 1: key bits 20..10 among the candidates.
-  for (int i = tid; i < kBins0; i += kFinThreads) h[i] = 0u;
-  __syncthreads();
-  for (uint32_t j = tid; j < n_c; j += kFinThreads) atomicAdd(&h[(cb[j].x >> 10) & 0x7FFu], 1u);
-  __syncthreads();
-  find_bin_desc<kBins0, kFinThreads>(h, need, red, res);
-  const uint32_t d1 = res[0];
-  need -= res[1];
-  // Round 2: key bits 9..0 among candidates in bin d1.
-  for (int i = tid; i < kBins0; i += kFinThreads) h[i] = 0u;
-  __syncthreads();
-  for (uint32_t j = tid; j < n_c; j += kFinThreads) {
-    const uint32_t key = cb[j].x;
-    if (((key >> 10) & 0x7FFu) == d1) atomicAdd(&h[key & 0x3FFu], 1u);
+  find_bin_desc<kBins, kFinThreads>(h, (uint32_t)k, tmp, res);
+  const uint32_t n_gt = ws.ctrl[(int64_t)b * kCtrl + 0];
+  const uint32_t n_c = ws.ctrl[(int64_t)b * kCtrl + 1];
+  // Candidates: in LDS when they fit, else read from the workspace.
+  const uint2* cb = ws.cand + (int64_t)b * ws.cap;
+  uint2* lc = reinterpret_cast<uint2*>(big);
+  const bool in_lds = n_c <= (uint32_t)kCandLds;
+  if (in_lds) {
+    for (uint32_t j = tid; j < n_c; j += kFinThreads) lc[j] = cb[j];
+    cb = lc;
   }
   __syncthreads();
-  find_bin_desc<1024, kFinThreads>(h, need, red, res);
-  const uint32_t d2 = res[0];
-  need -= res[1];
-  const uint32_t T = (b0 << 21) | (d1 << 10) | d2;
-  const uint32_t n_eq = h[d2];
-  __syncthreads();
-
-  // Among keys equal to T take the `need` lowest indices: find the index
-  // threshold I (inclusive) by a 3-round radix select from the low end.
-  uint32_t I = 0xFFFFFFFFu;
-  if (n_eq > need) {
-    uint32_t prefix = 0, pmask = 0;
-    const int shifts[3] = {22, 11, 0};
-    const uint32_t widths[3] = {0x1FFu, 0x7FFu, 0x7FFu};
-    uint32_t need_i = need;
-    for (int r = 0; r < 3; ++r) {
-      for (int i = tid; i < kBins0; i += kFinThreads) h[i] = 0u;
-      __syncthreads();
-      for (uint32_t j = tid; j < n_c; j += kFinThreads) {
-        const uint2 e = cb[j];
-        if (e.x == T && (e.y & pmask) == prefix) atomicAdd(&h[(e.y >> shifts[r]) & widths[r]], 1u);
-      }
-      __syncthreads();
-      find_bin_asc<kBins0, kFinThreads>(h, need_i, red, res);
-      prefix |= res[0] << shifts[r];
-      pmask |= widths[r] << shifts[r];
-      need_i -= res[1];
+  uint32_t need = (uint32_t)k - n_gt;  // >= 1 places for keys of bin b0
+  // Key rounds over the bits below the first digit, 11 at a time.
+  uint32_t kpre = 0, kmask = 0;  // determined low-bit prefix
+  for (int hi = sh; hi > 0; hi -= 11) {
+    const int lo = max(hi - 11, 0);
+    const uint32_t wmask = (1u << (hi - lo)) - 1u;
+    for (int i = tid; i < kBins; i += kFinThreads) h[i] = 0u;
+    __syncthreads();
+    for (uint32_t j = tid; j < n_c; j += kFinThreads) {
+      const uint32_t key = cb[j].x;
+      if ((key & kmask) == kpre) atomicAdd(&h[(key >> lo) & wmask], 1u);
     }
-    I = prefix;
+    __syncthreads();
+    find_bin_desc<kBins, kFinThreads>(h, need, tmp, res);
+    kpre |= res[0] << lo;
+    kmask |= wmask << lo;
+    need -= res[1];
   }
-
-  // Gather: the n_gt indices already in the output row, plus the resolved candidates.
+  // Threshold key T: candidates share bits >= sh (they are all in bin b0 of a
+  // request whose keys agree above the digit); the low bits are kpre.
+  // Among keys equal to T take the `need` lowest indices (index threshold I, inclusive).
+  uint32_t I = 0xFFFFFFFFu;
+  {
+    for (int i = tid; i < kBins; i += kFinThreads) h[i] = 0u;
+    __syncthreads();
+    uint32_t n_eq_local = 0;
+    for (uint32_t j = tid; j < n_c; j += kFinThreads) n_eq_local += ((cb[j].x & kmask) == kpre) ? 1u : 0u;
+    const uint32_t n_eq = block_incl_scan<kFinThreads>(n_eq_local, tmp);  // last thread holds the total
+    if (tid == kFinThreads - 1) res[0] = n_eq;
+    __syncthreads();
+    const uint32_t total_eq = res[0];
+    __syncthreads();
+    if (total_eq > need) {
+      uint32_t ipre = 0, imask = 0;
+      for (int hi = 31; hi > 0; hi -= 11) {
+        const int lo = max(hi - 11, 0);
+        const uint32_t wmask = (1u << (hi - lo)) - 1u;
+        for (int i = tid; i < kBins; i += kFinThreads) h[i] = 0u;
+        __syncthreads();
+        for (uint32_t j = tid; j < n_c; j += kFinThreads) {
+          const uint2 e = cb[j];
+          if ((e.x & kmask) == kpre && (e.y & imask) == ipre) atomicAdd(&h[(e.y >> lo) & wmask], 1u);
+        }
+        __syncthreads();
+        find_bin_asc<kBins, kFinThreads>(h, need, tmp, res);
+        ipre |= res[0] << lo;
+        imask |= wmask << lo;
+        need -= res[1];
+      }
+      I = ipre;
+    }
+  }
+  // Gather the k indices: the n_gt already in the output row plus the chosen candidates.
   if (tid == 0) cnt = n_gt;
-  for (uint32_t j = tid; j < n_gt; j += kFinThreads) sorted[j] = out[j];
+  for (uint32_t j = tid; j < n_gt; j += kFinThreads) sel[j] = out[j];
   __syncthreads();
   for (uint32_t j = tid; j < n_c; j += kFinThreads) {
     const uint2 e = cb[j];
-    if (e.x > T || (e.x == T && e.y <= I)) {
+    const uint32_t low = e.x & kmask;
+    if (low > kpre || (low == kpre && e.y <= I)) {
       const uint32_t p = atomicAdd(&cnt, 1u);
-      if (p < (uint32_t)k) sorted[p] = (int32_t)e.y;
+      if (p < (uint32_t)k) sel[p] = (int32_t)e.y;
     }
   }
   __syncthreads();
-  // Bitonic sort of the k entries (padded to a power of two with INT_MAX).
-  int n2 = 1;
-  while (n2 < k) n2 <<= 1;
-  for (int j = k + tid; j < n2; j += kFinThreads) sorted[j] = 0x7FFFFFFF;
-  __syncthreads();
-  for (int size = 2; size <= n2; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = tid; i < n2 / 2; i += kFinThreads) {
-        const int lo = 2 * i - (i & (stride - 1));
-        const int hi = lo + stride;
-        const bool up = (lo & size) == 0;
-        const int32_t a = sorted[lo], c2 = sorted[hi];
-        if ((a > c2) == up) {
-          sorted[lo] = c2;
-          sorted[hi] = a;
-        }
+  if ((int64_t)L <= kBitmapBits) {
+    // Ascending order via an LDS bitmap over [0, L) and a prefix popcount.
+    const int words = (int)((L + 31) / 32);
+    for (int i = tid; i < words; i += kFinThreads) big[i] = 0u;
+    __syncthreads();
+    for (int j = tid; j < k; j += kFinThreads) {
+      const int32_t t = sel[j];
+      atomicOr(&big[t >> 5], 1u << (t & 31));
+    }
+    __syncthreads();
+    const int per = (words + kFinThreads - 1) / kFinThreads;
+    const int w0 = min(words, tid * per), w1 = min(words, w0 + per);
+    uint32_t mine = 0;
+    for (int i = w0; i < w1; ++i) mine += __popc(big[i]);
+    uint32_t pos = block_incl_scan<kFinThreads>(mine, tmp) - mine;
+    for (int i = w0; i < w1; ++i) {
+      uint32_t m = big[i];
+      while (m) {
+        const int bit = __ffs(m) - 1;
+        m &= m - 1u;
+        out[pos++] = i * 32 + bit;
       }
-      __syncthreads();
     }
+  } else {
+    // Bitonic sort of the k entries (padded with INT_MAX) in place.
+    int n2 = 1;
+    while (n2 < k) n2 <<= 1;
+    for (int j = k + tid; j < n2; j += kFinThreads) sel[j] = 0x7FFFFFFF;
+    __syncthreads();
+    for (int size = 2; size <= n2; size <<= 1) {
+      for (int stride = size >> 1; stride > 0; stride >>= 1) {
+        for (int i = tid; i < n2 / 2; i += kFinThreads) {
+          const int lo = 2 * i - (i & (stride - 1));
+          const int hi = lo + stride;
+          const bool up = (lo & size) == 0;
+          const int32_t a = sel[lo], c = sel[hi];
+          if ((a > c) == up) { sel[lo] = c; sel[hi] = a; }
+        }
+        __syncthreads();
+      }
+    }
+    for (int j = tid; j < k; j += kFinThreads) out[j] = sel[j];
   }
-  for (int j = tid; j < k; j += kFinThreads) out[j] = sorted[j] == 0x7FFFFFFF ? -1 : sorted[j];
 }
 
 int launch_topk(const TopkArgs& a, hipStream_t s) {
   if (a.batch == 0) return 0;
   if (a.k > kMaxK || a.k < 1) return -2;
   TopkWs ws = carve(a.workspace, a.batch, a.max_len);
-  const int64_t n_hist = (int64_t)a.batch * kBins0, n_ctrl = (int64_t)a.batch * kCtrlWords;
-  hipLaunchKernelGGL(topk_clear_kernel, dim3((unsigned)std::min<int64_t>(1024, (n_hist + 255) / 256)), dim3(256), 0, s,
-                     ws.hist, ws.ctrl, n_hist, n_ctrl);
-  const int64_t chunks = a.max_len > 0 ? (a.max_len + kTkChunk - 1) / kTkChunk : 1;
-  const int64_t grid = (int64_t)a.batch * chunks;
+  const int64_t grid = (int64_t)a.batch * ws.chunks;
   if (grid > 0x7FFFFFFF) return -2;
-  hipLaunchKernelGGL(topk_hist_kernel, dim3((unsigned)grid), dim3(kTkThreads), 0, s, a.scores, a.score_stride, a.lens,
-                     a.max_len, a.k, ws.hist, (int32_t)chunks);
+  hipLaunchKernelGGL(topk_range_kernel, dim3((unsigned)grid), dim3(kTkThreads), 0, s, a.scores, a.score_stride,
+                     a.lens, a.max_len, a.k, ws);
+  hipLaunchKernelGGL(topk_hist_kernel, dim3((unsigned)grid), dim3(kTkThreads), 0, s, a.scores, a.score_stride,
+                     a.lens, a.max_len, a.k, ws);
   hipLaunchKernelGGL(topk_filter_kernel, dim3((unsigned)grid), dim3(kTkThreads), 0, s, a.scores, a.score_stride,
-                     a.lens, a.max_len, a.k, ws.hist, ws.ctrl, ws.cand, ws.cap, a.out_idx, (int32_t)chunks);
+                     a.lens, a.max_len, a.k, ws, a.out_idx);
   hipLaunchKernelGGL(topk_finish_kernel, dim3((unsigned)a.batch), dim3(kFinThreads), 0, s, a.lens, a.max_len, a.k,
-                     ws.hist, ws.ctrl, ws.cand, ws.cap, a.out_idx, a.status);
+                     ws, a.out_idx, a.status);
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 

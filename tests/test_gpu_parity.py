@@ -151,6 +151,30 @@ def test_topk_bad_len_flags_request():
     parity.check_topk_exact(o[:1], S[:1], np.array([10]), 8, "bad-len neighbour")
 
 
+def test_scores_growing_along_the_context():
+    """Logits that grow steadily along the tokens: later tiles exceed the first
+    tile's max by far more than the kernel's fixed-reference headroom, which
+    forces its recompute path; results must still match the oracle."""
+    _lib()
+    cfg = gen.CONFIGS["c2"].with_(batch=2)
+    inp = gen.make_inputs(cfg, lens=[3000, 777])
+    D = cfg.dim
+    u = gen.normals32(11, 0, 0, D)
+    u /= np.linalg.norm(u)
+    q = np.broadcast_to(u * 6.0, (2, cfg.n_heads, D)).astype(np.float32)
+    q[:, 1::2] *= -1.0                                  # half the heads see decreasing logits
+    inp.q = gen.to_bf16_bits(q)
+    P = cfg.page_size
+    kv = gen.bf16_bits_to_f32(inp.kv).reshape(-1, D)
+    for b in range(2):
+        for t in range(int(inp.lens[b])):
+            row = int(inp.block_table[b, t // P]) * P + t % P
+            kv[row] = u * (t / 40.0) + 0.05 * kv[row]
+    inp.kv = gen.to_bf16_bits(kv).reshape(inp.kv.shape)
+    for splits in (1, 3):
+        _check_full(inp, splits, "growing logits")
+
+
 # ------------------------------------------------------------ fault handling
 
 def test_device_faults_flag_only_the_offending_request():
