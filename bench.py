@@ -41,7 +41,8 @@ def parse():
     ap.add_argument("--no-flush", action="store_true")
     ap.add_argument("--cpu-requests", type=int, default=-1,
                     help="requests in the CPU-oracle sample (-1: auto, 0: skip)")
-    ap.add_argument("--profile-only", action="store_true", help="no CPU baseline, fewer extras (for rocprofv3)")
+    ap.add_argument("--profile-only", action="store_true",
+                    help="no CPU baseline; adds one plain 256 MiB device copy (counter calibration) for rocprofv3")
     return ap.parse_args()
 
 
@@ -174,14 +175,17 @@ def main():
             per_stage[n].append(evs[i].elapsed_time(evs[i + 1]))
     mean_ms = statistics.fmean(step_ms)
 
-    # Warm: K steps back to back.
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(args.steps):
-        step.run()
-    e1.record()
-    torch.cuda.synchronize()
-    warm_ms = e0.elapsed_time(e1) / args.steps
+    # Warm: K steps back to back (skipped under --profile-only so that a
+    # profiler's per-kernel averages cover the same launches as the events).
+    warm_ms = float("nan")
+    if not args.profile_only:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            step.run()
+        e1.record()
+        torch.cuda.synchronize()
+        warm_ms = e0.elapsed_time(e1) / args.steps
 
     alg = algorithmic(cfg, inp.lens)
     t_star = roofline_time_s(alg)
@@ -205,6 +209,15 @@ def main():
         roof = dict(bound="mfma", achieved=round(achieved, 2), peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
                     frac=round(achieved / BF16_PEAK_TFLOPS, 4), traffic=traffic, kernel=dom,
                     algorithmic_flops=int(dk["flops"]), avg_launch_us=round(t_dom * 1e6, 2))
+
+    if args.profile_only:
+        # A plain device-to-device copy of known size: the HBM counters read for
+        # it calibrate the counters read for the kernels.
+        src = torch.ones(256 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     n_cpu = args.cpu_requests
     if n_cpu < 0:
@@ -232,7 +245,8 @@ def main():
         "kernel_us": {k: round(v * 1e3, 2) for k, v in kernel_ms.items()},
         "step_ms_median_min_max": [round(statistics.median(step_ms), 4), round(min(step_ms), 4),
                                    round(max(step_ms), 4)],
-        "warm_ms_per_step": round(warm_ms, 4), "warm_value": round(cfg.batch / (warm_ms * 1e-3), 1),
+        "warm_ms_per_step": None if warm_ms != warm_ms else round(warm_ms, 4),
+        "warm_value": None if warm_ms != warm_ms else round(cfg.batch / (warm_ms * 1e-3), 1),
         "wall_ms_per_step_incl_flush": round(wall / args.steps * 1e3, 4),
     }
     print(json.dumps(line), flush=True)
