@@ -4,28 +4,33 @@
 // score(b, t) = sum_h w[b,h] * max(0, q_idx[b,h,:] . key(b,t)) (times the
 // token's FP8 scale, which is positive and so commutes with the ReLU).
 //
-// Work split: one workgroup (4 waves) per (request, chunk of kIdxChunk
-// tokens); the chunk's page ids are resolved into LDS first, so the key loads
-// never wait on a block-table load.  Each wave streams 64 tokens per step with
-// fully coalesced 16-byte loads (one page of 64 FP8 keys is 8 KiB of
-// consecutive bytes), always one step ahead (two register buffers), and
-// transposes them into MFMA operand order through its own LDS rows.  The math
-// is done in 16-token sub-blocks: S[heads x 16 tokens] = Q[heads x d] .
-// K^T[d x 16 tokens] with the heads on the MFMA's M side (the query stays in
-// registers for the whole chunk) and the tokens on N, so each lane loads a
-// contiguous slice of one key row straight from HBM.  Because a dot product
-// may sum its terms in any order, lane group g owns the contiguous quarter
-// [g*d/4, (g+1)*d/4) of the key row and k-step s takes KPL elements of it;
-// the query fragments use the same permutation.  The ReLU-weighted head sum
-// is a per-lane sum over the 4 rows it holds per M-tile plus two xor shuffles.
+// Work split: the batch's history is cut into steps of STEP_TOK consecutive
+// tokens of one request (8 KiB of keys), and every wave of a fixed,
+// GPU-filling grid takes an equal contiguous run of the flattened step list,
+// which may cross into the next request.  There is no tail of idle workgroups
+// and no per-chunk start-up; each wave finds its first step with one scan
+// over the request lengths.  A wave streams its steps with fully coalesced
+// 16-byte non-temporal loads (a page of 64 FP8 keys is 8 KiB of consecutive
+// bytes), always one step ahead (two register buffers), with the block-table
+// entries of the step after that already in registers, and transposes each
+// step into MFMA operand order through its own LDS rows.  The math is done in
+// 16-token sub-blocks: S[heads x 16 tokens] = Q[heads x d] . K^T[d x 16
+// tokens] with the heads on the MFMA's M side (the query stays in registers
+// while the request does not change) and the tokens on N.  Because a dot
+// product may sum its terms in any order, lane group g owns the contiguous
+// quarter [g*d/4, (g+1)*d/4) of the key row and k-step s takes KPL elements
+// of it; the query fragments use the same permutation.  The ReLU-weighted
+// head sum is a per-lane sum over the 4 rows it holds per M-tile plus two
+// xor shuffles.
 #include "common.h"
 #include "launch.h"
 
 namespace spmla {
 
 constexpr int kIdxThreads = 256;
-constexpr int kIdxChunk = 4096;         // tokens per workgroup
 constexpr int kIdxStepBytes = 8192;     // key bytes a wave fetches per step
+constexpr int kIdxWgPerCu = 2;          // resident workgroups per compute unit
+constexpr int kNumCu = 256;
 
 // Tokens a wave handles per step: 8 KiB of keys, at least one 16-token MFMA block.
 template <int ROW_BYTES>
@@ -35,20 +40,35 @@ struct IdxStep {
 
 // Flat workgroup id -> logical id such that consecutive logical ids share an
 // XCD (the dispatcher deals workgroups round-robin over the 8 XCDs, each with
-// its own L2), so the chunks of one request reuse its query in one L2.
+// its own L2), so neighbouring runs of steps (mostly the same request) read
+// its query through one L2.
 __device__ __forceinline__ int xcd_remap(int bid, int n) {
   const int q = n >> 3, r = n & 7;
   const int xcd = bid & 7, slot = bid >> 3;
   return xcd < r ? xcd * (q + 1) + slot : r * (q + 1) + (xcd - r) * q + slot;
 }
 
+__device__ __forceinline__ int64_t wave_sum_i64(int64_t v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+__device__ __forceinline__ int64_t wave_incl_scan_i64(int64_t v, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int64_t u = __shfl_up(v, o);
+    if (lane >= o) v += u;
+  }
+  return v;
+}
+
 template <class Op, int KDT, int KSTEPS, int MT>
 __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(
     const void* __restrict__ q_idx, const float* __restrict__ w, const uint8_t* __restrict__ k_pool,
     const float* __restrict__ k_scale, int32_t num_pages, int32_t page_shift,
-    const int32_t* __restrict__ bt, int32_t bt_stride, const int32_t* __restrict__ lens, int64_t max_len,
-    int32_t n_heads, float* __restrict__ scores, int64_t score_stride, int32_t* __restrict__ status,
-    int32_t chunks_per_req) {
+    const int32_t* __restrict__ bt, int32_t bt_stride, const int32_t* __restrict__ lens, int32_t batch,
+    int64_t max_len, int32_t n_heads, float* __restrict__ scores, int64_t score_stride,
+    int32_t* __restrict__ status) {
   constexpr int KPL = Op::KPL;
   constexpr int D = KSTEPS * 4 * KPL;            // key dim
   constexpr int GROUP_ELEMS = D / 4;             // contiguous elements a lane group owns
@@ -59,7 +79,6 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(
   constexpr int QE = kBf ? 2 : 4;                // query element bytes
   constexpr int STEP_TOK = IdxStep<ROW_BYTES>::tok;  // tokens per wave step
   constexpr int SUBS = STEP_TOK / 16;                // 16-token MFMA blocks per step
-  constexpr int WG_STEP = 4 * STEP_TOK;              // tokens per workgroup step
   constexpr int STEP_BYTES = STEP_TOK * ROW_BYTES;
   static_assert(ROW_BYTES % 16 == 0 && GROUP_BYTES % 4 == 0, "key rows must be whole 16-byte pieces");
   constexpr int PIECES = STEP_BYTES / 16;        // 16-byte pieces per wave step
@@ -67,157 +86,235 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(
   constexpr int ROW_PIECES = ROW_BYTES / 16;
   constexpr int LROW = ROW_BYTES + 16;           // padded LDS row (conflict-free slice reads)
   const int page_size = 1 << page_shift;
+  const int64_t bt_cap = (int64_t)bt_stride * page_size;
 
-  __shared__ int32_t pg[kIdxChunk / 16 + 1];     // page ids of the chunk (-1: bad)
   __shared__ __attribute__((aligned(16))) uint8_t stage[4][STEP_TOK * LROW];
 
-  const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  const int b = logical / chunks_per_req;
-  const int chunk = logical % chunks_per_req;
   const int lane = threadIdx.x & 63;
-  const int wv = threadIdx.x >> 6;
+  // Wave-uniform values are kept in scalar registers: the run bounds, the
+  // cursors and the request lengths then never wait on vector memory.
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4;
   const int r16 = lane & 15;
-
-  const int32_t L = lens[b];
-  if (L < 0 || (int64_t)L > max_len || (int64_t)L > (int64_t)bt_stride * page_size) {
-    if (chunk == 0 && threadIdx.x == 0 && status) atomicOr(status + b, kBadLen);
-    return;
-  }
-  const int64_t t_begin = (int64_t)chunk * kIdxChunk;
-  if (t_begin >= L) return;
-  const int64_t t_end = min((int64_t)L, t_begin + kIdxChunk);
-
-  // Resolve the chunk's pages once (t_begin is a multiple of the page size).
-  const int64_t pg0 = t_begin >> page_shift;
-  const int n_pg = (int)(((t_end - 1) >> page_shift) - pg0 + 1);
-  bool flagged = false;
-  for (int i = threadIdx.x; i < n_pg; i += kIdxThreads) {
-    int32_t p = bt[(int64_t)b * bt_stride + pg0 + i];
-    if (p < 0 || p >= num_pages) {
-      p = -1;
-      flagged = true;
-    }
-    pg[i] = p;
-  }
-  if (flagged && status) atomicOr(status + b, kBadPage);
-
-  // Query fragments (A operand: rows = heads), permuted like the key slices.
-  typename Op::frag qa[MT][KSTEPS];
-  float wr[MT][4];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const int h = mt * 16 + r16;
-    if (h < n_heads) {
-      uint32_t raw[(GROUP_ELEMS * QE + 3) / 4];
-      const uint8_t* qp = reinterpret_cast<const uint8_t*>(q_idx) + (((int64_t)b * n_heads + h) * D + g * GROUP_ELEMS) * QE;
-      load_raw<GROUP_ELEMS * QE>(qp, raw);
-      raw_to_frags<Op, kBf ? kBF16 : kF32, KSTEPS>(raw, qa[mt]);
-    } else {
-#pragma unroll
-      for (int s = 0; s < KSTEPS; ++s) qa[mt][s] = zero_frag<Op>();
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int hh = mt * 16 + g * 4 + i;
-      wr[mt][i] = hh < n_heads ? w[(int64_t)b * n_heads + hh] : 0.f;
-    }
-  }
-  __syncthreads();  // pg[] ready
-
-  float* sc_out = scores + (int64_t)b * score_stride;
+  const int64_t nw = (int64_t)gridDim.x * 4;
+  const int64_t gw = (int64_t)xcd_remap(blockIdx.x, gridDim.x) * 4 + wv;
   uint8_t* my_stage = stage[wv];
 
-  // Row of token t of the chunk (>= 0), -1 past the end, -2 on a bad page.
-  auto row_of = [&](int64_t t) __attribute__((always_inline)) -> int64_t {
-    if (t >= t_end) return -1;
-    const int32_t page = pg[(int)((t >> page_shift) - pg0)];
-    if (page < 0) return -2;
-    return ((int64_t)page << page_shift) + (t & (page_size - 1));
+  auto len_ok = [&](int32_t Lb) -> bool { return Lb >= 0 && (int64_t)Lb <= max_len && (int64_t)Lb <= bt_cap; };
+  auto steps_of = [&](int32_t Lb) -> int64_t { return len_ok(Lb) ? ((int64_t)Lb + STEP_TOK - 1) / STEP_TOK : 0; };
+
+  // ---- this wave's run of steps [u0, u1) of the flattened step list
+  int64_t mine = 0;
+  for (int i = lane; i < batch; i += 64) {
+    const int32_t Lb = lens[i];
+    mine += steps_of(Lb);
+    if (gw == 0 && !len_ok(Lb) && status) atomicOr(status + i, kBadLen);
+  }
+  int64_t total = wave_sum_i64(mine);
+  total = ((int64_t)__builtin_amdgcn_readfirstlane((int32_t)(total >> 32)) << 32) |
+          (uint32_t)__builtin_amdgcn_readfirstlane((int32_t)total);
+  const int64_t u0 = total * gw / nw, u1 = total * (gw + 1) / nw;
+  if (u0 >= u1) return;
+  int32_t b0 = 0;
+  int64_t s0 = 0;  // step index of u0 within request b0
+  {
+    int64_t base = 0;
+    for (int c = 0; c < batch; c += 64) {
+      const int i = c + lane;
+      const int64_t un = i < batch ? steps_of(lens[i]) : 0;
+      const int64_t inc = wave_incl_scan_i64(un, lane);
+      const int64_t tot = __shfl(inc, 63);
+      if (u0 < base + tot) {
+        const int j = __ffsll((unsigned long long)__ballot(base + inc > u0)) - 1;
+        b0 = __builtin_amdgcn_readfirstlane(c + j);
+        s0 = u0 - (base + __shfl(inc - un, j));
+        break;
+      }
+      base += tot;
+    }
+  }
+
+  s0 = ((int64_t)__builtin_amdgcn_readfirstlane((int32_t)(s0 >> 32)) << 32) |
+       (uint32_t)__builtin_amdgcn_readfirstlane((int32_t)s0);
+
+  // Query fragments (A operand: rows = heads), permuted like the key slices,
+  // and head weights of request `rb`.
+  typename Op::frag qa[MT][KSTEPS];
+  float wr[MT][4];
+  auto load_query = [&](int32_t rb) __attribute__((always_inline)) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int h = mt * 16 + r16;
+      if (h < n_heads) {
+        uint32_t raw[(GROUP_ELEMS * QE + 3) / 4];
+        const uint8_t* qp =
+            reinterpret_cast<const uint8_t*>(q_idx) + (((int64_t)rb * n_heads + h) * D + g * GROUP_ELEMS) * QE;
+        load_raw<GROUP_ELEMS * QE>(qp, raw);
+        raw_to_frags<Op, kBf ? kBF16 : kF32, KSTEPS>(raw, qa[mt]);
+      } else {
+#pragma unroll
+        for (int st = 0; st < KSTEPS; ++st) qa[mt][st] = zero_frag<Op>();
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int hh = mt * 16 + g * 4 + i;
+        wr[mt][i] = hh < n_heads ? w[(int64_t)rb * n_heads + hh] : 0.f;
+      }
+    }
   };
 
-  // A wave step covers tokens [t0 + STEP_TOK wv, +STEP_TOK).  Its key bytes are fetched as
-  // 16-byte pieces in token-major order, lane l taking piece 64 i + l of load
-  // i, so every load instruction reads 1 KiB of consecutive row bytes (a page
-  // is contiguous), with non-temporal loads since every key is read once per
-  // step.  The loads are unconditional (a piece past the end reads
-  // row 0, which always exists, and is never used), so the compiler can count
-  // them and keep the next step's loads in flight during this step's math.
-  uint32_t raw_a[LOADS][4], raw_b[LOADS][4];
-  float sc_a = 1.f, sc_b = 1.f;
-  auto issue = [&](int64_t t0, uint32_t (*raw)[4], float& sc) __attribute__((always_inline)) {
-    const int64_t tw = t0 + wv * STEP_TOK;
+  // Token tok of a step whose first token is t0 lies on the step's page
+  // tok >> page_shift when pages are no longer than a step (t0 is then a
+  // multiple of the page size), else on its only page at offset
+  // (t0 mod page size) + tok.
+  const bool multi_page = page_size < STEP_TOK;
+
+  // The run is walked one request at a time: steps [s, s_end) of request b
+  // (length L).  Within a request everything the loop needs is in scalar
+  // registers, so its only memory waits are for the keys themselves.
+  int32_t b = b0;
+  int32_t L = __builtin_amdgcn_readfirstlane(lens[b0]);
+  int64_t s = s0;
+  int64_t todo = u1 - u0;
+  while (true) {
+    const int64_t s_end = min(steps_of(L), s + todo);
+    const int64_t n = s_end - s;
+    load_query(b);
+    const int32_t* btb = bt + (int64_t)b * bt_stride;
+    float* sc_out = scores + (int64_t)b * score_stride;
+    const int64_t last_page = ((int64_t)L - 1) >> page_shift;
+
+    // Block-table entries of step si: lane j < 4 loads the entry of the
+    // step's j-th page (a step spans at most 4 pages, as pages hold at least
+    // 16 tokens); entries past the request's last page repeat its last page.
+    auto prep = [&](int64_t si) __attribute__((always_inline)) -> int32_t {
+      const int64_t first = (si * STEP_TOK) >> page_shift;
+      return btb[min(first + min(lane, 3), last_page)];
+    };
+    // Issue the key loads of step si.  The loads are unconditional (a token
+    // past the end, or a step past the run, reads row 0, which always
+    // exists, and is never used), so the compiler can count them and keep
+    // the next step's loads in flight during this step's math.  `sc` gets
+    // the FP8 scale of token `lane` (1 for other key types) and `bad_tok` is
+    // set if its page is invalid (applied at consume time, so that nothing
+    // here waits for the scale load).
+    auto issue = [&](int64_t si, int32_t pgv, uint32_t (*raw)[4], float& sc, int& bad_tok)
+        __attribute__((always_inline)) {
+      const int64_t t0 = si * STEP_TOK;
+      const int t0_in_page = multi_page ? 0 : (int)(t0 & (page_size - 1));
+      const int left = (int)max((int64_t)0, min((int64_t)L - t0, (int64_t)STEP_TOK));
+      // Cache row of token `tok` of the step (row 0 when past the end or on
+      // an invalid page, which `bad` then reports).  Branch-free, so the
+      // loads stay in one basic block.
+      auto row_of = [&](int tok, bool& bad) __attribute__((always_inline)) -> int64_t {
+        const int32_t page = __shfl(pgv, multi_page ? tok >> page_shift : 0);
+        const bool in = tok < left;
+        const bool valid = (page >= 0) & (page < num_pages);
+        bad = in & !valid;
+        const bool ok = in & valid;
+        return ((int64_t)(ok ? page : 0) << page_shift) + (ok ? (t0_in_page + tok) & (page_size - 1) : 0);
+      };
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int piece = min(i * 64 + lane, PIECES - 1);
-      const int64_t row = row_of(tw + piece / ROW_PIECES);
-      const int64_t safe = row >= 0 ? row : 0;
-      load_nt16(k_pool + safe * ROW_BYTES + (piece % ROW_PIECES) * 16, raw[i]);
-    }
-    if constexpr (KDT == kFP8) {
-      const int64_t row = row_of(tw + min(lane, STEP_TOK - 1));
-      sc = k_scale[row >= 0 ? row : 0];
-    }
-  };
-  auto consume = [&](int64_t t0, const uint32_t (*raw)[4], float sc) __attribute__((always_inline)) {
-    const int64_t tw = t0 + wv * STEP_TOK;
-    // Transpose through the wave's own LDS rows (padded by 16 bytes).
+      for (int i = 0; i < LOADS; ++i) {
+        const int piece = min(i * 64 + lane, PIECES - 1);
+        bool bad;
+        const int64_t row = row_of(piece / ROW_PIECES, bad);
+        load_nt16(k_pool + row * ROW_BYTES + (piece % ROW_PIECES) * 16, raw[i]);
+      }
+      bool bad;
+      const int64_t row = row_of(min(lane, STEP_TOK - 1), bad);
+      if constexpr (KDT == kFP8) {
+        sc = k_scale[row];
+      } else {
+        sc = 1.f;
+      }
+      bad_tok = bad;
+      if (__builtin_expect(__any(bad), 0) && bad && status) atomicOr(status + b, kBadPage);
+    };
+    auto consume = [&](int64_t si, const uint32_t (*raw)[4], float sc, int bad_tok) __attribute__((always_inline)) {
+      const int64_t t0 = si * STEP_TOK;
+      // Transpose through the wave's own LDS rows (padded by 16 bytes).
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int piece = i * 64 + lane;
-      if (piece < PIECES)
-        *reinterpret_cast<uint4*>(my_stage + (piece / ROW_PIECES) * LROW + (piece % ROW_PIECES) * 16) =
-            make_uint4(raw[i][0], raw[i][1], raw[i][2], raw[i][3]);
-    }
-    __builtin_amdgcn_wave_barrier();
+      for (int i = 0; i < LOADS; ++i) {
+        const int piece = i * 64 + lane;
+        if (piece < PIECES)
+          *reinterpret_cast<uint4*>(my_stage + (piece / ROW_PIECES) * LROW + (piece % ROW_PIECES) * 16) =
+              make_uint4(raw[i][0], raw[i][1], raw[i][2], raw[i][3]);
+      }
+      __builtin_amdgcn_wave_barrier();
 #pragma unroll
-    for (int j = 0; j < SUBS; ++j) {
-      const int tok = j * 16 + r16;  // token of this lane's MFMA column
-      uint32_t sl[RAW_DW];
-      const uint8_t* src = my_stage + tok * LROW + g * GROUP_BYTES;
+      for (int j = 0; j < SUBS; ++j) {
+        const int tok = j * 16 + r16;  // token of this lane's MFMA column
+        uint32_t sl[RAW_DW];
+        const uint8_t* src = my_stage + tok * LROW + g * GROUP_BYTES;
 #pragma unroll
-      for (int x = 0; x < RAW_DW; x += 4) {
-        if (x + 4 <= RAW_DW) {
-          const uint4 v = *reinterpret_cast<const uint4*>(src + 4 * x);
-          sl[x] = v.x; sl[x + 1] = v.y; sl[x + 2] = v.z; sl[x + 3] = v.w;
-        } else {
+        for (int x = 0; x < RAW_DW; x += 4) {
+          if (x + 4 <= RAW_DW) {
+            const uint4 v = *reinterpret_cast<const uint4*>(src + 4 * x);
+            sl[x] = v.x; sl[x + 1] = v.y; sl[x + 2] = v.z; sl[x + 3] = v.w;
+          } else {
 #pragma unroll
-          for (int y = x; y < RAW_DW; ++y) sl[y] = *reinterpret_cast<const uint32_t*>(src + 4 * y);
+            for (int y = x; y < RAW_DW; ++y) sl[y] = *reinterpret_cast<const uint32_t*>(src + 4 * y);
+          }
         }
+        typename Op::frag kb[KSTEPS];
+        raw_to_frags<Op, KDT, KSTEPS>(sl, kb);
+        f32x4 acc[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int st = 0; st < KSTEPS; ++st) {
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) acc[mt] = Op::mma(qa[mt][st], kb[st], acc[mt]);
+        }
+        float v = 0.f;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v += wr[mt][i] * fmaxf(acc[mt][i], 0.f);
+        }
+        v = wave_sum_xor16_32(v);
+        const float tsc = __shfl(sc, tok);
+        const bool bad = __shfl(bad_tok, tok) != 0;
+        const int64_t t = t0 + tok;
+        if (g == 0 && t < L) sc_out[t] = bad ? __uint_as_float(0x7FC00000u) : v * tsc;
       }
-      typename Op::frag kb[KSTEPS];
-      raw_to_frags<Op, KDT, KSTEPS>(sl, kb);
-      f32x4 acc[MT];
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < KSTEPS; ++s) {
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[mt] = Op::mma(qa[mt][s], kb[s], acc[mt]);
-      }
-      float v = 0.f;
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) v += wr[mt][i] * fmaxf(acc[mt][i], 0.f);
-      }
-      v = wave_sum_xor16_32(v);
-      const float tsc = __shfl(sc, tok);
-      const int64_t t = tw + tok;
-      if (g == 0 && t < t_end) sc_out[t] = row_of(t) == -2 ? __uint_as_float(0x7FC00000u) : v * tsc;
-    }
-    __builtin_amdgcn_wave_barrier();
-  };
+      __builtin_amdgcn_wave_barrier();
+    };
 
-  issue(t_begin, raw_a, sc_a);
-  for (int64_t t0 = t_begin; t0 < t_end; t0 += 2 * WG_STEP) {
-    // Issued unconditionally so that the wait before consume() only covers
-    // the older buffer.
-    issue(t0 + WG_STEP, raw_b, sc_b);
-    consume(t0, raw_a, sc_a);
-    if (t0 + WG_STEP >= t_end) break;
-    issue(t0 + 2 * WG_STEP, raw_a, sc_a);
-    consume(t0 + WG_STEP, raw_b, sc_b);
+    // Software pipeline, per step: the block-table entries of the step two
+    // ahead are requested first, then the key loads of the next step (whose
+    // entries were requested one step earlier, before the keys consumed
+    // now, so waiting for them never waits for those keys), then this step's
+    // keys are consumed.  Memory requests complete in order, so this
+    // ordering keeps two steps of keys in flight.  Steps past the request's
+    // share of the run only touch row 0 and are never consumed.
+    uint32_t raw_a[LOADS][4], raw_b[LOADS][4];
+    float sc_a, sc_b;
+    int bad_a, bad_b;
+    int32_t pg_a = prep(s);
+    int32_t pg_b = prep(s + 1);
+    issue(s, pg_a, raw_a, sc_a, bad_a);
+    int64_t k = 0;
+    for (; k + 1 < n; k += 2) {
+      pg_a = prep(s + k + 2);
+      issue(s + k + 1, pg_b, raw_b, sc_b, bad_b);
+      consume(s + k, raw_a, sc_a, bad_a);
+      pg_b = prep(s + k + 3);
+      issue(s + k + 2, pg_a, raw_a, sc_a, bad_a);
+      consume(s + k + 1, raw_b, sc_b, bad_b);
+    }
+    if (k < n) consume(s + k, raw_a, sc_a, bad_a);
+    __builtin_amdgcn_s_waitcnt(0);  // the loads of a step past the run are done with
+
+    todo -= n;
+    if (todo <= 0) break;
+    // The run goes on with the next request that has steps.
+    do {
+      ++b;
+      L = __builtin_amdgcn_readfirstlane(lens[b]);
+    } while (steps_of(L) == 0);
+    s = 0;
   }
 }
 
@@ -225,14 +322,15 @@ template <class Op, int KDT, int KSTEPS, int MT>
 static int launch_one(const IndexerArgs& a, hipStream_t stream) {
   int page_shift = 0;
   while ((1 << page_shift) < a.page_size) ++page_shift;
-  const int64_t chunks = (a.max_len + kIdxChunk - 1) / kIdxChunk;
-  const int64_t grid = (int64_t)a.batch * (chunks > 0 ? chunks : 1);
   if (a.batch == 0 || a.max_len == 0) return 0;
-  if (grid > 0x7FFFFFFF) return -2;
+  // Enough waves to fill the GPU, but not more than there are steps at most.
+  constexpr int ROW_BYTES = KSTEPS * 4 * Op::KPL * Storage<KDT>::bytes;
+  constexpr int STEP_TOK = IdxStep<ROW_BYTES>::tok;
+  const int64_t max_steps = (int64_t)a.batch * ((a.max_len + STEP_TOK - 1) / STEP_TOK);
+  const int64_t grid = std::min<int64_t>((int64_t)kNumCu * kIdxWgPerCu, (max_steps + 3) / 4);
   hipLaunchKernelGGL((indexer_kernel<Op, KDT, KSTEPS, MT>), dim3((unsigned)grid), dim3(kIdxThreads), 0, stream,
                      a.q_idx, a.w, reinterpret_cast<const uint8_t*>(a.k_pool), a.k_scale, a.num_pages, page_shift,
-                     a.bt, a.bt_stride, a.lens, a.max_len, a.n_heads, a.scores, a.score_stride, a.status,
-                     (int32_t)(chunks > 0 ? chunks : 1));
+                     a.bt, a.bt_stride, a.lens, a.batch, a.max_len, a.n_heads, a.scores, a.score_stride, a.status);
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 
