@@ -214,19 +214,36 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(
         const bool ok = in & valid;
         return ((int64_t)(ok ? page : 0) << page_shift) + (ok ? (t0_in_page + tok) & (page_size - 1) : 0);
       };
-#pragma unroll
-      for (int i = 0; i < LOADS; ++i) {
-        const int piece = min(i * 64 + lane, PIECES - 1);
-        bool bad;
-        const int64_t row = row_of(piece / ROW_PIECES, bad);
-        load_nt16(k_pool + row * ROW_BYTES + (piece % ROW_PIECES) * 16, raw[i]);
-      }
       bool bad;
-      const int64_t row = row_of(min(lane, STEP_TOK - 1), bad);
-      if constexpr (KDT == kFP8) {
-        sc = k_scale[row];
+      if (!multi_page) {
+        // The whole step is on one page: a scalar base address plus 32-bit
+        // per-lane offsets (a token past the end reads the step's first row).
+        const int32_t page = __builtin_amdgcn_readfirstlane(pgv);
+        const bool page_ok = page >= 0 && page < num_pages;
+        const int64_t row0 = page_ok ? ((int64_t)page << page_shift) + t0_in_page : 0;
+        const uint8_t* base = k_pool + row0 * ROW_BYTES;
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) {
+          const int piece = min(i * 64 + lane, PIECES - 1);
+          const int tok = piece / ROW_PIECES;
+          const int off = (tok < left ? tok * ROW_BYTES : 0) + (piece % ROW_PIECES) * 16;
+          load_nt16(base + off, raw[i]);
+        }
+        const int tok = min(lane, STEP_TOK - 1);
+        if constexpr (KDT == kFP8) sc = k_scale[row0 + (tok < left ? tok : 0)];
+        else sc = 1.f;
+        bad = tok < left && !page_ok;
       } else {
-        sc = 1.f;
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) {
+          const int piece = min(i * 64 + lane, PIECES - 1);
+          bool bad_i;
+          const int64_t row = row_of(piece / ROW_PIECES, bad_i);
+          load_nt16(k_pool + row * ROW_BYTES + (piece % ROW_PIECES) * 16, raw[i]);
+        }
+        const int64_t row = row_of(min(lane, STEP_TOK - 1), bad);
+        if constexpr (KDT == kFP8) sc = k_scale[row];
+        else sc = 1.f;
       }
       bad_tok = bad;
       if (__builtin_expect(__any(bad), 0) && bad && status) atomicOr(status + b, kBadPage);
@@ -271,7 +288,12 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) v += wr[mt][i] * fmaxf(acc[mt][i], 0.f);
+          for (int i = 0; i < 4; ++i) {
+            // ReLU as an integer max on the bit pattern (one instruction: a
+            // negative float has a negative integer pattern).
+            const float r = __int_as_float(max(__float_as_int(acc[mt][i]), 0));
+            v += wr[mt][i] * r;
+          }
         }
         v = wave_sum_xor16_32(v);
         const float tsc = __shfl(sc, tok);

@@ -97,10 +97,11 @@ def test_poisoned_tails_are_never_read():
 
 # ----------------------------------------------------------------- top-k only
 
-def _gpu_topk(scores, lens, k):
+def _gpu_topk(scores, lens, k, max_len=None):
     spm = _lib()
     B, stride = scores.shape
-    max_len = int(max(lens)) if len(lens) else 0
+    if max_len is None:
+        max_len = int(max(lens)) if len(lens) else 0
     s = torch.from_numpy(np.ascontiguousarray(scores, np.float32)).cuda()
     l = torch.tensor(lens, dtype=torch.int32, device="cuda")
     out = torch.full((B, k), -7, dtype=torch.int32, device="cuda")
@@ -133,6 +134,23 @@ def test_topk_large_continuous():
     S = rng.standard_normal((4, 300032)).astype(np.float32) * 30 + 144
     idx, st = _gpu_topk(S, lens, 2048)
     parity.check_topk_exact(idx, S, np.array(lens), 2048, "continuous")
+
+
+@pytest.mark.parametrize("max_len", [None, 300000])
+def test_topk_big_tie_groups(max_len):
+    """Tie groups larger than what a workgroup holds on chip (every key equal;
+    two values with the k-th falling inside ~15000 equal ones), plus a plain
+    row; max_len 300000 sends the same rows through the multi-workgroup
+    path."""
+    rng = np.random.default_rng(5)
+    lens = [40000, 30000, 20000]
+    S = np.zeros((3, 300032 if max_len else 40064), np.float32)
+    S[0, :] = 1.25
+    S[1, :] = (rng.random(S.shape[1]) < 0.5).astype(np.float32)
+    S[2, :] = rng.standard_normal(S.shape[1]).astype(np.float32)
+    idx, st = _gpu_topk(S, lens, 2048, max_len)
+    assert not st.any()
+    parity.check_topk_exact(idx, S, np.array(lens), 2048, f"big ties max_len={max_len}")
 
 
 def test_topk_bad_len_flags_request():
