@@ -17,8 +17,9 @@
 //             into the request's global one.
 //  3. filter: every chunk finds the bin b0 holding the k-th best key and
 //             streams its keys again: keys above b0 are selected outright,
-//             keys in b0 become candidates.  Both are compacted in LDS first,
-//             so each workgroup reserves its output range with one atomic.
+//             keys in b0 become candidates.  Each thread counts both, one
+//             block scan gives every thread its offsets and each workgroup
+//             reserves its output ranges with one atomic per kind.
 //  4. finish: one workgroup per request resolves the candidates in LDS
 //             (further 11-bit rounds on the remaining key bits, then on the
 //             token index for exact ties) and writes the k_eff indices in
@@ -38,7 +39,7 @@ constexpr int kTkChunk = kTkThreads * kTkPer;    // 4096 keys per workgroup
 constexpr int kBins = 2048;
 constexpr int kFinThreads = 1024;
 constexpr int kMaxK = 4096;
-constexpr int kCtrl = 8;                         // out_count, cand_count
+constexpr int kCtrl = 8;                         // selected count, candidate count, digit shift
 constexpr int kFinLdsWords = 32768;              // 128 KiB: candidates, then the bitmap
 constexpr int kCandLds = kFinLdsWords / 2;       // candidates that fit in LDS (uint2 each)
 constexpr int64_t kBitmapBits = (int64_t)kFinLdsWords * 32;
@@ -271,13 +272,6 @@ __device__ void find_bin_asc(const uint32_t* h, uint32_t need, uint32_t* tmp, ui
   __syncthreads();
 }
 
-// Rank of this lane among the lanes of its wave with pred set, and the count.
-__device__ __forceinline__ uint32_t wave_rank(bool pred, uint32_t* count) {
-  const uint64_t mask = __ballot(pred);
-  *count = (uint32_t)__popcll(mask);
-  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
-}
-
 __global__ __launch_bounds__(kTkThreads) void topk_filter_kernel(const float* __restrict__ scores, int64_t stride,
                                                                  const int32_t* __restrict__ lens, int64_t max_len,
                                                                  int32_t k, TopkWs ws, int32_t* __restrict__ out_idx) {
@@ -285,9 +279,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_filter_kernel(const float* __
   __shared__ uint32_t tmp[kTkThreads / 64];
   __shared__ uint32_t res[2];
   __shared__ uint32_t s_mm[2];
-  __shared__ uint32_t n_sel, n_cnd, base_sel, base_cnd;
-  __shared__ int32_t sel_buf[kTkChunk];
-  __shared__ uint2 cnd_buf[kTkChunk];
+  __shared__ uint32_t base_sel, base_cnd;
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
   const int b = logical / ws.chunks, chunk = logical % ws.chunks;
   const int32_t L = lens[b];
@@ -300,41 +292,39 @@ __global__ __launch_bounds__(kTkThreads) void topk_filter_kernel(const float* __
   load_chunk(scores + (int64_t)b * stride, t0, t1, key, in);
   const uint32_t* gh = ws.hist + (int64_t)b * kBins;
   for (int i = threadIdx.x; i < kBins; i += kTkThreads) h[i] = gh[i];
-  if (threadIdx.x == 0) { n_sel = 0u; n_cnd = 0u; }
   request_range(ws.range + (int64_t)b * ws.chunks, n_act, s_mm);
   const int sh = digit_shift(s_mm[0], s_mm[1]);
   find_bin_desc<kBins, kTkThreads>(h, (uint32_t)k, tmp, res);
   const uint32_t b0 = res[0];
-  // Compact this chunk's selected and candidate keys in LDS (one LDS atomic per wave each).
+  if (chunk == 0 && threadIdx.x == 0) ws.ctrl[(int64_t)b * kCtrl + 2] = (uint32_t)sh;
+  // Two-phase compaction: count this thread's selected keys (above b0) and
+  // candidates (in b0), one block scan of both counts packed in a word, one
+  // global atomic per kind for the whole chunk, then direct writes.
+  uint32_t cs = 0, cc = 0;
 #pragma unroll
   for (int j = 0; j < kTkPer; ++j) {
     const uint32_t d = (key[j] >> sh) & (kBins - 1);
-    const bool sel = in[j] && d > b0;
-    const bool cnd = in[j] && d == b0;
-    uint32_t cs, cc;
-    const uint32_t rs = wave_rank(sel, &cs);
-    const uint32_t rc = wave_rank(cnd, &cc);
-    uint32_t bs = 0, bc = 0;
-    if ((threadIdx.x & 63) == 0) {
-      if (cs) bs = atomicAdd(&n_sel, cs);
-      if (cc) bc = atomicAdd(&n_cnd, cc);
-    }
-    bs = (uint32_t)__shfl((int)bs, 0);
-    bc = (uint32_t)__shfl((int)bc, 0);
-    const int64_t t = t0 + (int64_t)j * kTkThreads + threadIdx.x;
-    if (sel) sel_buf[bs + rs] = (int32_t)t;
-    if (cnd) cnd_buf[bc + rc] = make_uint2(key[j], (uint32_t)t);
+    cs += (in[j] && d > b0) ? 1u : 0u;
+    cc += (in[j] && d == b0) ? 1u : 0u;
+  }
+  const uint32_t packed = (cs << 16) | cc;  // at most kTkPer each
+  const uint32_t incl = block_incl_scan<kTkThreads>(packed, tmp);
+  if (threadIdx.x == kTkThreads - 1) {
+    const uint32_t ns = incl >> 16, nc = incl & 0xFFFFu;
+    base_sel = ns ? atomicAdd(ws.ctrl + (int64_t)b * kCtrl + 0, ns) : 0u;
+    base_cnd = nc ? atomicAdd(ws.ctrl + (int64_t)b * kCtrl + 1, nc) : 0u;
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    base_sel = n_sel ? atomicAdd(ws.ctrl + (int64_t)b * kCtrl + 0, n_sel) : 0u;
-    base_cnd = n_cnd ? atomicAdd(ws.ctrl + (int64_t)b * kCtrl + 1, n_cnd) : 0u;
-  }
-  __syncthreads();
+  uint32_t ps = base_sel + ((incl - packed) >> 16), pc = base_cnd + ((incl - packed) & 0xFFFFu);
   int32_t* out = out_idx + (int64_t)b * k;
   uint2* cb = ws.cand + (int64_t)b * ws.cap;
-  for (uint32_t i = threadIdx.x; i < n_sel; i += kTkThreads) out[base_sel + i] = sel_buf[i];
-  for (uint32_t i = threadIdx.x; i < n_cnd; i += kTkThreads) cb[base_cnd + i] = cnd_buf[i];
+#pragma unroll
+  for (int j = 0; j < kTkPer; ++j) {
+    const uint32_t d = (key[j] >> sh) & (kBins - 1);
+    const int64_t t = t0 + (int64_t)j * kTkThreads + threadIdx.x;
+    if (in[j] && d > b0) out[ps++] = (int32_t)t;
+    if (in[j] && d == b0) cb[pc++] = make_uint2(key[j], (uint32_t)t);
+  }
 }
 
 __global__ __launch_bounds__(kFinThreads) void topk_finish_kernel(const int32_t* __restrict__ lens, int64_t max_len,
@@ -360,13 +350,7 @@ __global__ __launch_bounds__(kFinThreads) void topk_finish_kernel(const int32_t*
     for (int j = tid; j < k; j += kFinThreads) out[j] = j < L ? j : -1;
     return;
   }
-  const int n_act = (int)((L + kTkChunk - 1) / kTkChunk);
-  request_range(ws.range + (int64_t)b * ws.chunks, n_act, s_mm);
-  const int sh = digit_shift(s_mm[0], s_mm[1]);
-  const uint32_t* gh = ws.hist + (int64_t)b * kBins;
-  for (int i = tid; i < kBins; i += kFinThreads) h[i] = gh[i];
-  __syncthreads();
-  find_bin_desc<kBins, kFinThreads>(h, (uint32_t)k, tmp, res);
+  const int sh = (int)ws.ctrl[(int64_t)b * kCtrl + 2];  // the digit shift the filter used
   const uint32_t n_gt = ws.ctrl[(int64_t)b * kCtrl + 0];
   const uint32_t n_c = ws.ctrl[(int64_t)b * kCtrl + 1];
   // Candidates: in LDS when they fit, else read from the workspace.
