@@ -89,6 +89,7 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(
   const int64_t bt_cap = (int64_t)bt_stride * page_size;
 
   __shared__ __attribute__((aligned(16))) uint8_t stage[4][STEP_TOK * LROW];
+  __shared__ float step_scores[4][STEP_TOK];  // a step's scores, written out by the whole wave at once
 
   const int lane = threadIdx.x & 63;
   // Wave-uniform values are kept in scalar registers: the run bounds, the
@@ -298,9 +299,11 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(
         v = wave_sum_xor16_32(v);
         const float tsc = __shfl(sc, tok);
         const bool bad = __shfl(bad_tok, tok) != 0;
-        const int64_t t = t0 + tok;
-        if (g == 0 && t < L) sc_out[t] = bad ? __uint_as_float(0x7FC00000u) : v * tsc;
+        if (g == 0) step_scores[wv][tok] = bad ? __uint_as_float(0x7FC00000u) : v * tsc;
       }
+      // One 256-byte store per step instead of a 64-byte store per 16 tokens.
+      __builtin_amdgcn_wave_barrier();
+      if (lane < STEP_TOK && t0 + lane < L) sc_out[t0 + lane] = step_scores[wv][lane];
       __builtin_amdgcn_wave_barrier();
     };
 
