@@ -126,7 +126,7 @@ def main():
     import torch
     import spmla_gen as gen
     from spmla_gen.torch_io import device_batch
-    from sparse_paged_mla_amd.step import DecodeStep
+    from sparse_paged_mla_amd.step import DEFAULT_SPLITS, DecodeStep
     import sparse_paged_mla_amd as spm
 
     spm.load_library()
@@ -137,8 +137,7 @@ def main():
     torch.cuda.synchronize()
     print(f"[bench] {cfg.name}: inputs ready in {time.perf_counter() - t_gen:.1f} s "
           f"(sum L = {int(inp.lens.sum())}, pool {inp.num_pages} pages)", file=sys.stderr, flush=True)
-    default_splits = {"c1": 1, "c2": 4, "c3": 2, "c3f": 2, "c4": 2, "c5": 8}
-    splits = args.splits or default_splits.get(cfg.name, 1)
+    splits = args.splits or DEFAULT_SPLITS.get(cfg.name, 1)
     step = DecodeStep(db, num_splits=splits)
     stages = ["indexer", "select", "attend", "merge"] if step.sparse else ["attend", "merge"]
     if splits == 1:

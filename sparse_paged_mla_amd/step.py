@@ -29,6 +29,11 @@ class DeviceBatch:
     k_idx_scale: Optional[torch.Tensor] = None
 
 
+# KV splits per workload as timed: enough (request, split, head group)
+# workgroups to fill 256 compute units without splitting short token lists.
+DEFAULT_SPLITS = {"c1": 1, "c2": 4, "c3": 2, "c3f": 2, "c4": 2, "c5": 8}
+
+
 class DecodeStep:
     """Holds the step's output and scratch buffers for a fixed batch shape."""
 
