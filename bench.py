@@ -35,7 +35,7 @@ def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--config", default="c3f")
     ap.add_argument("--splits", type=int, default=0, help="KV splits (0: per-workload default)")
     ap.add_argument("--no-flush", action="store_true")
@@ -77,8 +77,12 @@ def roofline_time_s(a):
 
 
 def kernel_source_sha(name):
+    """Hash of a kernel source together with the compiler flags it is built with."""
+    from sparse_paged_mla_amd.build import FLAGS
     p = os.path.join(ROOT, "sparse_paged_mla_amd", "csrc", name)
-    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+    h = hashlib.sha256(open(p, "rb").read())
+    h.update(" ".join(FLAGS).encode())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(kernel_file, workload):
@@ -145,8 +149,15 @@ def main():
     flush_buf = torch.ones(512 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
     flush_sink = torch.zeros((), dtype=torch.float32, device="cuda")
 
-    def run_timed(flush):
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
+    # Every event the timed region records is created (and recorded once)
+    # up front: creating events while timing costs the steps measurable time.
+    ev_sets = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(args.steps)]
+    for evs in ev_sets:
+        for e in evs:
+            e.record()
+    torch.cuda.synchronize()
+
+    def run_timed(flush, evs):
         if flush:
             flush_sink.copy_(flush_buf.amax())
         evs[0].record()
@@ -155,15 +166,16 @@ def main():
             evs[i + 1].record()
         return evs
 
-    for _ in range(args.warmup):
-        run_timed(False)
+    # Warm-up steps are the timed steps' exact twins (cache sweep included).
+    flush = not args.no_flush
+    for i in range(args.warmup):
+        run_timed(flush, ev_sets[i % args.steps])
     torch.cuda.synchronize()
     assert not step.status.cpu().numpy().any(), "device status flags set on clean inputs"
 
-    flush = not args.no_flush
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    recs = [run_timed(flush) for _ in range(args.steps)]
+    recs = [run_timed(flush, evs) for evs in ev_sets]
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     per_stage = {n: [] for n in stages}

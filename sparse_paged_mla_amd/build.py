@@ -1,7 +1,9 @@
 """Build libsparse_mla.so in-tree with hipcc for gfx950.
 
 Every HIP source is compiled with packed-fp32 code generation turned off
-(the compiler would otherwise fuse ordinary float pairs into packed ops)."""
+(the compiler would otherwise fuse ordinary float pairs into packed ops), and
+with MFMA results kept in ordinary vector registers (instead of accumulation
+registers that every use must first copy out)."""
 import os
 import subprocess
 import sys
@@ -14,7 +16,8 @@ LIB = os.path.join(HERE, "libsparse_mla.so")
 SOURCES = ["api.cpp", "indexer.hip", "topk.hip", "mla_decode.hip", "lse_merge.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
-         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-mllvm", "-amdgpu-mfma-vgpr-form"]
 
 
 def _compile(src, verbose):
