@@ -62,7 +62,10 @@ __device__ __forceinline__ int64_t wave_incl_scan_i64(int64_t v, int lane) {
   return v;
 }
 
-template <class Op, int KDT, int KSTEPS, int MT>
+// MULTI: pages shorter than a step (a step's tokens span several pages).
+// A compile-time choice: with both paths in one kernel the compiler's
+// memory-wait accounting merges them and waits far more than either needs.
+template <class Op, int KDT, int KSTEPS, int MT, bool MULTI>
 __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(
     const void* __restrict__ q_idx, const float* __restrict__ w, const uint8_t* __restrict__ k_pool,
     const float* __restrict__ k_scale, int32_t num_pages, int32_t page_shift,
@@ -165,10 +168,10 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(
   };
 
   // Token tok of a step whose first token is t0 lies on the step's page
-  // tok >> page_shift when pages are no longer than a step (t0 is then a
+  // tok >> page_shift when pages are shorter than a step (t0 is then a
   // multiple of the page size), else on its only page at offset
   // (t0 mod page size) + tok.
-  const bool multi_page = page_size < STEP_TOK;
+  constexpr bool multi_page = MULTI;
 
   // The run is walked one request at a time: steps [s, s_end) of request b
   // (length L).  Within a request everything the loop needs is in scalar
@@ -353,9 +356,14 @@ static int launch_one(const IndexerArgs& a, hipStream_t stream) {
   constexpr int STEP_TOK = IdxStep<ROW_BYTES>::tok;
   const int64_t max_steps = (int64_t)a.batch * ((a.max_len + STEP_TOK - 1) / STEP_TOK);
   const int64_t grid = std::min<int64_t>((int64_t)kNumCu * kIdxWgPerCu, (max_steps + 3) / 4);
-  hipLaunchKernelGGL((indexer_kernel<Op, KDT, KSTEPS, MT>), dim3((unsigned)grid), dim3(kIdxThreads), 0, stream,
-                     a.q_idx, a.w, reinterpret_cast<const uint8_t*>(a.k_pool), a.k_scale, a.num_pages, page_shift,
-                     a.bt, a.bt_stride, a.lens, a.batch, a.max_len, a.n_heads, a.scores, a.score_stride, a.status);
+  if (a.page_size < STEP_TOK)
+    hipLaunchKernelGGL((indexer_kernel<Op, KDT, KSTEPS, MT, true>), dim3((unsigned)grid), dim3(kIdxThreads), 0, stream,
+                       a.q_idx, a.w, reinterpret_cast<const uint8_t*>(a.k_pool), a.k_scale, a.num_pages, page_shift,
+                       a.bt, a.bt_stride, a.lens, a.batch, a.max_len, a.n_heads, a.scores, a.score_stride, a.status);
+  else
+    hipLaunchKernelGGL((indexer_kernel<Op, KDT, KSTEPS, MT, false>), dim3((unsigned)grid), dim3(kIdxThreads), 0, stream,
+                       a.q_idx, a.w, reinterpret_cast<const uint8_t*>(a.k_pool), a.k_scale, a.num_pages, page_shift,
+                       a.bt, a.bt_stride, a.lens, a.batch, a.max_len, a.n_heads, a.scores, a.score_stride, a.status);
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 
