@@ -193,6 +193,56 @@ def test_scores_growing_along_the_context():
         _check_full(inp, splits, "growing logits")
 
 
+def test_fp8_growing_logits_recompute():
+    """The same growing logits on an FP8 cache: the FP8-cache kernel's own
+    recompute pass (with the segment table kept from the first pass when the
+    split has one segment, rebuilt when it has several)."""
+    _lib()
+    cfg = gen.CONFIGS["c2"].with_(batch=2, cache_dtype=gen.FP8)
+    inp = gen.make_inputs(cfg, lens=[3000, 777])
+    D = cfg.dim
+    u = gen.normals32(11, 0, 0, D)
+    u /= np.linalg.norm(u)
+    q = np.broadcast_to(u * 6.0, (2, cfg.n_heads, D)).astype(np.float32)
+    q[:, 1::2] *= -1.0
+    inp.q = gen.to_bf16_bits(q)
+    P = cfg.page_size
+    rows = np.zeros((inp.num_pages * P, D), np.float32)
+    for b in range(2):
+        for t in range(int(inp.lens[b])):
+            row = int(inp.block_table[b, t // P]) * P + t % P
+            rows[row] = u * (t / 40.0) + 0.05 * gen.normals32(12, b, t, D)
+    codes, scales = gen.to_fp8_rows(rows)
+    inp.kv = codes.reshape(inp.kv.shape)
+    inp.kv_scale = scales.reshape(inp.kv_scale.shape)
+    for splits in (1, 2, 3):   # 3000 tokens: 3, 2 and 1 segments of 1024 per split
+        _check_full(inp, splits, "growing logits fp8")
+
+
+@pytest.mark.parametrize("n_heads", [8, 40, 72])
+def test_fp8_partial_head_groups(n_heads):
+    """Head counts that leave waves, and lanes within a wave, without a head."""
+    _lib()
+    cfg = gen.CONFIGS["c3f"].with_(batch=3, n_heads=n_heads)
+    _check_full(gen.make_inputs(cfg, lens=[70, 2500, 5000]), 3, f"fp8 {n_heads} heads")
+
+
+@pytest.mark.parametrize("splits", [1, 2, 5])
+def test_fp8_dense_multi_segment(splits):
+    """Dense attention on an FP8 cache: splits longer than one segment table
+    (1024 positions) and a ragged last tile."""
+    _lib()
+    cfg = gen.CONFIGS["c2"].with_(batch=2, cache_dtype=gen.FP8)
+    _check_full(gen.make_inputs(cfg, lens=[2500, 4133]), splits, "dense fp8")
+
+
+def test_fp8_empty_splits():
+    """A small top-k spread over many splits leaves whole splits empty."""
+    _lib()
+    cfg = gen.CONFIGS["c3f"].with_(batch=2, topk=32)
+    _check_full(gen.make_inputs(cfg, lens=[40, 3000]), 4, "fp8 empty splits")
+
+
 # ------------------------------------------------------------ fault handling
 
 def test_device_faults_flag_only_the_offending_request():
