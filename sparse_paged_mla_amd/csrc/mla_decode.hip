@@ -466,10 +466,9 @@ __global__ __launch_bounds__(kDecThreads) void mla_decode_kernel(
 // and 4 + g of a 128-dim block, so lane group g holds dims 16g..16g+15 and
 // 64+16g..64+16g+15 of it: the query operand uses the same order.
 namespace f8dec {
-constexpr int kD = 576, kDC = 512, kRope = 64;
+constexpr int kD = 576, kDC = 512;
 constexpr int kRS = 608;
 constexpr int kTileBytes = kTile * kRS;
-constexpr int kChunks = kD / 16;  // 16-byte chunks per cache row
 __device__ __forceinline__ int rowbase(int r) { return r * kRS; }
 __device__ __forceinline__ int swz(int r) { return ((r >> 3) ^ (r >> 4)) & 1; }
 }  // namespace f8dec

@@ -6,26 +6,29 @@
 // entries under (key desc, index asc), a total order, so the result is unique
 // whatever order atomics land in.
 //
-// Launches per call (all on the caller's stream), over (request, chunk)
-// workgroups except the last:
-//  1. range:  each chunk's min and max key go to the workspace, and the chunk
-//             clears its share of the request's histogram and counters.
-//  2. hist:   every chunk folds the per-chunk ranges into the request's key
-//             range, picks the 11-bit digit that starts at the highest bit in
-//             which the request's keys differ (so the digit spreads whatever
-//             the score scale), histograms it in LDS and adds the histogram
-//             into the request's global one.
-//  3. filter: every chunk finds the bin b0 holding the k-th best key and
-//             streams its keys again: keys above b0 are selected outright,
-//             keys in b0 become candidates.  Each thread counts both, one
-//             block scan gives every thread its offsets and each workgroup
-//             reserves its output ranges with one atomic per kind.
-//  4. finish: one workgroup per request resolves the candidates in LDS
-//             (further 11-bit rounds on the remaining key bits, then on the
-//             token index for exact ties) and writes the k_eff indices in
-//             ascending order: they are set in an LDS bitmap over [0, L) and
-//             read back with a prefix popcount (bitonic sort when L exceeds
-//             the bitmap).
+// Launches per call (both on the caller's stream):
+//  1. collect: (request, 4096-key chunk) workgroups.  Each first derives the
+//     request's threshold key tau from a sample of its keys (all of them
+//     when the request has at most 4096, else 16 evenly spread runs of 256):
+//     one histogram of the sample over the 11 bits below the bits its keys
+//     share, and tau the lower edge of the bin holding the sample key of
+//     rank r: k when the sample is the whole request, else e + 4 sqrt(e) + 4
+//     where e = k * 4096 / L is the expected count of sampled keys at or
+//     above the request's k-th largest key, so somewhat more than k keys of
+//     the request reach tau (fewer only if the sample count falls four
+//     deviations short).  Every workgroup of a
+//     request reads the same sample and derives the same tau.  It then
+//     copies its chunk's keys >= tau, with their indices, to the chunk's own
+//     slice of the candidate buffer and writes their count (no atomics, so
+//     nothing needs clearing between calls).
+//  2. finish: one workgroup per request gathers the chunks' candidates into
+//     LDS, selects the k_eff best exactly (11-bit rounds over the key, then
+//     over the index for ties) and writes their indices in ascending order
+//     (an LDS bitmap over [0, L) and a prefix popcount).  Should tau admit
+//     fewer than k keys (the sample fell far short: vanishingly rare for any
+//     spread of scores, but adversarial orders can do it), or more than fit
+//     in LDS (huge tie groups), the same rounds run over the whole request
+//     read from the scores, so the result is exact in every case.
 #include "common.h"
 #include "launch.h"
 
@@ -39,17 +42,16 @@ constexpr int kTkChunk = kTkThreads * kTkPer;    // 4096 keys per workgroup
 constexpr int kBins = 2048;
 constexpr int kFinThreads = 1024;
 constexpr int kMaxK = 4096;
-constexpr int kCtrl = 8;                         // selected count, candidate count, digit shift
+constexpr int kSampleRuns = 16, kSampleRun = 256;
+constexpr int kSample = kSampleRuns * kSampleRun;  // keys sampled from a long request
 constexpr int kFinLdsWords = 32768;              // 128 KiB: candidates, then the bitmap
 constexpr int kCandLds = kFinLdsWords / 2;       // candidates that fit in LDS (uint2 each)
 constexpr int64_t kBitmapBits = (int64_t)kFinLdsWords * 32;
+static_assert(kSample == kTkChunk, "a collect workgroup holds one sample key per chunk key");
 
 struct TopkWs {
-  uint32_t* hist;   // [B, kBins]
-  uint32_t* ctrl;   // [B, kCtrl]
-  uint2* range;     // [B, chunks] (min key, max key)
-  uint2* cand;      // [B, cap] (key, index)
-  int64_t cap;
+  uint32_t* count;  // [B, chunks] candidates of each chunk
+  uint2* cand;      // [B, chunks, kTkChunk] (key, index), chunk c's in its own slice
   int32_t chunks;
 };
 
@@ -59,24 +61,17 @@ static inline int32_t n_chunks(int64_t max_len) { return (int32_t)std::max<int64
 size_t topk_workspace_size(int32_t batch, int64_t max_len, int32_t k) {
   (void)k;
   if (batch <= 0 || max_len < 0) return 0;
-  const size_t b = (size_t)batch;
-  return align_up(b * kBins * 4, 256) + align_up(b * kCtrl * 4, 256) + align_up(b * n_chunks(max_len) * 8, 256) +
-         align_up(b * (size_t)std::max<int64_t>(max_len, 1) * 8, 256);
+  const size_t bc = (size_t)batch * (size_t)n_chunks(max_len);
+  return align_up(bc * 4, 256) + bc * kTkChunk * 8;
 }
 
 static TopkWs carve(void* ws, int32_t batch, int64_t max_len) {
   TopkWs w;
-  const size_t b = (size_t)batch;
   uint8_t* p = reinterpret_cast<uint8_t*>(ws);
   w.chunks = n_chunks(max_len);
-  w.hist = reinterpret_cast<uint32_t*>(p);
-  p += align_up(b * kBins * 4, 256);
-  w.ctrl = reinterpret_cast<uint32_t*>(p);
-  p += align_up(b * kCtrl * 4, 256);
-  w.range = reinterpret_cast<uint2*>(p);
-  p += align_up(b * w.chunks * 8, 256);
-  w.cand = reinterpret_cast<uint2*>(p);
-  w.cap = std::max<int64_t>(max_len, 1);
+  const size_t bc = (size_t)batch * (size_t)w.chunks;
+  w.count = reinterpret_cast<uint32_t*>(p);
+  w.cand = reinterpret_cast<uint2*>(p + align_up(bc * 4, 256));
   return w;
 }
 
@@ -95,15 +90,7 @@ __device__ __forceinline__ int xcd_remap(int bid, int n) {
   return xcd < r ? xcd * (q + 1) + slot : r * (q + 1) + (xcd - r) * q + slot;
 }
 
-// Block reduction helpers (any block size that is a multiple of 64).
-__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
-  for (int o = 32; o > 0; o >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, o));
-  return v;
-}
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-  for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o));
-  return v;
-}
+// Block scan helpers (any block size that is a multiple of 64).
 __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
   const int lane = threadIdx.x & 63;
   for (int o = 1; o < 64; o <<= 1) {
@@ -125,27 +112,26 @@ __device__ __forceinline__ uint32_t block_incl_scan(uint32_t v, uint32_t* tmp) {
   return v + pre;
 }
 
-// The digit that starts at the highest bit where the request's keys differ.
-__device__ __forceinline__ int digit_shift(uint32_t kmin, uint32_t kmax) {
+// Radix rounds over a key set whose smallest and largest keys are known
+// start at the highest bit in which those two differ: the bits above are
+// common to every key (returned as prefix and mask), and the first 11-bit
+// round spreads the keys instead of piling them into a few bins.
+__device__ __forceinline__ int first_round_top(uint32_t kmin, uint32_t kmax, uint32_t* pre, uint32_t* mask) {
   const uint32_t diff = kmin ^ kmax;
-  const int hb = diff ? 31 - __clz(diff) : 0;
-  return max(hb + 1 - 11, 0);
+  const int top = diff ? 32 - __clz(diff) : 1;  // bits [0, top) can differ
+  const int hi = max(top, 11);
+  *mask = hi >= 32 ? 0u : ~((1u << hi) - 1u);
+  *pre = kmin & *mask;
+  return hi;
 }
 
-__device__ __forceinline__ void request_range(const uint2* rng, int n, uint32_t* s_mm) {
-  // Called by all threads; result in s_mm[0..1] after the trailing barrier.
-  uint32_t lo = 0xFFFFFFFFu, hi = 0u;
-  for (int i = threadIdx.x; i < n; i += blockDim.x) {
-    const uint2 r = rng[i];
-    lo = min(lo, r.x);
-    hi = max(hi, r.y);
-  }
-  lo = wave_min_u32(lo);
-  hi = wave_max_u32(hi);
-  if (threadIdx.x == 0) { s_mm[0] = 0xFFFFFFFFu; s_mm[1] = 0u; }
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) { atomicMin(&s_mm[0], lo); atomicMax(&s_mm[1], hi); }
-  __syncthreads();
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  for (int o = 32; o > 0; o >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, o));
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o));
+  return v;
 }
 
 // Thread-to-key mapping of a chunk: key j of thread tid is t0 + j*256 + tid
@@ -160,68 +146,6 @@ __device__ __forceinline__ void load_chunk(const float* s, int64_t t0, int64_t t
   }
 #pragma unroll
   for (int j = 0; j < kTkPer; ++j) key[j] = order_key(v[j]);
-}
-
-__global__ __launch_bounds__(kTkThreads) void topk_range_kernel(const float* __restrict__ scores, int64_t stride,
-                                                                const int32_t* __restrict__ lens, int64_t max_len,
-                                                                int32_t k, TopkWs ws) {
-  __shared__ uint32_t s_mm[2];
-  const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  const int b = logical / ws.chunks, chunk = logical % ws.chunks;
-  const int32_t L = lens[b];
-  if (!len_ok(L, max_len) || L <= k) return;
-  const int n_act = (int)((L + kTkChunk - 1) / kTkChunk);
-  if (chunk >= n_act) return;
-  // This chunk's share of the request's histogram (and the counters, chunk 0).
-  const int per = (kBins + n_act - 1) / n_act;
-  for (int i = chunk * per + threadIdx.x; i < min(kBins, (chunk + 1) * per); i += kTkThreads)
-    ws.hist[(int64_t)b * kBins + i] = 0u;
-  if (chunk == 0 && threadIdx.x < kCtrl) ws.ctrl[(int64_t)b * kCtrl + threadIdx.x] = 0u;
-  const int64_t t0 = (int64_t)chunk * kTkChunk, t1 = min((int64_t)L, t0 + kTkChunk);
-  uint32_t key[kTkPer];
-  bool in[kTkPer];
-  load_chunk(scores + (int64_t)b * stride, t0, t1, key, in);
-  uint32_t lo = 0xFFFFFFFFu, hi = 0u;
-#pragma unroll
-  for (int j = 0; j < kTkPer; ++j) {
-    if (in[j]) { lo = min(lo, key[j]); hi = max(hi, key[j]); }
-  }
-  lo = wave_min_u32(lo);
-  hi = wave_max_u32(hi);
-  if (threadIdx.x == 0) { s_mm[0] = 0xFFFFFFFFu; s_mm[1] = 0u; }
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) { atomicMin(&s_mm[0], lo); atomicMax(&s_mm[1], hi); }
-  __syncthreads();
-  if (threadIdx.x == 0) ws.range[(int64_t)b * ws.chunks + chunk] = make_uint2(s_mm[0], s_mm[1]);
-}
-
-__global__ __launch_bounds__(kTkThreads) void topk_hist_kernel(const float* __restrict__ scores, int64_t stride,
-                                                               const int32_t* __restrict__ lens, int64_t max_len,
-                                                               int32_t k, TopkWs ws) {
-  __shared__ uint32_t h[kBins];
-  __shared__ uint32_t s_mm[2];
-  const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  const int b = logical / ws.chunks, chunk = logical % ws.chunks;
-  const int32_t L = lens[b];
-  if (!len_ok(L, max_len) || L <= k) return;
-  const int n_act = (int)((L + kTkChunk - 1) / kTkChunk);
-  if (chunk >= n_act) return;
-  const int64_t t0 = (int64_t)chunk * kTkChunk, t1 = min((int64_t)L, t0 + kTkChunk);
-  uint32_t key[kTkPer];
-  bool in[kTkPer];
-  load_chunk(scores + (int64_t)b * stride, t0, t1, key, in);
-  for (int i = threadIdx.x; i < kBins; i += kTkThreads) h[i] = 0u;
-  request_range(ws.range + (int64_t)b * ws.chunks, n_act, s_mm);
-  const int sh = digit_shift(s_mm[0], s_mm[1]);
-#pragma unroll
-  for (int j = 0; j < kTkPer; ++j)
-    if (in[j]) atomicAdd(&h[(key[j] >> sh) & (kBins - 1)], 1u);
-  __syncthreads();
-  uint32_t* gh = ws.hist + (int64_t)b * kBins;
-  for (int i = threadIdx.x; i < kBins; i += kTkThreads) {
-    const uint32_t c = h[i];
-    if (c) atomicAdd(gh + i, c);
-  }
 }
 
 // Block-wide search over a histogram in LDS from the top bin down: the bin x
@@ -272,62 +196,101 @@ __device__ void find_bin_asc(const uint32_t* h, uint32_t need, uint32_t* tmp, ui
   __syncthreads();
 }
 
-__global__ __launch_bounds__(kTkThreads) void topk_filter_kernel(const float* __restrict__ scores, int64_t stride,
-                                                                 const int32_t* __restrict__ lens, int64_t max_len,
-                                                                 int32_t k, TopkWs ws, int32_t* __restrict__ out_idx) {
+// Threshold key tau of a request whose length exceeds k (see the top of the
+// file); called by all kTkThreads threads, barriers inside.
+__device__ uint32_t request_tau(const float* __restrict__ s, int32_t L, int32_t k, uint32_t* h, uint32_t* tmp,
+                                uint32_t* res, uint32_t* s_mm) {
+  const int tid = threadIdx.x;
+  const bool whole = L <= kSample;
+  uint32_t key[kTkPer];
+  bool in[kTkPer];
+  {
+    float v[kTkPer];
+#pragma unroll
+    for (int j = 0; j < kTkPer; ++j) {
+      const int e = j * kTkThreads + tid;
+      int64_t t;
+      if (whole) {
+        t = e;
+      } else {
+        const int64_t run = e / kSampleRun;
+        t = run * ((int64_t)L - kSampleRun) / (kSampleRuns - 1) + e % kSampleRun;
+      }
+      in[j] = t < L;
+      v[j] = s[in[j] ? t : 0];
+    }
+#pragma unroll
+    for (int j = 0; j < kTkPer; ++j) key[j] = order_key(v[j]);
+  }
+  uint32_t lo_k = 0xFFFFFFFFu, hi_k = 0u;
+#pragma unroll
+  for (int j = 0; j < kTkPer; ++j)
+    if (in[j]) { lo_k = min(lo_k, key[j]); hi_k = max(hi_k, key[j]); }
+  lo_k = wave_min_u32(lo_k);
+  hi_k = wave_max_u32(hi_k);
+  if (tid == 0) { s_mm[0] = 0xFFFFFFFFu; s_mm[1] = 0u; }
+  for (int i = tid; i < kBins; i += kTkThreads) h[i] = 0u;
+  __syncthreads();
+  if ((tid & 63) == 0) { atomicMin(&s_mm[0], lo_k); atomicMax(&s_mm[1], hi_k); }
+  __syncthreads();
+  uint32_t pre, mask;
+  const int hi = first_round_top(s_mm[0], s_mm[1], &pre, &mask);
+  const int lo = hi - 11;
+  // Rank r of tau's bin in the sample: k for the whole request, else
+  // e + 4 sqrt(e) + 4 with e = k * kSample / L.
+  uint32_t need = (uint32_t)k;
+  if (!whole) {
+    const float e = (float)k * (float)kSample / (float)L;
+    const float r = e + 4.f * sqrtf(e) + 4.f;
+    need = (uint32_t)min((int64_t)kSample, (int64_t)ceilf(r));
+  }
+#pragma unroll
+  for (int j = 0; j < kTkPer; ++j)
+    if (in[j]) atomicAdd(&h[(key[j] >> lo) & 2047u], 1u);
+  __syncthreads();
+  find_bin_desc<kBins, kTkThreads>(h, need, tmp, res);
+  return pre | (res[0] << lo);
+}
+
+// (request, chunk) workgroups: every key >= tau goes to the chunk's slice of
+// the candidate buffer, in chunk order (one block scan), and the chunk's
+// count to its slot.
+__global__ __launch_bounds__(kTkThreads) void topk_collect_kernel(const float* __restrict__ scores, int64_t stride,
+                                                                  const int32_t* __restrict__ lens, int64_t max_len,
+                                                                  int32_t k, TopkWs ws) {
   __shared__ uint32_t h[kBins];
   __shared__ uint32_t tmp[kTkThreads / 64];
   __shared__ uint32_t res[2];
   __shared__ uint32_t s_mm[2];
-  __shared__ uint32_t base_sel, base_cnd;
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
   const int b = logical / ws.chunks, chunk = logical % ws.chunks;
   const int32_t L = lens[b];
   if (!len_ok(L, max_len) || L <= k) return;
   const int n_act = (int)((L + kTkChunk - 1) / kTkChunk);
   if (chunk >= n_act) return;
+  const float* s = scores + (int64_t)b * stride;
   const int64_t t0 = (int64_t)chunk * kTkChunk, t1 = min((int64_t)L, t0 + kTkChunk);
   uint32_t key[kTkPer];
   bool in[kTkPer];
-  load_chunk(scores + (int64_t)b * stride, t0, t1, key, in);
-  const uint32_t* gh = ws.hist + (int64_t)b * kBins;
-  for (int i = threadIdx.x; i < kBins; i += kTkThreads) h[i] = gh[i];
-  request_range(ws.range + (int64_t)b * ws.chunks, n_act, s_mm);
-  const int sh = digit_shift(s_mm[0], s_mm[1]);
-  find_bin_desc<kBins, kTkThreads>(h, (uint32_t)k, tmp, res);
-  const uint32_t b0 = res[0];
-  if (chunk == 0 && threadIdx.x == 0) ws.ctrl[(int64_t)b * kCtrl + 2] = (uint32_t)sh;
-  // Two-phase compaction: count this thread's selected keys (above b0) and
-  // candidates (in b0), one block scan of both counts packed in a word, one
-  // global atomic per kind for the whole chunk, then direct writes.
-  uint32_t cs = 0, cc = 0;
+  load_chunk(s, t0, t1, key, in);
+  const uint32_t tau = request_tau(s, L, k, h, tmp, res, s_mm);
+  uint32_t c = 0;
+#pragma unroll
+  for (int j = 0; j < kTkPer; ++j) c += (in[j] && key[j] >= tau) ? 1u : 0u;
+  const uint32_t incl = block_incl_scan<kTkThreads>(c, tmp);
+  const int64_t slot = (int64_t)b * ws.chunks + chunk;
+  if (threadIdx.x == kTkThreads - 1) ws.count[slot] = incl;
+  uint32_t p = incl - c;
+  uint2* cb = ws.cand + slot * kTkChunk;
 #pragma unroll
   for (int j = 0; j < kTkPer; ++j) {
-    const uint32_t d = (key[j] >> sh) & (kBins - 1);
-    cs += (in[j] && d > b0) ? 1u : 0u;
-    cc += (in[j] && d == b0) ? 1u : 0u;
-  }
-  const uint32_t packed = (cs << 16) | cc;  // at most kTkPer each
-  const uint32_t incl = block_incl_scan<kTkThreads>(packed, tmp);
-  if (threadIdx.x == kTkThreads - 1) {
-    const uint32_t ns = incl >> 16, nc = incl & 0xFFFFu;
-    base_sel = ns ? atomicAdd(ws.ctrl + (int64_t)b * kCtrl + 0, ns) : 0u;
-    base_cnd = nc ? atomicAdd(ws.ctrl + (int64_t)b * kCtrl + 1, nc) : 0u;
-  }
-  __syncthreads();
-  uint32_t ps = base_sel + ((incl - packed) >> 16), pc = base_cnd + ((incl - packed) & 0xFFFFu);
-  int32_t* out = out_idx + (int64_t)b * k;
-  uint2* cb = ws.cand + (int64_t)b * ws.cap;
-#pragma unroll
-  for (int j = 0; j < kTkPer; ++j) {
-    const uint32_t d = (key[j] >> sh) & (kBins - 1);
     const int64_t t = t0 + (int64_t)j * kTkThreads + threadIdx.x;
-    if (in[j] && d > b0) out[ps++] = (int32_t)t;
-    if (in[j] && d == b0) cb[pc++] = make_uint2(key[j], (uint32_t)t);
+    if (in[j] && key[j] >= tau) cb[p++] = make_uint2(key[j], (uint32_t)t);
   }
 }
 
-__global__ __launch_bounds__(kFinThreads) void topk_finish_kernel(const int32_t* __restrict__ lens, int64_t max_len,
+__global__ __launch_bounds__(kFinThreads) void topk_finish_kernel(const float* __restrict__ scores, int64_t stride,
+                                                                  const int32_t* __restrict__ lens, int64_t max_len,
                                                                   int32_t k, TopkWs ws, int32_t* __restrict__ out_idx,
                                                                   int32_t* __restrict__ status) {
   __shared__ uint32_t big[kFinLdsWords];   // candidates (uint2), later the bitmap
@@ -335,7 +298,7 @@ __global__ __launch_bounds__(kFinThreads) void topk_finish_kernel(const int32_t*
   __shared__ int32_t sel[kMaxK];
   __shared__ uint32_t tmp[kFinThreads / 64];
   __shared__ uint32_t res[2];
-  __shared__ uint32_t s_mm[2];
+  __shared__ uint32_t coff[kFinThreads];  // chunk offsets in the gathered candidate list
   __shared__ uint32_t cnt;
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
@@ -350,28 +313,64 @@ __global__ __launch_bounds__(kFinThreads) void topk_finish_kernel(const int32_t*
     for (int j = tid; j < k; j += kFinThreads) out[j] = j < L ? j : -1;
     return;
   }
-  const int sh = (int)ws.ctrl[(int64_t)b * kCtrl + 2];  // the digit shift the filter used
-  const uint32_t n_gt = ws.ctrl[(int64_t)b * kCtrl + 0];
-  const uint32_t n_c = ws.ctrl[(int64_t)b * kCtrl + 1];
-  // Candidates: in LDS when they fit, else read from the workspace.
-  const uint2* cb = ws.cand + (int64_t)b * ws.cap;
-  uint2* lc = reinterpret_cast<uint2*>(big);
-  const bool in_lds = n_c <= (uint32_t)kCandLds;
-  if (in_lds) {
-    for (uint32_t j = tid; j < n_c; j += kFinThreads) lc[j] = cb[j];
-    cb = lc;
-  }
+  // Candidates: the chunks' keys >= tau gathered into LDS, or, should fewer
+  // than k or more than LDS holds have reached tau (or the request have more
+  // chunks than this workgroup has threads), every key of the request read
+  // from the scores.
+  const int n_act = (int)((L + kTkChunk - 1) / kTkChunk);
+  const int64_t slot0 = (int64_t)b * ws.chunks;
+  const uint32_t c_mine = (tid < n_act) ? ws.count[slot0 + tid] : 0u;
+  const uint32_t c_incl = block_incl_scan<kFinThreads>(c_mine, tmp);
+  if (tid < n_act) coff[tid] = c_incl - c_mine;
+  if (tid == kFinThreads - 1) res[0] = c_incl;
   __syncthreads();
-  uint32_t need = (uint32_t)k - n_gt;  // >= 1 places for keys of bin b0
-  // Key rounds over the bits below the first digit, 11 at a time.
-  uint32_t kpre = 0, kmask = 0;  // determined low-bit prefix
-  for (int hi = sh; hi > 0; hi -= 11) {
+  const uint32_t n_cand = res[0];
+  const bool whole = n_cand < (uint32_t)k || n_cand > (uint32_t)kCandLds || n_act > kFinThreads;
+  const uint32_t n_c = whole ? (uint32_t)L : n_cand;
+  const float* srow = scores + (int64_t)b * stride;
+  uint2* lc = reinterpret_cast<uint2*>(big);
+  uint32_t cmax = 0u;  // largest candidate key (all candidates are >= tau)
+  if (!whole) {
+    // Candidate j lives in the last chunk c with coff[c] <= j (binary search).
+    for (uint32_t j = tid; j < n_cand; j += kFinThreads) {
+      int lo_c = 0, hi_c = n_act - 1;
+      while (lo_c < hi_c) {
+        const int mid = (lo_c + hi_c + 1) >> 1;
+        if (coff[mid] <= j) lo_c = mid; else hi_c = mid - 1;
+      }
+      const uint2 e = ws.cand[(slot0 + lo_c) * kTkChunk + (j - coff[lo_c])];
+      lc[j] = e;
+      cmax = max(cmax, e.x);
+    }
+  }
+  cmax = wave_max_u32(cmax);
+  uint32_t cmin = 0xFFFFFFFFu;  // smallest candidate key
+  if (!whole)
+    for (uint32_t j = tid; j < n_c; j += kFinThreads) cmin = min(cmin, lc[j].x);
+  cmin = wave_min_u32(cmin);
+  if (tid == 0) { res[0] = 0u; res[1] = 0xFFFFFFFFu; }
+  __syncthreads();
+  if ((tid & 63) == 0) { atomicMax(&res[0], cmax); atomicMin(&res[1], cmin); }
+  __syncthreads();
+  cmax = res[0];
+  cmin = res[1];
+  __syncthreads();
+  const uint2* cb = lc;
+  auto cand = [&](uint32_t j) -> uint2 { return whole ? make_uint2(order_key(srow[j]), j) : cb[j]; };
+  uint32_t need = (uint32_t)k;
+  // Key rounds, 11 bits at a time from the highest bit in which the
+  // candidates can differ (they lie in [tau, largest collected key]; all 32
+  // bits for the whole request): the k-th best key T among the candidates.
+  uint32_t kpre = 0, kmask = 0;  // determined high-bit prefix
+  int hi0 = 32;
+  if (!whole) hi0 = first_round_top(cmin, cmax, &kpre, &kmask);
+  for (int hi = hi0; hi > 0; hi -= 11) {
     const int lo = max(hi - 11, 0);
     const uint32_t wmask = (1u << (hi - lo)) - 1u;
     for (int i = tid; i < kBins; i += kFinThreads) h[i] = 0u;
     __syncthreads();
     for (uint32_t j = tid; j < n_c; j += kFinThreads) {
-      const uint32_t key = cb[j].x;
+      const uint32_t key = cand(j).x;
       if ((key & kmask) == kpre) atomicAdd(&h[(key >> lo) & wmask], 1u);
     }
     __syncthreads();
@@ -380,15 +379,14 @@ __global__ __launch_bounds__(kFinThreads) void topk_finish_kernel(const int32_t*
     kmask |= wmask << lo;
     need -= res[1];
   }
-  // Threshold key T: candidates share bits >= sh (they are all in bin b0 of a
-  // request whose keys agree above the digit); the low bits are kpre.
-  // Among keys equal to T take the `need` lowest indices (index threshold I, inclusive).
+  // T = kpre.  Among keys equal to T take the `need` lowest indices (index
+  // threshold I, inclusive).
   uint32_t I = 0xFFFFFFFFu;
   {
     for (int i = tid; i < kBins; i += kFinThreads) h[i] = 0u;
     __syncthreads();
     uint32_t n_eq_local = 0;
-    for (uint32_t j = tid; j < n_c; j += kFinThreads) n_eq_local += ((cb[j].x & kmask) == kpre) ? 1u : 0u;
+    for (uint32_t j = tid; j < n_c; j += kFinThreads) n_eq_local += (cand(j).x == kpre) ? 1u : 0u;
     const uint32_t n_eq = block_incl_scan<kFinThreads>(n_eq_local, tmp);  // last thread holds the total
     if (tid == kFinThreads - 1) res[0] = n_eq;
     __syncthreads();
@@ -402,8 +400,8 @@ __global__ __launch_bounds__(kFinThreads) void topk_finish_kernel(const int32_t*
         for (int i = tid; i < kBins; i += kFinThreads) h[i] = 0u;
         __syncthreads();
         for (uint32_t j = tid; j < n_c; j += kFinThreads) {
-          const uint2 e = cb[j];
-          if ((e.x & kmask) == kpre && (e.y & imask) == ipre) atomicAdd(&h[(e.y >> lo) & wmask], 1u);
+          const uint2 e = cand(j);
+          if (e.x == kpre && (e.y & imask) == ipre) atomicAdd(&h[(e.y >> lo) & wmask], 1u);
         }
         __syncthreads();
         find_bin_asc<kBins, kFinThreads>(h, need, tmp, res);
@@ -414,14 +412,12 @@ __global__ __launch_bounds__(kFinThreads) void topk_finish_kernel(const int32_t*
       I = ipre;
     }
   }
-  // Gather the k indices: the n_gt already in the output row plus the chosen candidates.
-  if (tid == 0) cnt = n_gt;
-  for (uint32_t j = tid; j < n_gt; j += kFinThreads) sel[j] = out[j];
+  // Gather the k indices: candidates above T, and those equal to T up to index I.
+  if (tid == 0) cnt = 0u;
   __syncthreads();
   for (uint32_t j = tid; j < n_c; j += kFinThreads) {
-    const uint2 e = cb[j];
-    const uint32_t low = e.x & kmask;
-    if (low > kpre || (low == kpre && e.y <= I)) {
+    const uint2 e = cand(j);
+    if (e.x > kpre || (e.x == kpre && e.y <= I)) {
       const uint32_t p = atomicAdd(&cnt, 1u);
       if (p < (uint32_t)k) sel[p] = (int32_t)e.y;
     }
@@ -478,14 +474,10 @@ int launch_topk(const TopkArgs& a, hipStream_t s) {
   TopkWs ws = carve(a.workspace, a.batch, a.max_len);
   const int64_t grid = (int64_t)a.batch * ws.chunks;
   if (grid > 0x7FFFFFFF) return -2;
-  hipLaunchKernelGGL(topk_range_kernel, dim3((unsigned)grid), dim3(kTkThreads), 0, s, a.scores, a.score_stride,
+  hipLaunchKernelGGL(topk_collect_kernel, dim3((unsigned)grid), dim3(kTkThreads), 0, s, a.scores, a.score_stride,
                      a.lens, a.max_len, a.k, ws);
-  hipLaunchKernelGGL(topk_hist_kernel, dim3((unsigned)grid), dim3(kTkThreads), 0, s, a.scores, a.score_stride,
-                     a.lens, a.max_len, a.k, ws);
-  hipLaunchKernelGGL(topk_filter_kernel, dim3((unsigned)grid), dim3(kTkThreads), 0, s, a.scores, a.score_stride,
-                     a.lens, a.max_len, a.k, ws, a.out_idx);
-  hipLaunchKernelGGL(topk_finish_kernel, dim3((unsigned)a.batch), dim3(kFinThreads), 0, s, a.lens, a.max_len, a.k,
-                     ws, a.out_idx, a.status);
+  hipLaunchKernelGGL(topk_finish_kernel, dim3((unsigned)a.batch), dim3(kFinThreads), 0, s, a.scores, a.score_stride,
+                     a.lens, a.max_len, a.k, ws, a.out_idx, a.status);
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 

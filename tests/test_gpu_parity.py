@@ -153,6 +153,28 @@ def test_topk_big_tie_groups(max_len):
     parity.check_topk_exact(idx, S, np.array(lens), 2048, f"big ties max_len={max_len}")
 
 
+def test_topk_sample_miss_falls_back():
+    """Rows whose sampled positions hold the largest keys: the threshold from
+    the sample then admits fewer than k keys, and the finish must select over
+    the whole request.  The sample positions are the top-k kernel's own (16
+    runs of 256 keys starting evenly over [0, L - 256]); also a row sorted in
+    decreasing order and one sorted in increasing order."""
+    rng = np.random.default_rng(23)
+    lens = [100000, 250000, 90000, 90000]
+    S = rng.random((4, 250048)).astype(np.float32)
+    for r in (0, 1):
+        L = lens[r]
+        for run in range(16):
+            t0 = run * (L - 256) // 15
+            S[r, t0:t0 + 256] = 10.0 + rng.random(256).astype(np.float32)
+    S[2, :90000] = np.sort(S[2, :90000])[::-1]
+    S[3, :90000] = np.sort(S[3, :90000])
+    for k in (2048, 32):
+        idx, st = _gpu_topk(S, lens, k)
+        assert not st.any()
+        parity.check_topk_exact(idx, S, np.array(lens), k, f"sample miss k={k}")
+
+
 def test_topk_bad_len_flags_request():
     S = np.random.default_rng(0).standard_normal((3, 256)).astype(np.float32)
     spm = _lib()
