@@ -11,6 +11,10 @@ namespace spmla {
 constexpr int kMergeThreads = 256;
 constexpr int kMaxSplits = 64;
 
+// SP > 0: exactly SP splits and d == 512, with each lane's partial slices
+// loaded before (and so overlapping) the wait for the split lse values;
+// SP == 0: any split count and d.
+template <int SP>
 __global__ __launch_bounds__(kMergeThreads) void lse_merge_kernel(const float* __restrict__ o_part,
                                                                   const float* __restrict__ lse_part, int32_t batch,
                                                                   int32_t splits, int32_t n_heads, int32_t d,
@@ -21,6 +25,19 @@ __global__ __launch_bounds__(kMergeThreads) void lse_merge_kernel(const float* _
   const int64_t row = (int64_t)blockIdx.x * (kMergeThreads / 64) + wid;
   if (row >= (int64_t)batch * n_heads) return;
   const int64_t b = row / n_heads, h = row % n_heads;
+  if constexpr (SP > 0) {
+    splits = SP;
+    d = 512;
+  }
+  // Partial slices of this lane (SP > 0): dims 4*lane + 256*i of split sp.
+  float4 pv[SP > 0 ? SP : 1][2];
+  if constexpr (SP > 0) {
+#pragma unroll
+    for (int sp = 0; sp < SP; ++sp)
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        pv[sp][i] = *reinterpret_cast<const float4*>(o_part + ((b * SP + sp) * n_heads + h) * 512 + lane * 4 + 256 * i);
+  }
   // Lane s < splits holds lse of split s.
   float my = -INFINITY;
   bool nan_seen = false;
@@ -45,15 +62,30 @@ __global__ __launch_bounds__(kMergeThreads) void lse_merge_kernel(const float* _
   const float L = M + logf(sum);
   wsh[wid][lane] = e / sum;  // = exp(lse_s - L); the wave's own slots only
   __builtin_amdgcn_wave_barrier();
-  for (int i = lane * 4; i < d; i += 256) {
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int sp = 0; sp < splits; ++sp) {
-      const float ws = wsh[wid][sp];
-      if (ws == 0.f) continue;
-      const float4 v = *reinterpret_cast<const float4*>(o_part + ((b * splits + sp) * n_heads + h) * d + i);
-      acc.x += ws * v.x; acc.y += ws * v.y; acc.z += ws * v.z; acc.w += ws * v.w;
+  if constexpr (SP > 0) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int sp = 0; sp < SP; ++sp) {
+        const float ws = wsh[wid][sp];
+        if (ws == 0.f) continue;  // an empty split: its partial (perhaps never written) is not used
+        const float4 v = pv[sp][i];
+        acc.x += ws * v.x; acc.y += ws * v.y; acc.z += ws * v.z; acc.w += ws * v.w;
+      }
+      *reinterpret_cast<float4*>(orow + lane * 4 + 256 * i) = acc;
     }
-    *reinterpret_cast<float4*>(orow + i) = acc;
+  } else {
+    for (int i = lane * 4; i < d; i += 256) {
+      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int sp = 0; sp < splits; ++sp) {
+        const float ws = wsh[wid][sp];
+        if (ws == 0.f) continue;
+        const float4 v = *reinterpret_cast<const float4*>(o_part + ((b * splits + sp) * n_heads + h) * d + i);
+        acc.x += ws * v.x; acc.y += ws * v.y; acc.z += ws * v.z; acc.w += ws * v.w;
+      }
+      *reinterpret_cast<float4*>(orow + i) = acc;
+    }
   }
   if (lane == 0) lse[row] = L;
 }
@@ -64,8 +96,14 @@ int launch_merge(const MergeArgs& a, hipStream_t s) {
   if (a.num_splits > kMaxSplits) return -2;
   const int64_t grid = (rows + (kMergeThreads / 64) - 1) / (kMergeThreads / 64);
   if (grid > 0x7FFFFFFF) return -2;
-  hipLaunchKernelGGL(lse_merge_kernel, dim3((unsigned)grid), dim3(kMergeThreads), 0, s, a.o_part, a.lse_part, a.batch,
-                     a.num_splits, a.n_heads, a.d, a.o, a.lse);
+#define SPMLA_MERGE(SPN)                                                                                       \
+  hipLaunchKernelGGL(lse_merge_kernel<SPN>, dim3((unsigned)grid), dim3(kMergeThreads), 0, s, a.o_part, a.lse_part, \
+                     a.batch, a.num_splits, a.n_heads, a.d, a.o, a.lse)
+  if (a.d == 512 && a.num_splits == 2) SPMLA_MERGE(2);
+  else if (a.d == 512 && a.num_splits == 4) SPMLA_MERGE(4);
+  else if (a.d == 512 && a.num_splits == 8) SPMLA_MERGE(8);
+  else SPMLA_MERGE(0);
+#undef SPMLA_MERGE
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 

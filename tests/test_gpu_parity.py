@@ -363,15 +363,19 @@ def test_k_ge_len_equals_dense():
 
 # --------------------------------------------------------------- lse merge only
 
-def test_merge_matches_oracle_on_random_partials():
+@pytest.mark.parametrize("S", [2, 4, 5, 8])
+def test_merge_matches_oracle_on_random_partials(S):
+    """Split counts with a specialised kernel (2, 4, 8 at d = 512) and without
+    (5); empty splits hold NaN partials, which must not be used."""
     spm = _lib()
     rng = np.random.default_rng(3)
-    B, S, H, d = 3, 5, 16, 512
+    B, H, d = 3, 16, 512
     op = rng.standard_normal((B, S, H, d)).astype(np.float32)
     lp = (rng.standard_normal((B, S, H)) * 4).astype(np.float32)
     lp[0, 1:, :] = -np.inf                 # only split 0 non-empty
+    op[0, 1:, :, :] = np.nan               # never written by an empty split
     lp[1, :, 3] = -np.inf                  # a fully empty row
-    lp[2, 2, 5] = np.nan                   # NaN propagates
+    lp[2, S - 1, 5] = np.nan               # NaN propagates
     o = torch.empty(B, H, d, device="cuda")
     l = torch.empty(B, H, device="cuda")
     spm.lse_merge(torch.from_numpy(op).cuda(), torch.from_numpy(lp).cuda(), o, l)
