@@ -30,6 +30,8 @@ namespace spmla {
 constexpr int kIdxThreads = 256;
 constexpr int kIdxStepBytes = 8192;     // key bytes a wave fetches per step
 constexpr int kIdxWgPerCu = 2;          // resident workgroups per compute unit
+constexpr int kIdxLdsPerWg = 160 * 1024 / kIdxWgPerCu;
+constexpr int kIdxMaxHeldSteps = 40;    // steps of scores a wave holds in LDS before writing them
 constexpr int kNumCu = 256;
 
 // Tokens a wave handles per step: 8 KiB of keys, at least one 16-token MFMA block.
@@ -91,8 +93,15 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(
   const int page_size = 1 << page_shift;
   const int64_t bt_cap = (int64_t)bt_stride * page_size;
 
+  // Scores are held in LDS and written once a wave's run (or its part in one
+  // request) ends, or when HELD steps are waiting: the stores then come after
+  // nearly all of the grid's key reads instead of between them, where each
+  // small write costs the reads far more than its bytes.
+  constexpr int STAGE_BYTES = 4 * STEP_TOK * LROW;
+  constexpr int HELD_FIT = (kIdxLdsPerWg - STAGE_BYTES) / (4 * STEP_TOK * 4);
+  constexpr int HELD = HELD_FIT < 1 ? 1 : HELD_FIT > kIdxMaxHeldSteps ? kIdxMaxHeldSteps : HELD_FIT;
   __shared__ __attribute__((aligned(16))) uint8_t stage[4][STEP_TOK * LROW];
-  __shared__ float step_scores[4][STEP_TOK];  // a step's scores, written out by the whole wave at once
+  __shared__ __attribute__((aligned(16))) float held[4][HELD * STEP_TOK];
 
   const int lane = threadIdx.x & 63;
   // Wave-uniform values are kept in scalar registers: the run bounds, the
@@ -184,6 +193,8 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(
     const int64_t s_end = min(steps_of(L), s + todo);
     const int64_t n = s_end - s;
     load_query(b);
+    int n_held = 0;     // steps whose scores wait in held[wv]
+    int64_t t_held = 0; // first token of those steps (they are consecutive)
     const int32_t* btb = bt + (int64_t)b * bt_stride;
     float* sc_out = scores + (int64_t)b * score_stride;
     const int64_t last_page = ((int64_t)L - 1) >> page_shift;
@@ -252,6 +263,24 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(
       bad_tok = bad;
       if (__builtin_expect(__any(bad), 0) && bad && status) atomicOr(status + b, kBadPage);
     };
+    // The whole wave writes the held scores with 16-byte stores.
+    auto write_held = [&]() __attribute__((always_inline)) {
+      __builtin_amdgcn_wave_barrier();
+      const int cnt = n_held * STEP_TOK;
+      for (int i = lane * 4; i < cnt; i += 256) {
+        const int64_t t = t_held + i;
+        const float4 v4 = *reinterpret_cast<const float4*>(&held[wv][i]);
+        if (t + 3 < L) {
+          *reinterpret_cast<float4*>(sc_out + t) = v4;
+        } else {
+          if (t < L) sc_out[t] = v4.x;
+          if (t + 1 < L) sc_out[t + 1] = v4.y;
+          if (t + 2 < L) sc_out[t + 2] = v4.z;
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+      n_held = 0;
+    };
     auto consume = [&](int64_t si, const uint32_t (*raw)[4], float sc, int bad_tok) __attribute__((always_inline)) {
       const int64_t t0 = si * STEP_TOK;
       // Transpose through the wave's own LDS rows (padded by 16 bytes).
@@ -302,12 +331,10 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(
         v = wave_sum_xor16_32(v);
         const float tsc = __shfl(sc, tok);
         const bool bad = __shfl(bad_tok, tok) != 0;
-        if (g == 0) step_scores[wv][tok] = bad ? __uint_as_float(0x7FC00000u) : v * tsc;
+        if (g == 0) held[wv][n_held * STEP_TOK + tok] = bad ? __uint_as_float(0x7FC00000u) : v * tsc;
       }
-      // One 256-byte store per step instead of a 64-byte store per 16 tokens.
-      __builtin_amdgcn_wave_barrier();
-      if (lane < STEP_TOK && t0 + lane < L) sc_out[t0 + lane] = step_scores[wv][lane];
-      __builtin_amdgcn_wave_barrier();
+      if (n_held == 0) t_held = t0;
+      if (++n_held == HELD) write_held();
     };
 
     // Software pipeline, per step: the block-table entries of the step two
@@ -333,6 +360,7 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(
       consume(s + k + 1, raw_b, sc_b, bad_b);
     }
     if (k < n) consume(s + k, raw_a, sc_a, bad_a);
+    if (n_held > 0) write_held();
     __builtin_amdgcn_s_waitcnt(0);  // the loads of a step past the run are done with
 
     todo -= n;
