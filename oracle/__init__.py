@@ -32,6 +32,12 @@ def _load():
     lib.oracle_fp8_e4m3_value.argtypes = [ctypes.c_uint8]
     lib.oracle_bf16_value.restype = d
     lib.oracle_bf16_value.argtypes = [ctypes.c_uint16]
+    lib.oracle_fp8_e4m3_encode_array.restype = None
+    lib.oracle_fp8_e4m3_encode_array.argtypes = [vp, i64, vp]
+    lib.oracle_bf16_encode_array.restype = None
+    lib.oracle_bf16_encode_array.argtypes = [vp, i64, vp]
+    lib.oracle_cache_append.restype = ctypes.c_int
+    lib.oracle_cache_append.argtypes = [vp, ctypes.c_int, i32, i32, vp, vp, ctypes.c_int, i32, i32, vp, i32, vp, vp]
     lib.oracle_indexer_scores.restype = ctypes.c_int
     lib.oracle_indexer_scores.argtypes = [vp, ctypes.c_int, vp, vp, vp, ctypes.c_int, i32, i32, vp, i32, vp, i32,
                                           i64, i32, i32, vp, vp, i64, vp]
@@ -184,3 +190,40 @@ def decode_step(inp, k=None, splits=None):
                                cfg.d_latent, cfg.d_rope, cfg.softmax_scale)
     out.update(o=o, lse=lse, status=st)
     return out
+
+
+def fp8_e4m3_encode(q):
+    """float32 array -> uint8 e4m3fn codes (nearest, ties to even, saturating)."""
+    q = np.ascontiguousarray(q, np.float32)
+    out = np.empty(q.shape, np.uint8)
+    _load().oracle_fp8_e4m3_encode_array(_p(q), q.size, _p(out))
+    return out
+
+
+def bf16_encode(x):
+    """float32 array -> uint16 bf16 bit patterns (nearest, ties to even)."""
+    x = np.ascontiguousarray(x, np.float32)
+    out = np.empty(x.shape, np.uint16)
+    _load().oracle_bf16_encode_array(_p(x), x.size, _p(out))
+    return out
+
+
+def cache_append(rows, pool, pool_scale, block_table, positions):
+    """Write row b of `rows` ([B, dim] float32, or uint16 bf16 bits) to slot
+    positions[b] of request b in `pool` ([num_pages, P, dim] float32 / uint16
+    bf16 / uint8 FP8 codes, with `pool_scale` [num_pages, P] float32 when FP8),
+    in place.  Returns the per-request status bits."""
+    rows = np.ascontiguousarray(rows)
+    B, dim = rows.shape
+    assert pool.flags.c_contiguous and pool.shape[2] == dim
+    num_pages, P = pool.shape[0], pool.shape[1]
+    pdt = _fmt(pool)
+    if pdt == 2:
+        assert pool_scale is not None and pool_scale.flags.c_contiguous and pool_scale.dtype == np.float32
+    bt = _c(block_table, np.int32)
+    pos = _c(positions, np.int32)
+    status = np.zeros(B, np.int32)
+    rc = _load().oracle_cache_append(_p(rows), _fmt(rows), B, dim, _p(pool), _p(pool_scale) if pdt == 2 else None,
+                                     pdt, num_pages, P, _p(bt), bt.shape[1], _p(pos), _p(status))
+    assert rc == 0
+    return status

@@ -33,6 +33,10 @@
  *    lse = -inf.
  *  - FP8 rows: OCP e4m3fn code times the row's fp32 scale, one scale per token
  *    over the whole row.
+ *  - Cache append (quantise on write): scale = absmax / 448 in fp32 (1 for a
+ *    zero row), each code the nearest e4m3 value of the fp32 quotient x / scale
+ *    with ties to the even code; the pages name e4m3 [WA section 1] but not
+ *    the scale rule or the rounding.
  *
  * Parity pins for every function live in the tests (brute force on tiny
  * inputs, closed forms, invariants, library routines); see the test files.
@@ -376,6 +380,99 @@ int oracle_lse_merge(const double* o_part, const double* lse_part, int32_t batch
       lse[(int64_t)b * n_heads + h] = L;
     }
   }
+  return 0;
+}
+
+/* ------------------------------------------------------------ cache append */
+
+/* OCP e4m3fn code of a binary32 value: the finite code nearest to |q|, ties
+ * going to the code with an even mantissa, chosen by looking at all 127
+ * non-negative finite codes; magnitudes past 448 take the largest code
+ * (saturation, the generator's convention for the FP8 cache).  The sign bit
+ * is q's own, so -0 and negative values that round to zero give 0x80.  NaN
+ * gives the NaN code. */
+uint8_t oracle_fp8_e4m3_encode(float q) {
+  if (isnan(q)) return signbit(q) ? 0xFF : 0x7F;
+  if (isinf(q)) return signbit(q) ? 0xFE : 0x7E;
+  double a = fabs((double)q);
+  int best = 0;
+  double best_d = INFINITY;
+  for (int c = 0; c <= 0x7E; ++c) {
+    double d = fabs(oracle_fp8_e4m3_value((uint8_t)c) - a);
+    if (d < best_d || (d == best_d && (c & 1) == 0)) {
+      best_d = d;
+      best = c;
+    }
+  }
+  return (uint8_t)(signbit(q) ? (best | 0x80) : best);
+}
+
+void oracle_fp8_e4m3_encode_array(const float* q, int64_t n, uint8_t* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = oracle_fp8_e4m3_encode(q[i]);
+}
+
+/* bf16 bits of a binary32 value, round to nearest with ties to even (the
+ * upper 16 bits, incremented when the dropped half exceeds one half ulp or
+ * equals it with an odd kept part); NaN stays a quiet NaN. */
+uint16_t oracle_bf16_encode(float x) {
+  uint32_t u;
+  memcpy(&u, &x, sizeof u);
+  if (isnan(x)) return (uint16_t)((u >> 16) | 0x0040);
+  uint32_t kept = u >> 16, dropped = u & 0xFFFF;
+  if (dropped > 0x8000 || (dropped == 0x8000 && (kept & 1))) kept += 1;
+  return (uint16_t)kept;
+}
+
+void oracle_bf16_encode_array(const float* x, int64_t n, uint16_t* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = oracle_bf16_encode(x[i]);
+}
+
+/* Append one new token row per request to its page slot.  Each decode step
+ * appends the token just produced to its sequence, whose cache lives in
+ * blocks reached through the block table [EG, "Continuous Batching": the
+ * per-step loop]; an FP8 cache stores e4m3 codes [WA section 1].  Token
+ * positions[b] of request b goes to page block_table[b][t / P], slot t mod P
+ * (t < 0: the request appends nothing).  FP8 pool (reading): one fp32 scale
+ * per token, s = absmax / 448 computed in fp32 (1 for an all-zero row), and
+ * code_i = e4m3(x_i / s) with the quotient rounded to fp32 first; bf16 pool:
+ * x rounded to nearest even; fp32 pool: x.  A position past the mapped pages
+ * flags BAD_LEN and a page id outside [0, num_pages) flags BAD_PAGE; such a
+ * request writes nothing. */
+int oracle_cache_append(const void* rows, int row_dtype, int32_t batch, int32_t dim, void* pool, float* pool_scale,
+                        int pool_dtype, int32_t num_pages, int32_t page_size, const int32_t* bt, int32_t bt_stride,
+                        const int32_t* positions, int32_t* status) {
+  float* x = (float*)malloc(sizeof(float) * (size_t)(dim > 0 ? dim : 1));
+  if (!x) return -1;
+  for (int32_t b = 0; b < batch; ++b) {
+    int32_t t = positions[b];
+    if (t < 0) continue;
+    if ((int64_t)t >= (int64_t)bt_stride * page_size) {
+      status[b] |= OR_BAD_LEN;
+      continue;
+    }
+    int64_t row = row_of(bt, bt_stride, b, t, page_size, num_pages);
+    if (row < 0) {
+      status[b] |= OR_BAD_PAGE;
+      continue;
+    }
+    for (int32_t i = 0; i < dim; ++i) x[i] = (float)elem(rows, row_dtype, (int64_t)b * dim + i);
+    if (pool_dtype == OR_FP8) {
+      float amax = 0.0f;
+      for (int32_t i = 0; i < dim; ++i)
+        if (fabsf(x[i]) > amax) amax = fabsf(x[i]);
+      float sc = amax > 0.0f ? amax / 448.0f : 1.0f;
+      pool_scale[row] = sc;
+      for (int32_t i = 0; i < dim; ++i) {
+        float q = x[i] / sc;
+        ((uint8_t*)pool)[row * dim + i] = oracle_fp8_e4m3_encode(q);
+      }
+    } else if (pool_dtype == OR_BF16) {
+      for (int32_t i = 0; i < dim; ++i) ((uint16_t*)pool)[row * dim + i] = oracle_bf16_encode(x[i]);
+    } else {
+      for (int32_t i = 0; i < dim; ++i) ((float*)pool)[row * dim + i] = x[i];
+    }
+  }
+  free(x);
   return 0;
 }
 

@@ -430,3 +430,136 @@ def test_mla_pool_accounting_matches_generator_layout():
         nbytes = inp.kv.nbytes + (inp.kv_scale.nbytes if inp.kv_scale is not None else 0)
         elem = inp.kv.itemsize
         assert nbytes / slots == oracle.mla_bytes_per_token(c.d_latent, c.d_rope, elem, 4 if elem == 1 else 0)
+
+
+# --------------------------------------------------------------- cache append
+
+def _fp8_values():
+    return np.array([oracle.fp8_e4m3_value(c) for c in range(256)])
+
+
+def test_fp8_encode_round_trips_every_code():
+    vals = _fp8_values()
+    finite = [c for c in range(256) if c not in (0x7F, 0xFF)]
+    codes = oracle.fp8_e4m3_encode(np.array([vals[c] for c in finite], np.float32))
+    np.testing.assert_array_equal(codes, np.array(finite, np.uint8))
+    assert oracle.fp8_e4m3_encode(np.array([np.nan], np.float32))[0] == 0x7F
+
+
+def test_fp8_encode_ties_go_to_even_and_saturate():
+    vals = _fp8_values()
+    lo = np.arange(0x00, 0x7E)
+    mids = ((vals[lo] + vals[lo + 1]) / 2).astype(np.float32)
+    assert np.array_equal(mids.astype(np.float64), (vals[lo] + vals[lo + 1]) / 2)  # exact in fp32
+    want = np.where(lo % 2 == 0, lo, lo + 1).astype(np.uint8)
+    np.testing.assert_array_equal(oracle.fp8_e4m3_encode(mids), want)
+    np.testing.assert_array_equal(oracle.fp8_e4m3_encode(-mids), want | 0x80)
+    up = np.nextafter(mids, np.float32(np.inf))
+    dn = np.nextafter(mids, np.float32(0))
+    np.testing.assert_array_equal(oracle.fp8_e4m3_encode(up), (lo + 1).astype(np.uint8))
+    np.testing.assert_array_equal(oracle.fp8_e4m3_encode(dn), lo.astype(np.uint8))
+    big = np.array([448.0, 448.01, 463.9, 464.0, 1e6, np.inf, -500.0], np.float32)
+    np.testing.assert_array_equal(oracle.fp8_e4m3_encode(big), [0x7E] * 6 + [0xFE])
+    tiny = np.array([2.0 ** -10, 2.0 ** -10 * 1.0001, -2.0 ** -11, -0.0], np.float32)
+    np.testing.assert_array_equal(oracle.fp8_e4m3_encode(tiny), [0x00, 0x01, 0x80, 0x80])
+
+
+def test_fp8_encode_matches_torch_cast():
+    rng = np.random.default_rng(5)
+    mag = np.exp2(rng.uniform(-12, np.log2(448.0), 200_000))
+    q = (mag * rng.choice([-1.0, 1.0], mag.size)).astype(np.float32)
+    ref = torch.from_numpy(q).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(oracle.fp8_e4m3_encode(q), ref)
+
+
+def test_bf16_encode_matches_torch_cast():
+    rng = np.random.default_rng(6)
+    x = rng.standard_normal(100_000).astype(np.float32) * np.exp2(rng.integers(-20, 20, 100_000))
+    x = x.astype(np.float32)
+    ties = (x.view(np.uint32) & np.uint32(0xFFFF0000)) | np.uint32(0x8000)  # exact halfway cases
+    x = np.concatenate([x, ties.view(np.float32)])
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(oracle.bf16_encode(x), ref)
+
+
+def _append_case(pool_dtype, dim=40, P=4, num_pages=6):
+    rng = np.random.default_rng(7)
+    bt = np.array([[3, 1], [0, 5], [2, 4]], np.int32)
+    if pool_dtype == "fp8":
+        pool = np.full((num_pages, P, dim), 0x55, np.uint8)
+        sc = np.full((num_pages, P), 9.0, np.float32)
+    elif pool_dtype == "bf16":
+        pool, sc = np.full((num_pages, P, dim), 0x1234, np.uint16), None
+    else:
+        pool, sc = np.full((num_pages, P, dim), 9.0, np.float32), None
+    return rng, bt, pool, sc
+
+
+def test_cache_append_fp8_closed_forms():
+    rng, bt, pool, sc = _append_case("fp8")
+    dim, P = pool.shape[2], pool.shape[1]
+    rows = np.zeros((3, dim), np.float32)
+    rows[0, 7] = -3.25                            # one non-zero element
+    x2 = rng.standard_normal(dim).astype(np.float32) * 5
+    rows[2] = x2
+    pos = np.array([5, 2, 6], np.int32)          # pages bt[0][1]=1 slot 1, bt[1][0]=0 slot 2, bt[2][1]=4 slot 2
+    before = pool.copy(), sc.copy()
+    st = oracle.cache_append(rows, pool, sc, bt, pos)
+    assert not st.any()
+    # request 0: scale = 3.25/448 in fp32, the element itself -> -448
+    assert sc[1, 1] == np.float32(np.float32(3.25) / np.float32(448.0))
+    want0 = np.zeros(dim, np.uint8)
+    want0[7] = 0xFE
+    np.testing.assert_array_equal(pool[1, 1], want0)
+    # request 1: an all-zero row has scale 1 and zero codes
+    assert sc[0, 2] == 1.0 and not pool[0, 2].any()
+    # request 2: the amax element hits 448 exactly; all others are within half
+    # an e4m3 step of x / scale (relative 2^-4 for normals, 2^-10 absolute below)
+    s2 = sc[4, 2]
+    assert s2 == np.float32(np.float32(np.abs(x2).max()) / np.float32(448.0))
+    vals = _fp8_values()
+    deq = vals[pool[4, 2]]
+    q = x2.astype(np.float64) / np.float64(s2)
+    j = int(np.argmax(np.abs(x2)))
+    assert abs(deq[j]) == 448.0
+    err = np.abs(deq - q)
+    assert np.all(err <= np.maximum(np.abs(q) * 2.0 ** -4, 2.0 ** -10) * (1 + 1e-6))
+    # every other slot is untouched
+    changed = np.zeros(pool.shape[:2], bool)
+    changed[1, 1] = changed[0, 2] = changed[4, 2] = True
+    assert np.array_equal(pool[~changed], before[0][~changed]) and np.array_equal(sc[~changed], before[1][~changed])
+
+
+@pytest.mark.parametrize("pool_dtype", ["bf16", "fp32"])
+def test_cache_append_wide_pools(pool_dtype):
+    rng, bt, pool, _ = _append_case(pool_dtype)
+    dim = pool.shape[2]
+    rows = rng.standard_normal((3, dim)).astype(np.float32)
+    pos = np.array([0, 7, 3], np.int32)          # page 3 slot 0, page 5 slot 3, page 2 slot 3
+    st = oracle.cache_append(rows, pool, None, bt, pos)
+    assert not st.any()
+    for b, (pg, sl) in enumerate([(3, 0), (5, 3), (2, 3)]):
+        if pool_dtype == "bf16":
+            ref = torch.from_numpy(rows[b]).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        else:
+            ref = rows[b]
+        np.testing.assert_array_equal(pool[pg, sl], ref)
+    # bf16 input rows into an FP8 pool decode exactly before quantising
+    _, bt, p8, sc = _append_case("fp8")
+    bits = gen.to_bf16_bits(rows)
+    oracle.cache_append(bits, p8, sc, bt, pos)
+    p8b, scb = _append_case("fp8")[2:]
+    oracle.cache_append(gen.bf16_bits_to_f32(bits), p8b, scb, bt, pos)
+    assert np.array_equal(p8, p8b) and np.array_equal(sc, scb)
+
+
+def test_cache_append_status_and_skips():
+    _, bt, pool, sc = _append_case("fp8")
+    bt = bt.copy()
+    bt[1, 1] = 99                                 # request 1's second page is not a pool page
+    rows = np.ones((3, pool.shape[2]), np.float32)
+    pos = np.array([-1, 6, 8], np.int32)          # skip; page 99; past the 2 mapped pages
+    before = pool.copy(), sc.copy()
+    st = oracle.cache_append(rows, pool, sc, bt, pos)
+    assert list(st) == [0, oracle.BAD_PAGE, oracle.BAD_LEN]
+    assert np.array_equal(pool, before[0]) and np.array_equal(sc, before[1])
