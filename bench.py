@@ -99,6 +99,49 @@ def measured_traffic(kernel_file, workload):
     return rec.get("hbm_bytes_per_launch")
 
 
+def time_cache_append(cfg, db, inp, steps, flush, run_flush):
+    """The step before the path: each request's new token row appended to the
+    latent pool and its indexer key to the key pool, both quantised to FP8 on
+    write (two kv_cache_append calls, timed together with HIP events on the
+    launch stream, cold like the step).  Writes the requests' last slots."""
+    import numpy as np
+    import torch
+    import spmla_gen as gen
+    import sparse_paged_mla_amd as spm
+    B = cfg.batch
+    lat = np.stack([gen.normals32(cfg.seed, gen.T_NEW_KV, b, cfg.dim) for b in range(B)])
+    key = np.stack([gen.normals32(cfg.seed, gen.T_NEW_KIDX, b, cfg.idx_dim) for b in range(B)])
+    lat_t = torch.from_numpy(gen.to_bf16_bits(lat).view(np.int16)).view(torch.bfloat16).cuda()
+    key_t = torch.from_numpy(gen.to_bf16_bits(key).view(np.int16)).view(torch.bfloat16).cuda()
+    pos = (db.lens - 1).to(torch.int32)
+    status = torch.zeros(B, dtype=torch.int32, device="cuda")
+
+    def both():
+        spm.kv_cache_append(lat_t, db.kv, db.kv_scale, db.block_table, pos, status)
+        spm.kv_cache_append(key_t, db.k_idx, db.k_idx_scale, db.block_table, pos, status)
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for _ in range(3):
+        both()
+    ts = []
+    for e0, e1 in evs:
+        if flush:
+            run_flush()
+        e0.record()
+        both()
+        e1.record()
+    torch.cuda.synchronize()
+    assert not status.cpu().numpy().any(), "append flagged a request on clean inputs"
+    us = statistics.fmean(e0.elapsed_time(e1) for e0, e1 in evs) * 1e3
+    # Algorithmic bytes: the bf16 rows read, codes and scales written, and one
+    # position and block-table entry read per request, for both pools.
+    nbytes = B * (cfg.dim * 3 + 4 + cfg.idx_dim * 3 + 4 + 2 * 8)
+    return {"us_per_step": round(us, 2), "calls": 2, "algorithmic_bytes": nbytes,
+            "achieved_GBps": round(nbytes / (us * 1e-6) / 1e9, 2),
+            "frac_hbm": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 6),
+            "note": "two launches of a few hundred bytes per request: launch-bound"}
+
+
 def cpu_baseline(inp, n_req):
     """The fp64 oracle, as it stands, on the first n_req requests of the same inputs (one thread)."""
     import numpy as np
@@ -198,6 +241,10 @@ def main():
         torch.cuda.synchronize()
         warm_ms = e0.elapsed_time(e1) / args.steps
 
+    app = None if cfg.dense or cfg.cache_dtype != gen.FP8 else time_cache_append(cfg, db, inp, args.steps, flush,
+                                                                                 run_flush=lambda: flush_sink.copy_(
+                                                                                     flush_buf.amax()))
+
     alg = algorithmic(cfg, inp.lens)
     t_star = roofline_time_s(alg)
     kname = {"indexer": "indexer", "select": "topk", "attend": "decode", "merge": "merge"}
@@ -254,6 +301,7 @@ def main():
         "step_roofline": {"t_star_us": round(t_star * 1e6, 2), "t_step_us": round(mean_ms * 1e3, 2),
                           "frac": round(t_star / (mean_ms * 1e-3), 4)},
         "kernel_us": {k: round(v * 1e3, 2) for k, v in kernel_ms.items()},
+        "cache_append": app,
         "step_ms_median_min_max": [round(statistics.median(step_ms), 4), round(min(step_ms), 4),
                                    round(max(step_ms), 4)],
         "warm_ms_per_step": None if warm_ms != warm_ms else round(warm_ms, 4),

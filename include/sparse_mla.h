@@ -192,6 +192,40 @@ int lse_merge(const float* o_part, const float* lse_part,
               int32_t batch, int32_t num_splits, int32_t n_heads, int32_t d,
               float* o, float* lse, void* stream);
 
+/*
+ * kv_cache_append -- write each request's new token row into its page slot,
+ * quantising on write for an FP8 pool: the counterpart of dequant-on-read.
+ * Every decode step appends the token it produced to its sequence, whose
+ * cache sits in pages reached through the block table [EG, "Continuous
+ * Batching": the per-step loop]; an FP8 cache holds e4m3 codes [WA section 1].
+ * Called once for the latent pool (row_dim = d_latent + d_rope) and once for
+ * the indexer-key pool (row_dim = d) with the same block table.
+ *
+ *  rows       [batch, row_dim] row_dtype F32 or BF16: the new rows.
+ *  pool       [num_pages, page_size, row_dim] pool_dtype F32, BF16 or FP8_E4M3,
+ *             written in place; pool_scale [num_pages, page_size] fp32 (FP8
+ *             only, else may be NULL).
+ *  positions  [batch] int32: the slot of request b is token positions[b]
+ *             (page block_table[b][t / page_size], slot t mod page_size);
+ *             t < 0 appends nothing for that request.  With context lengths
+ *             that already count the new token, t = context_lens[b] - 1.
+ *             Distinct requests must name distinct slots.
+ *
+ * FP8 pool: scale s = absmax(row) / 448 computed in fp32 (1 for an all-zero
+ * row), stored in pool_scale; element i becomes the e4m3 code nearest to the
+ * fp32 quotient x_i / s, ties to the even code.  BF16 pool: x rounded to
+ * nearest even.  F32 pool: x.  Rows must be finite.  A position at or past
+ * bt_stride * page_size sets SPMLA_REQ_BAD_LEN, a page id outside
+ * [0, num_pages) sets SPMLA_REQ_BAD_PAGE; such a request writes nothing.
+ * Supported: row_dim a multiple of 8 in [8, 4096]; page_size 16/32/64/128;
+ * rows and pool 16-byte aligned.  Nothing is read from the pool.
+ */
+int kv_cache_append(const void* rows, int32_t row_dtype, int32_t batch, int32_t row_dim,
+                    void* pool, float* pool_scale, int32_t pool_dtype,
+                    int32_t num_pages, int32_t page_size,
+                    const int32_t* block_table, int32_t bt_stride,
+                    const int32_t* positions, int32_t* req_status, void* stream);
+
 /* Message of the last failing call on this thread (host memory, valid until
  * the next call on this thread). */
 const char* spmla_last_error(void);

@@ -50,6 +50,8 @@ def load_library():
     lib.mla_paged_decode.restype = ctypes.c_int
     lib.mla_paged_decode.argtypes = [vp, i32, vp, vp, i32, i32, i32, vp, i32, vp, i32, i64, vp, i32, i32, i32, i32,
                                      f32, i32, vp, vp, vp, vp]
+    lib.kv_cache_append.restype = ctypes.c_int
+    lib.kv_cache_append.argtypes = [vp, i32, i32, i32, vp, vp, i32, i32, i32, vp, i32, vp, vp, vp]
     lib.lse_merge.restype = ctypes.c_int
     lib.lse_merge.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp]
     lib.spmla_last_error.restype = ctypes.c_char_p
@@ -134,3 +136,17 @@ def lse_merge(o_part, lse_part, o, lse, stream=None):
     lib = load_library()
     B, S, H, d = o_part.shape
     _check(lib.lse_merge(_ptr(o_part), _ptr(lse_part), B, S, H, d, _ptr(o), _ptr(lse), _stream(stream)))
+
+
+def kv_cache_append(rows, pool, pool_scale, block_table, positions, req_status=None, stream=None):
+    """Write rows[b] ([B, dim] fp32/bf16) to slot positions[b] of request b in
+    pool ([num_pages, P, dim] fp32/bf16/FP8; FP8 quantises with a per-token
+    scale written to pool_scale [num_pages, P])."""
+    lib = load_library()
+    B, dim = rows.shape
+    num_pages, page_size = pool.shape[0], pool.shape[1]
+    if pool.shape[2] != dim:
+        raise ValueError("pool row length differs from the rows'")
+    _check(lib.kv_cache_append(_ptr(rows), _dtype_code(rows), B, dim, _ptr(pool), _ptr(pool_scale),
+                               _dtype_code(pool), num_pages, page_size, _ptr(block_table), block_table.shape[1],
+                               _ptr(positions), _ptr(req_status), _stream(stream)))

@@ -144,4 +144,27 @@ int lse_merge(const float* o_part, const float* lse_part, int32_t batch, int32_t
   return map_launch(spmla::launch_merge(a, reinterpret_cast<hipStream_t>(stream)), w);
 }
 
+int kv_cache_append(const void* rows, int32_t row_dtype, int32_t batch, int32_t row_dim, void* pool,
+                    float* pool_scale, int32_t pool_dtype, int32_t num_pages, int32_t page_size,
+                    const int32_t* block_table, int32_t bt_stride, const int32_t* positions, int32_t* req_status,
+                    void* stream) {
+  const char* w = "kv_cache_append";
+  if (batch < 0) return fail(SPMLA_EINVAL, "%s: batch < 0", w);
+  if (row_dtype != SPMLA_F32 && row_dtype != SPMLA_BF16)
+    return fail(SPMLA_EUNSUPPORTED, "%s: row_dtype must be F32 or BF16", w);
+  if (pool_dtype < SPMLA_F32 || pool_dtype > SPMLA_FP8_E4M3) return fail(SPMLA_EINVAL, "%s: bad pool_dtype", w);
+  if (row_dim < 8 || row_dim > 4096 || row_dim % 8 != 0)
+    return fail(SPMLA_EUNSUPPORTED, "%s: row_dim must be a multiple of 8 in [8, 4096]", w);
+  if (num_pages < 1) return fail(SPMLA_EINVAL, "%s: num_pages must be >= 1", w);
+  if (!is_pow2_page(page_size)) return fail(SPMLA_EUNSUPPORTED, "%s: page_size must be 16, 32, 64 or 128", w);
+  if (bt_stride < 1) return fail(SPMLA_EINVAL, "%s: bt_stride must be >= 1", w);
+  if (batch == 0) return ok();
+  if (!rows || !pool || !block_table || !positions) return fail(SPMLA_EINVAL, "%s: null pointer", w);
+  if (pool_dtype == SPMLA_FP8_E4M3 && !pool_scale) return fail(SPMLA_EINVAL, "%s: an FP8 pool needs pool_scale", w);
+  if (!aligned16(rows) || !aligned16(pool)) return fail(SPMLA_EINVAL, "%s: rows and pool must be 16-byte aligned", w);
+  spmla::AppendArgs a{rows, row_dtype, batch, row_dim, pool, pool_scale, pool_dtype, num_pages, page_size,
+                      block_table, bt_stride, positions, req_status};
+  return map_launch(spmla::launch_cache_append(a, reinterpret_cast<hipStream_t>(stream)), w);
+}
+
 }  // extern "C"

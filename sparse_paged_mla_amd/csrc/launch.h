@@ -39,4 +39,10 @@ struct MergeArgs {
 };
 int launch_merge(const MergeArgs& a, hipStream_t stream);
 
+struct AppendArgs {
+  const void* rows; int row_dtype; int32_t batch, dim; void* pool; float* pool_scale; int pool_dtype;
+  int32_t num_pages, page_size; const int32_t* bt; int32_t bt_stride; const int32_t* positions; int32_t* status;
+};
+int launch_cache_append(const AppendArgs& a, hipStream_t stream);
+
 }  // namespace spmla

@@ -24,7 +24,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libspmla_gen.so")
 _lib = None
 
-T_LENS, T_PERM, T_Q, T_KV, T_QIDX, T_W, T_KIDX, T_FILL = range(8)
+T_LENS, T_PERM, T_Q, T_KV, T_QIDX, T_W, T_KIDX, T_FILL, T_NEW_KV, T_NEW_KIDX = range(10)
 
 
 def _load():

@@ -32,7 +32,7 @@ def lib():
 def test_header_declares_the_four_operations():
     names = _declared()
     for n in ("dsa_indexer_scores", "topk_select", "mla_paged_decode", "lse_merge", "topk_workspace_bytes",
-              "spmla_last_error"):
+              "kv_cache_append", "spmla_last_error"):
         assert n in names, names
 
 
@@ -140,3 +140,26 @@ def test_merge_rejects(lib):
     assert f(FAKE, FAKE, 2, 4, 4, 512, MIS, FAKE, None) == EINVAL
     assert f(FAKE, FAKE, -2, 4, 4, 512, FAKE, FAKE, None) == EINVAL
     assert f(None, None, 0, 4, 4, 512, None, None, None) == OK
+
+
+def _app(lib, rows=FAKE, row_dtype=1, batch=4, dim=576, pool=FAKE, scale=FAKE, pool_dtype=2, num_pages=10, P=64,
+         bt=FAKE, bt_stride=4, pos=FAKE):
+    return lib.kv_cache_append(rows, row_dtype, batch, dim, pool, scale, pool_dtype, num_pages, P, bt, bt_stride, pos,
+                               None, None)
+
+
+def test_append_rejects(lib):
+    assert _app(lib, row_dtype=2) == EUNSUPPORTED      # FP8 rows in
+    assert _app(lib, pool_dtype=3) == EINVAL
+    assert _app(lib, dim=20) == EUNSUPPORTED
+    assert _app(lib, dim=4104) == EUNSUPPORTED
+    assert _app(lib, P=48) == EUNSUPPORTED
+    assert _app(lib, num_pages=0) == EINVAL
+    assert _app(lib, bt_stride=0) == EINVAL
+    assert _app(lib, batch=-1) == EINVAL
+    assert _app(lib, scale=None) == EINVAL             # an FP8 pool needs its scales
+    assert _app(lib, rows=None) == EINVAL
+    assert _app(lib, pos=None) == EINVAL
+    assert _app(lib, pool=MIS) == EINVAL
+    assert "16-byte" in lib.spmla_last_error().decode()
+    assert _app(lib, batch=0, rows=None, pool=None, bt=None, pos=None) == OK
