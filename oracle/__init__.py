@@ -16,7 +16,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "liboracle_spmla.so")
 _lib = None
 
-BAD_PAGE, BAD_LEN, BAD_INDEX = 1, 2, 4
+BAD_PAGE, BAD_LEN, BAD_INDEX, BAD_TAG = 1, 2, 4, 8
 
 
 def _load():
@@ -36,6 +36,8 @@ def _load():
     lib.oracle_fp8_e4m3_encode_array.argtypes = [vp, i64, vp]
     lib.oracle_bf16_encode_array.restype = None
     lib.oracle_bf16_encode_array.argtypes = [vp, i64, vp]
+    lib.oracle_page_check.restype = ctypes.c_int
+    lib.oracle_page_check.argtypes = [vp, vp, i32, vp, i32, i64, vp, i32, i32, vp]
     lib.oracle_cache_append.restype = ctypes.c_int
     lib.oracle_cache_append.argtypes = [vp, ctypes.c_int, i32, i32, vp, vp, ctypes.c_int, i32, i32, vp, i32, vp, vp]
     lib.oracle_indexer_scores.restype = ctypes.c_int
@@ -226,4 +228,19 @@ def cache_append(rows, pool, pool_scale, block_table, positions):
     rc = _load().oracle_cache_append(_p(rows), _fmt(rows), B, dim, _p(pool), _p(pool_scale) if pdt == 2 else None,
                                      pdt, num_pages, P, _p(bt), bt.shape[1], _p(pos), _p(status))
     assert rc == 0
+    return status
+
+
+def page_check(block_table, bt_tags, lens, page_tags, page_size, max_len=None):
+    """Per-request status bits of the page-integrity check (BAD_LEN, BAD_PAGE, BAD_TAG)."""
+    bt = _c(block_table, np.int32)
+    tags = _c(bt_tags, np.uint64)
+    assert tags.shape == bt.shape
+    lens = _c(lens, np.int32)
+    pt = _c(page_tags, np.uint64)
+    B = lens.shape[0]
+    max_len = int(lens.max()) if max_len is None and B else int(max_len or 0)
+    status = np.zeros(B, np.int32)
+    assert _load().oracle_page_check(_p(bt), _p(tags), bt.shape[1], _p(lens), B, max_len, _p(pt), pt.shape[0],
+                                     int(page_size), _p(status)) == 0
     return status

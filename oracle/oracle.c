@@ -47,7 +47,7 @@
 #include <string.h>
 
 enum { OR_F32 = 0, OR_BF16 = 1, OR_FP8 = 2 };
-enum { OR_BAD_PAGE = 1, OR_BAD_LEN = 2, OR_BAD_INDEX = 4 };
+enum { OR_BAD_PAGE = 1, OR_BAD_LEN = 2, OR_BAD_INDEX = 4, OR_BAD_TAG = 8 };
 
 /* ---------------------------------------------------------------- decoders */
 
@@ -473,6 +473,39 @@ int oracle_cache_append(const void* rows, int row_dtype, int32_t batch, int32_t 
     }
   }
   free(x);
+  return 0;
+}
+
+/* ------------------------------------------------------- page integrity */
+
+/* Integrity check of every request's page mapping before the cache is read.
+ * Each physical page carries a tag that is new on every reallocation, and
+ * before decode reads the cache the server checks which request uses which
+ * page; on a mismatch the request is aborted rather than served wrong data
+ * [WA section 3: tag management, mapping verification].  Reading: the tag
+ * each request expects for its logical page j is recorded beside its block
+ * table entry (bt_tags[b][j], written when the page was given to it), and
+ * the check compares it with the page's current tag page_tags[bt[b][j]] for
+ * every page the request's length covers.  A length outside
+ * [0, min(max_len, bt_stride * page_size)] flags BAD_LEN (nothing else is
+ * checked); a page id outside [0, num_pages) flags BAD_PAGE; a tag that
+ * differs flags BAD_TAG.  Entries past a request's pages are not looked at. */
+int oracle_page_check(const int32_t* bt, const uint64_t* bt_tags, int32_t bt_stride, const int32_t* lens,
+                      int32_t batch, int64_t max_len, const uint64_t* page_tags, int32_t num_pages,
+                      int32_t page_size, int32_t* status) {
+  for (int32_t b = 0; b < batch; ++b) {
+    int32_t len = lens[b];
+    if (!len_ok(len, bt_stride, page_size, max_len)) {
+      status[b] |= OR_BAD_LEN;
+      continue;
+    }
+    int64_t pages = ((int64_t)len + page_size - 1) / page_size;
+    for (int64_t j = 0; j < pages; ++j) {
+      int32_t p = bt[(int64_t)b * bt_stride + j];
+      if (p < 0 || p >= num_pages) status[b] |= OR_BAD_PAGE;
+      else if (page_tags[p] != bt_tags[(int64_t)b * bt_stride + j]) status[b] |= OR_BAD_TAG;
+    }
+  }
   return 0;
 }
 

@@ -563,3 +563,59 @@ def test_cache_append_status_and_skips():
     st = oracle.cache_append(rows, pool, sc, bt, pos)
     assert list(st) == [0, oracle.BAD_PAGE, oracle.BAD_LEN]
     assert np.array_equal(pool, before[0]) and np.array_equal(sc, before[1])
+
+
+# ------------------------------------------------------- page integrity check
+
+def _tag_case(seed=3, B=6, P=16, stride=5):
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(1, stride * P + 1, B).astype(np.int32)
+    num_pages = B * stride + 4
+    bt = rng.permutation(num_pages)[: B * stride].reshape(B, stride).astype(np.int32)
+    page_tags = rng.integers(0, 2 ** 63, num_pages, dtype=np.uint64)
+    bt_tags = page_tags[bt]
+    return rng, lens, bt, bt_tags, page_tags, P
+
+
+def test_page_check_closed_forms():
+    rng, lens, bt, bt_tags, page_tags, P = _tag_case()
+    assert not oracle.page_check(bt, bt_tags, lens, page_tags, P).any()
+    # A reallocated page (new tag) flags exactly the requests whose length covers it.
+    b, j = 2, (int(lens[2]) - 1) // P
+    page_tags2 = page_tags.copy()
+    page_tags2[bt[b, j]] ^= np.uint64(1)
+    st = oracle.page_check(bt, bt_tags, lens, page_tags2, P)
+    assert list(np.nonzero(st)[0]) == [b] and st[b] == oracle.BAD_TAG
+    # Entries past a request's pages are never looked at.
+    lens3 = lens.copy()
+    lens3[0] = P                                  # one page
+    bt3, tags3 = bt.copy(), bt_tags.copy()
+    bt3[0, 1:] = -7
+    tags3[0, 1:] = 12345
+    assert not oracle.page_check(bt3, tags3, lens3, page_tags, P).any()
+    # Bad page id, bad length, empty request.
+    bt4 = bt.copy()
+    bt4[1, 0] = 10 ** 6
+    lens4 = lens.copy()
+    lens4[3] = bt.shape[1] * P + 1
+    lens4[4] = 0
+    st = oracle.page_check(bt4, bt_tags, lens4, page_tags, P, max_len=bt.shape[1] * P + 1)
+    assert st[1] == oracle.BAD_PAGE and st[3] == oracle.BAD_LEN and st[4] == 0
+    assert st[0] == st[2] == st[5] == 0
+
+
+def test_page_check_matches_numpy_brute_force():
+    for seed in range(20):
+        rng, lens, bt, bt_tags, page_tags, P = _tag_case(seed, B=12, stride=7)
+        page_tags = page_tags.copy()
+        flip = rng.choice(page_tags.size, 5, replace=False)
+        page_tags[flip] += np.uint64(1)
+        bt = bt.copy()
+        bt[rng.integers(0, bt.shape[0]), rng.integers(0, bt.shape[1])] = -1
+        pages = (lens + P - 1) // P
+        used = np.arange(bt.shape[1])[None, :] < pages[:, None]
+        bad_page = used & ((bt < 0) | (bt >= page_tags.size))
+        safe = np.clip(bt, 0, page_tags.size - 1)
+        bad_tag = used & ~bad_page & (page_tags[safe] != bt_tags)
+        want = np.where(bad_page.any(1), oracle.BAD_PAGE, 0) | np.where(bad_tag.any(1), oracle.BAD_TAG, 0)
+        np.testing.assert_array_equal(oracle.page_check(bt, bt_tags, lens, page_tags, P), want)
