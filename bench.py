@@ -142,6 +142,43 @@ def time_cache_append(cfg, db, inp, steps, flush, run_flush):
             "note": "two launches of a few hundred bytes per request: launch-bound"}
 
 
+def time_page_check(cfg, db, inp, steps, flush, run_flush):
+    """The KV-page integrity check a server may run before the step reads the
+    cache (one kv_page_check call over every covered block-table entry),
+    timed cold like the step.  Tags: page p carries p * 0x9E3779B97F4A7C15
+    mod 2^64 (distinct for every page) and every entry records its page's tag."""
+    import numpy as np
+    import torch
+    import sparse_paged_mla_amd as spm
+    P = cfg.page_size
+    page_tags = np.arange(inp.num_pages, dtype=np.uint64) * np.uint64(0x9E3779B97F4A7C15)
+    bt = inp.block_table
+    bt_tags = np.where(bt >= 0, page_tags[np.clip(bt, 0, None)], np.uint64(0)).astype(np.uint64)
+    pt_t = torch.from_numpy(page_tags.view(np.int64)).cuda()
+    bt_tags_t = torch.from_numpy(bt_tags.view(np.int64)).cuda()
+    status = torch.zeros(cfg.batch, dtype=torch.int32, device="cuda")
+
+    def check():
+        spm.kv_page_check(db.block_table, bt_tags_t, db.lens, db.max_len, pt_t, P, status)
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for _ in range(3):
+        check()
+    for e0, e1 in evs:
+        if flush:
+            run_flush()
+        e0.record()
+        check()
+        e1.record()
+    torch.cuda.synchronize()
+    assert not status.cpu().numpy().any(), "page check flagged a request on clean inputs"
+    us = statistics.fmean(e0.elapsed_time(e1) for e0, e1 in evs) * 1e3
+    entries = int(((inp.lens + P - 1) // P).sum())
+    nbytes = entries * (4 + 8 + 8) + 4 * cfg.batch
+    return {"us": round(us, 2), "entries": entries, "algorithmic_bytes": nbytes,
+            "achieved_GBps": round(nbytes / (us * 1e-6) / 1e9, 1)}
+
+
 def cpu_baseline(inp, n_req):
     """The fp64 oracle, as it stands, on the first n_req requests of the same inputs (one thread)."""
     import numpy as np
@@ -245,6 +282,9 @@ def main():
                                                                                  run_flush=lambda: flush_sink.copy_(
                                                                                      flush_buf.amax()))
 
+    chk = time_page_check(cfg, db, inp, args.steps, flush, run_flush=lambda: flush_sink.copy_(flush_buf.amax()))
+    chk["overhead_frac_of_step"] = round(chk["us"] / (mean_ms * 1e3), 4)
+
     alg = algorithmic(cfg, inp.lens)
     t_star = roofline_time_s(alg)
     kname = {"indexer": "indexer", "select": "topk", "attend": "decode", "merge": "merge"}
@@ -302,6 +342,7 @@ def main():
                           "frac": round(t_star / (mean_ms * 1e-3), 4)},
         "kernel_us": {k: round(v * 1e3, 2) for k, v in kernel_ms.items()},
         "cache_append": app,
+        "page_check": chk,
         "step_ms_median_min_max": [round(statistics.median(step_ms), 4), round(min(step_ms), 4),
                                    round(max(step_ms), 4)],
         "warm_ms_per_step": None if warm_ms != warm_ms else round(warm_ms, 4),

@@ -74,7 +74,7 @@ typedef enum {
 } spmla_dtype;
 
 /* Per-request status bits written to req_status[b]. */
-enum { SPMLA_REQ_BAD_PAGE = 1, SPMLA_REQ_BAD_LEN = 2, SPMLA_REQ_BAD_INDEX = 4 };
+enum { SPMLA_REQ_BAD_PAGE = 1, SPMLA_REQ_BAD_LEN = 2, SPMLA_REQ_BAD_INDEX = 4, SPMLA_REQ_BAD_TAG = 8 };
 
 /*
  * dsa_indexer_scores -- indexer score of every history token of every request
@@ -225,6 +225,33 @@ int kv_cache_append(const void* rows, int32_t row_dtype, int32_t batch, int32_t 
                     int32_t num_pages, int32_t page_size,
                     const int32_t* block_table, int32_t bt_stride,
                     const int32_t* positions, int32_t* req_status, void* stream);
+
+/*
+ * kv_page_check -- the KV-page integrity check, a separate batched pass run
+ * before a step reads the cache.  Every physical page carries a tag that is
+ * new on each reallocation; before decode reads the cache the mapping of
+ * requests to pages is verified, and a request whose tags or mapping do not
+ * match is aborted rather than served wrong data [WA section 3].  The check
+ * is kept out of the attention kernels, as the pages keep it.
+ *
+ *  block_table [batch, bt_stride] int32 and bt_tags [batch, bt_stride]
+ *              uint64: entry j of request b and the tag its page had when it
+ *              was given to the request.
+ *  page_tags   [num_pages] uint64: each page's current tag.
+ *  req_status  [batch] int32 (required): for every entry j <
+ *              ceil(context_lens[b] / page_size), a page id outside
+ *              [0, num_pages) ORs SPMLA_REQ_BAD_PAGE and a tag that differs
+ *              from page_tags[page] ORs SPMLA_REQ_BAD_TAG; a length outside
+ *              [0, min(max_len, bt_stride * page_size)] ORs SPMLA_REQ_BAD_LEN.
+ *              Entries past a request's pages are not read.
+ *
+ * The outputs that the other calls produce for a flagged request must not be
+ * used.  Supported: page_size 16/32/64/128; tag arrays 8-byte aligned.
+ */
+int kv_page_check(const int32_t* block_table, const uint64_t* bt_tags, int32_t bt_stride,
+                  const int32_t* context_lens, int32_t batch, int64_t max_len,
+                  const uint64_t* page_tags, int32_t num_pages, int32_t page_size,
+                  int32_t* req_status, void* stream);
 
 /* Message of the last failing call on this thread (host memory, valid until
  * the next call on this thread). */

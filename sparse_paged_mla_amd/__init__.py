@@ -18,7 +18,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libsparse_mla.so")
 
 F32, BF16, FP8_E4M3 = 0, 1, 2
-BAD_PAGE, BAD_LEN, BAD_INDEX = 1, 2, 4
+BAD_PAGE, BAD_LEN, BAD_INDEX, BAD_TAG = 1, 2, 4, 8
 STATUS_NAMES = {0: "SPMLA_OK", -1: "SPMLA_EINVAL", -2: "SPMLA_EUNSUPPORTED", -3: "SPMLA_ELAUNCH",
                 -4: "SPMLA_EWORKSPACE"}
 
@@ -52,6 +52,8 @@ def load_library():
                                      f32, i32, vp, vp, vp, vp]
     lib.kv_cache_append.restype = ctypes.c_int
     lib.kv_cache_append.argtypes = [vp, i32, i32, i32, vp, vp, i32, i32, i32, vp, i32, vp, vp, vp]
+    lib.kv_page_check.restype = ctypes.c_int
+    lib.kv_page_check.argtypes = [vp, vp, i32, vp, i32, i64, vp, i32, i32, vp, vp]
     lib.lse_merge.restype = ctypes.c_int
     lib.lse_merge.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp]
     lib.spmla_last_error.restype = ctypes.c_char_p
@@ -150,3 +152,17 @@ def kv_cache_append(rows, pool, pool_scale, block_table, positions, req_status=N
     _check(lib.kv_cache_append(_ptr(rows), _dtype_code(rows), B, dim, _ptr(pool), _ptr(pool_scale),
                                _dtype_code(pool), num_pages, page_size, _ptr(block_table), block_table.shape[1],
                                _ptr(positions), _ptr(req_status), _stream(stream)))
+
+
+def kv_page_check(block_table, bt_tags, context_lens, max_len, page_tags, page_size, req_status, stream=None):
+    """OR BAD_PAGE / BAD_TAG / BAD_LEN into req_status for every request whose
+    covered block-table entries have a bad page id or a tag (int64 [B,
+    bt_stride], the page's tag when it was given out) other than the page's
+    current tag (page_tags int64 [num_pages])."""
+    lib = load_library()
+    B = context_lens.shape[0]
+    if bt_tags.shape != block_table.shape:
+        raise ValueError("bt_tags must have the block table's shape")
+    _check(lib.kv_page_check(_ptr(block_table), _ptr(bt_tags), block_table.shape[1], _ptr(context_lens), B,
+                             int(max_len), _ptr(page_tags), page_tags.shape[0], int(page_size), _ptr(req_status),
+                             _stream(stream)))

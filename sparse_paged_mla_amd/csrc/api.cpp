@@ -167,4 +167,18 @@ int kv_cache_append(const void* rows, int32_t row_dtype, int32_t batch, int32_t 
   return map_launch(spmla::launch_cache_append(a, reinterpret_cast<hipStream_t>(stream)), w);
 }
 
+int kv_page_check(const int32_t* block_table, const uint64_t* bt_tags, int32_t bt_stride, const int32_t* context_lens,
+                  int32_t batch, int64_t max_len, const uint64_t* page_tags, int32_t num_pages, int32_t page_size,
+                  int32_t* req_status, void* stream) {
+  const char* w = "kv_page_check";
+  if (int rc = check_paging(w, num_pages, page_size, block_table, bt_stride, context_lens, batch, max_len)) return rc;
+  if (batch == 0) return ok();
+  if (!bt_tags || !page_tags || !req_status) return fail(SPMLA_EINVAL, "%s: null pointer", w);
+  if ((reinterpret_cast<uintptr_t>(bt_tags) | reinterpret_cast<uintptr_t>(page_tags)) & 7u)
+    return fail(SPMLA_EINVAL, "%s: tag arrays must be 8-byte aligned", w);
+  spmla::PageCheckArgs a{block_table, bt_tags, bt_stride, context_lens, batch, max_len, page_tags, num_pages,
+                         page_size, req_status};
+  return map_launch(spmla::launch_page_check(a, reinterpret_cast<hipStream_t>(stream)), w);
+}
+
 }  // extern "C"

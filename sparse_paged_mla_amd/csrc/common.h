@@ -12,7 +12,7 @@
 namespace spmla {
 
 enum : int { kF32 = 0, kBF16 = 1, kFP8 = 2 };
-enum : int { kBadPage = 1, kBadLen = 2, kBadIndex = 4 };
+enum : int { kBadPage = 1, kBadLen = 2, kBadIndex = 4, kBadTag = 8 };
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;

@@ -45,4 +45,10 @@ struct AppendArgs {
 };
 int launch_cache_append(const AppendArgs& a, hipStream_t stream);
 
+struct PageCheckArgs {
+  const int32_t* bt; const uint64_t* bt_tags; int32_t bt_stride; const int32_t* lens; int32_t batch;
+  int64_t max_len; const uint64_t* page_tags; int32_t num_pages, page_size; int32_t* status;
+};
+int launch_page_check(const PageCheckArgs& a, hipStream_t stream);
+
 }  // namespace spmla

@@ -32,7 +32,7 @@ def lib():
 def test_header_declares_the_four_operations():
     names = _declared()
     for n in ("dsa_indexer_scores", "topk_select", "mla_paged_decode", "lse_merge", "topk_workspace_bytes",
-              "kv_cache_append", "spmla_last_error"):
+              "kv_cache_append", "kv_page_check", "spmla_last_error"):
         assert n in names, names
 
 
@@ -163,3 +163,15 @@ def test_append_rejects(lib):
     assert _app(lib, pool=MIS) == EINVAL
     assert "16-byte" in lib.spmla_last_error().decode()
     assert _app(lib, batch=0, rows=None, pool=None, bt=None, pos=None) == OK
+
+
+def test_page_check_rejects(lib):
+    f = lib.kv_page_check
+    assert f(FAKE, FAKE, 4, FAKE, 2, 100, FAKE, 10, 48, FAKE, None) == EUNSUPPORTED
+    assert f(FAKE, FAKE, 0, FAKE, 2, 100, FAKE, 10, 64, FAKE, None) == EINVAL
+    assert f(FAKE, FAKE, 4, FAKE, 2, 100, FAKE, 0, 64, FAKE, None) == EINVAL
+    assert f(FAKE, None, 4, FAKE, 2, 100, FAKE, 10, 64, FAKE, None) == EINVAL
+    assert f(FAKE, FAKE, 4, FAKE, 2, 100, None, 10, 64, FAKE, None) == EINVAL
+    assert f(FAKE, FAKE, 4, FAKE, 2, 100, FAKE, 10, 64, None, None) == EINVAL   # status is the output
+    assert f(FAKE, MIS, 4, FAKE, 2, 100, FAKE, 10, 64, FAKE, None) == EINVAL
+    assert f(None, None, 4, None, 0, 0, None, 10, 64, None, None) == OK
