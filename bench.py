@@ -232,39 +232,45 @@ def main():
     # Every event the timed region records is created (and recorded once)
     # up front: creating events while timing costs the steps measurable time.
     ev_sets = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(args.steps)]
-    for evs in ev_sets:
+    ev_sets_k = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(args.steps)]
+    for evs in ev_sets + ev_sets_k:
         for e in evs:
             e.record()
     torch.cuda.synchronize()
 
-    def run_timed(flush, evs):
+    def run_timed(flush, evs, per_kernel):
+        """One step between evs[0] and evs[-1]; with per_kernel, an event after
+        every stage as well (each such event costs the step 2-3 us, so the
+        step time that gives `value` is taken without them)."""
         if flush:
             flush_sink.copy_(flush_buf.amax())
         evs[0].record()
         for i, name in enumerate(stages):
             getattr(step, name)()
-            evs[i + 1].record()
+            if per_kernel or i == len(stages) - 1:
+                evs[i + 1].record()
         return evs
 
-    # Warm-up steps are the timed steps' exact twins (cache sweep included).
+    # Warm-up steps are the timed steps' twins (cache sweep included).
     flush = not args.no_flush
     for i in range(args.warmup):
-        run_timed(flush, ev_sets[i % args.steps])
+        run_timed(flush, ev_sets[i % args.steps], i % 2 == 1)
     torch.cuda.synchronize()
     assert not step.status.cpu().numpy().any(), "device status flags set on clean inputs"
 
+    # The K timed steps: whole-step events only.
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    recs = [run_timed(flush, evs) for evs in ev_sets]
+    recs = [run_timed(flush, evs, False) for evs in ev_sets]
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    per_stage = {n: [] for n in stages}
-    step_ms = []
-    for evs in recs:
-        step_ms.append(evs[0].elapsed_time(evs[-1]))
-        for i, n in enumerate(stages):
-            per_stage[n].append(evs[i].elapsed_time(evs[i + 1]))
+    step_ms = [evs[0].elapsed_time(evs[-1]) for evs in recs]
     mean_ms = statistics.fmean(step_ms)
+    # K more steps with an event after every kernel: per-kernel times.
+    recs_k = [run_timed(flush, evs, True) for evs in ev_sets_k]
+    torch.cuda.synchronize()
+    per_stage = {n: [evs[i].elapsed_time(evs[i + 1]) for evs in recs_k] for i, n in enumerate(stages)}
+    step_k_ms = statistics.fmean(evs[0].elapsed_time(evs[-1]) for evs in recs_k)
 
     # Warm: K steps back to back (skipped under --profile-only so that a
     # profiler's per-kernel averages cover the same launches as the events).
@@ -341,6 +347,7 @@ def main():
         "step_roofline": {"t_star_us": round(t_star * 1e6, 2), "t_step_us": round(mean_ms * 1e3, 2),
                           "frac": round(t_star / (mean_ms * 1e-3), 4)},
         "kernel_us": {k: round(v * 1e3, 2) for k, v in kernel_ms.items()},
+        "ms_per_step_with_kernel_events": round(step_k_ms, 4),
         "cache_append": app,
         "page_check": chk,
         "step_ms_median_min_max": [round(statistics.median(step_ms), 4), round(min(step_ms), 4),

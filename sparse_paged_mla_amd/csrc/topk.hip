@@ -18,16 +18,21 @@
 //     the request reach tau (fewer only if the sample count falls four
 //     deviations short).  Every workgroup of a
 //     request reads the same sample and derives the same tau.  It then
-//     copies its chunk's keys >= tau, with their indices, to the chunk's own
-//     slice of the candidate buffer and writes their count (no atomics, so
-//     nothing needs clearing between calls).
+//     copies its chunk's keys >= tau, with their indices and in token order,
+//     to the chunk's own slice of the candidate buffer, and writes their
+//     count and smallest and largest key (no atomics, so nothing needs
+//     clearing between calls).
 //  2. finish: one workgroup per request gathers the chunks' candidates into
-//     LDS, selects the k_eff best exactly (11-bit rounds over the key, then
-//     over the index for ties) and writes their indices in ascending order
-//     (an LDS bitmap over [0, L) and a prefix popcount).  Should tau admit
+//     LDS (still in token order) and selects the k_eff best exactly: 11-bit
+//     rounds over the key from the highest bit in which the candidates
+//     differ; once the bin holding the k-th best key has at most 64 keys,
+//     one wave ranks them by (key, index) and the k-th best fixes the
+//     threshold; otherwise the rounds go on and ties are split by rounds
+//     over the index.  The selected indices are written in ascending order
+//     by one block scan over the token-ordered candidates.  Should tau admit
 //     fewer than k keys (the sample fell far short: vanishingly rare for any
 //     spread of scores, but adversarial orders can do it), or more than fit
-//     in LDS (huge tie groups), the same rounds run over the whole request
+//     in LDS (huge tie groups), the same steps run over the whole request
 //     read from the scores, so the result is exact in every case.
 #include "common.h"
 #include "launch.h"
@@ -44,14 +49,13 @@ constexpr int kFinThreads = 1024;
 constexpr int kMaxK = 4096;
 constexpr int kSampleRuns = 16, kSampleRun = 256;
 constexpr int kSample = kSampleRuns * kSampleRun;  // keys sampled from a long request
-constexpr int kFinLdsWords = 32768;              // 128 KiB: candidates, then the bitmap
+constexpr int kFinLdsWords = 32768;              // 128 KiB of gathered candidates
 constexpr int kCandLds = kFinLdsWords / 2;       // candidates that fit in LDS (uint2 each)
-constexpr int64_t kBitmapBits = (int64_t)kFinLdsWords * 32;
 static_assert(kSample == kTkChunk, "a collect workgroup holds one sample key per chunk key");
 
 struct TopkWs {
-  uint32_t* count;  // [B, chunks] candidates of each chunk
-  uint2* cand;      // [B, chunks, kTkChunk] (key, index), chunk c's in its own slice
+  uint4* meta;      // [B, chunks] (candidate count, smallest key, largest key, 0) of each chunk
+  uint2* cand;      // [B, chunks, kTkChunk] (key, index), chunk c's in its own slice, ascending index
   int32_t chunks;
 };
 
@@ -62,7 +66,7 @@ size_t topk_workspace_size(int32_t batch, int64_t max_len, int32_t k) {
   (void)k;
   if (batch <= 0 || max_len < 0) return 0;
   const size_t bc = (size_t)batch * (size_t)n_chunks(max_len);
-  return align_up(bc * 4, 256) + bc * kTkChunk * 8;
+  return align_up(bc * 16, 256) + bc * kTkChunk * 8;
 }
 
 static TopkWs carve(void* ws, int32_t batch, int64_t max_len) {
@@ -70,8 +74,8 @@ static TopkWs carve(void* ws, int32_t batch, int64_t max_len) {
   uint8_t* p = reinterpret_cast<uint8_t*>(ws);
   w.chunks = n_chunks(max_len);
   const size_t bc = (size_t)batch * (size_t)w.chunks;
-  w.count = reinterpret_cast<uint32_t*>(p);
-  w.cand = reinterpret_cast<uint2*>(p + align_up(bc * 4, 256));
+  w.meta = reinterpret_cast<uint4*>(p);
+  w.cand = reinterpret_cast<uint2*>(p + align_up(bc * 16, 256));
   return w;
 }
 
@@ -253,8 +257,11 @@ __device__ uint32_t request_tau(const float* __restrict__ s, int32_t L, int32_t 
 }
 
 // (request, chunk) workgroups: every key >= tau goes to the chunk's slice of
-// the candidate buffer, in chunk order (one block scan), and the chunk's
-// count to its slot.
+// the candidate buffer in ascending token order, and the chunk's count and
+// smallest and largest candidate keys to its metadata slot.  Key j of
+// thread tid is token t0 + j*256 + tid, so token order is row j first: each
+// wave ballots its selected keys row by row, and one wave scan over the 64
+// (row, wave) counts gives every key its place.
 __global__ __launch_bounds__(kTkThreads) void topk_collect_kernel(const float* __restrict__ scores, int64_t stride,
                                                                   const int32_t* __restrict__ lens, int64_t max_len,
                                                                   int32_t k, TopkWs ws) {
@@ -262,6 +269,8 @@ __global__ __launch_bounds__(kTkThreads) void topk_collect_kernel(const float* _
   __shared__ uint32_t tmp[kTkThreads / 64];
   __shared__ uint32_t res[2];
   __shared__ uint32_t s_mm[2];
+  __shared__ uint32_t rw[kTkPer * (kTkThreads / 64)];  // (row, wave) counts, then their exclusive scan
+  static_assert(kTkPer * (kTkThreads / 64) == 64, "one wave scans the (row, wave) counts");
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
   const int b = logical / ws.chunks, chunk = logical % ws.chunks;
   const int32_t L = lens[b];
@@ -274,18 +283,37 @@ __global__ __launch_bounds__(kTkThreads) void topk_collect_kernel(const float* _
   bool in[kTkPer];
   load_chunk(s, t0, t1, key, in);
   const uint32_t tau = request_tau(s, L, k, h, tmp, res, s_mm);
-  uint32_t c = 0;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const uint64_t below = (1ull << lane) - 1ull;
+  uint32_t rank[kTkPer];
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
 #pragma unroll
-  for (int j = 0; j < kTkPer; ++j) c += (in[j] && key[j] >= tau) ? 1u : 0u;
-  const uint32_t incl = block_incl_scan<kTkThreads>(c, tmp);
+  for (int j = 0; j < kTkPer; ++j) {
+    const bool sel = in[j] && key[j] >= tau;
+    const uint64_t m = __ballot(sel);
+    rank[j] = (uint32_t)__popcll(m & below);
+    if (lane == 0) rw[j * (kTkThreads / 64) + wv] = (uint32_t)__popcll(m);
+    if (sel) { kmin = min(kmin, key[j]); kmax = max(kmax, key[j]); }
+  }
+  kmin = wave_min_u32(kmin);
+  kmax = wave_max_u32(kmax);
+  if (threadIdx.x == 0) { s_mm[0] = 0xFFFFFFFFu; s_mm[1] = 0u; }
+  __syncthreads();
+  if (lane == 0) { atomicMin(&s_mm[0], kmin); atomicMax(&s_mm[1], kmax); }
+  if (wv == 0) {
+    const uint32_t v = rw[lane];
+    const uint32_t incl = wave_incl_scan(v);
+    rw[lane] = incl - v;
+    if (lane == 63) res[0] = incl;
+  }
+  __syncthreads();
   const int64_t slot = (int64_t)b * ws.chunks + chunk;
-  if (threadIdx.x == kTkThreads - 1) ws.count[slot] = incl;
-  uint32_t p = incl - c;
+  if (threadIdx.x == 0) ws.meta[slot] = make_uint4(res[0], s_mm[0], s_mm[1], 0u);
   uint2* cb = ws.cand + slot * kTkChunk;
 #pragma unroll
   for (int j = 0; j < kTkPer; ++j) {
     const int64_t t = t0 + (int64_t)j * kTkThreads + threadIdx.x;
-    if (in[j] && key[j] >= tau) cb[p++] = make_uint2(key[j], (uint32_t)t);
+    if (in[j] && key[j] >= tau) cb[rw[j * (kTkThreads / 64) + wv] + rank[j]] = make_uint2(key[j], (uint32_t)t);
   }
 }
 
@@ -293,15 +321,18 @@ __global__ __launch_bounds__(kFinThreads) void topk_finish_kernel(const float* _
                                                                   const int32_t* __restrict__ lens, int64_t max_len,
                                                                   int32_t k, TopkWs ws, int32_t* __restrict__ out_idx,
                                                                   int32_t* __restrict__ status) {
-  __shared__ uint32_t big[kFinLdsWords];   // candidates (uint2), later the bitmap
+  __shared__ uint32_t big[kFinLdsWords];   // gathered candidates (uint2)
   __shared__ uint32_t h[kBins];
-  __shared__ int32_t sel[kMaxK];
   __shared__ uint32_t tmp[kFinThreads / 64];
   __shared__ uint32_t res[2];
   __shared__ uint32_t coff[kFinThreads];  // chunk offsets in the gathered candidate list
-  __shared__ uint32_t cnt;
+  __shared__ uint32_t ccnt[kFinThreads];  // chunk candidate counts
+  __shared__ uint32_t s_mm[2];
+  __shared__ uint2 bin_list[64];           // members of the boundary bin, when few
+  __shared__ uint32_t bin_cnt;
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
+  const int lane = tid & 63;
   const int32_t L = lens[b];
   int32_t* out = out_idx + (int64_t)b * k;
   if (!len_ok(L, max_len)) {
@@ -313,58 +344,53 @@ __global__ __launch_bounds__(kFinThreads) void topk_finish_kernel(const float* _
     for (int j = tid; j < k; j += kFinThreads) out[j] = j < L ? j : -1;
     return;
   }
-  // Candidates: the chunks' keys >= tau gathered into LDS, or, should fewer
-  // than k or more than LDS holds have reached tau (or the request have more
-  // chunks than this workgroup has threads), every key of the request read
-  // from the scores.
+  // Candidates: the chunks' keys >= tau gathered into LDS in token order, or,
+  // should fewer than k or more than LDS holds have reached tau (or the
+  // request have more chunks than this workgroup has threads), every key of
+  // the request read from the scores.
   const int n_act = (int)((L + kTkChunk - 1) / kTkChunk);
   const int64_t slot0 = (int64_t)b * ws.chunks;
-  const uint32_t c_mine = (tid < n_act) ? ws.count[slot0 + tid] : 0u;
-  const uint32_t c_incl = block_incl_scan<kFinThreads>(c_mine, tmp);
-  if (tid < n_act) coff[tid] = c_incl - c_mine;
+  const uint4 meta = (tid < n_act) ? ws.meta[slot0 + tid] : make_uint4(0u, 0xFFFFFFFFu, 0u, 0u);
+  if (tid == 0) { s_mm[0] = 0xFFFFFFFFu; s_mm[1] = 0u; }
+  const uint32_t c_incl = block_incl_scan<kFinThreads>(meta.x, tmp);
+  if (tid < n_act) { coff[tid] = c_incl - meta.x; ccnt[tid] = meta.x; }
   if (tid == kFinThreads - 1) res[0] = c_incl;
+  {
+    const uint32_t wmin = wave_min_u32(meta.y), wmax = wave_max_u32(meta.z);
+    if (lane == 0) { atomicMin(&s_mm[0], wmin); atomicMax(&s_mm[1], wmax); }
+  }
   __syncthreads();
   const uint32_t n_cand = res[0];
   const bool whole = n_cand < (uint32_t)k || n_cand > (uint32_t)kCandLds || n_act > kFinThreads;
   const uint32_t n_c = whole ? (uint32_t)L : n_cand;
   const float* srow = scores + (int64_t)b * stride;
   uint2* lc = reinterpret_cast<uint2*>(big);
-  uint32_t cmax = 0u;  // largest candidate key (all candidates are >= tau)
   if (!whole) {
-    // Candidate j lives in the last chunk c with coff[c] <= j (binary search).
-    for (uint32_t j = tid; j < n_cand; j += kFinThreads) {
-      int lo_c = 0, hi_c = n_act - 1;
-      while (lo_c < hi_c) {
-        const int mid = (lo_c + hi_c + 1) >> 1;
-        if (coff[mid] <= j) lo_c = mid; else hi_c = mid - 1;
-      }
-      const uint2 e = ws.cand[(slot0 + lo_c) * kTkChunk + (j - coff[lo_c])];
-      lc[j] = e;
-      cmax = max(cmax, e.x);
+    // Wave w copies chunks w, w + 16, ...: each chunk's slice goes to its
+    // offset in the gathered list.
+    for (int c = tid >> 6; c < n_act; c += kFinThreads / 64) {
+      const uint32_t n = ccnt[c], off = coff[c];
+      const uint2* src = ws.cand + (slot0 + c) * kTkChunk;
+      for (uint32_t i = lane; i < n; i += 64) lc[off + i] = src[i];
     }
   }
-  cmax = wave_max_u32(cmax);
-  uint32_t cmin = 0xFFFFFFFFu;  // smallest candidate key
-  if (!whole)
-    for (uint32_t j = tid; j < n_c; j += kFinThreads) cmin = min(cmin, lc[j].x);
-  cmin = wave_min_u32(cmin);
-  if (tid == 0) { res[0] = 0u; res[1] = 0xFFFFFFFFu; }
-  __syncthreads();
-  if ((tid & 63) == 0) { atomicMax(&res[0], cmax); atomicMin(&res[1], cmin); }
-  __syncthreads();
-  cmax = res[0];
-  cmin = res[1];
+  const uint32_t cmin = s_mm[0], cmax = s_mm[1];
+  if (tid == 0) bin_cnt = 0u;
   __syncthreads();
   const uint2* cb = lc;
   auto cand = [&](uint32_t j) -> uint2 { return whole ? make_uint2(order_key(srow[j]), j) : cb[j]; };
   uint32_t need = (uint32_t)k;
   // Key rounds, 11 bits at a time from the highest bit in which the
-  // candidates can differ (they lie in [tau, largest collected key]; all 32
-  // bits for the whole request): the k-th best key T among the candidates.
+  // candidates can differ (they lie in [smallest, largest collected key];
+  // all 32 bits for the whole request).  After a round, a boundary bin of at
+  // most 64 keys is finished by one wave ranking them instead of further
+  // rounds.
   uint32_t kpre = 0, kmask = 0;  // determined high-bit prefix
   int hi0 = 32;
   if (!whole) hi0 = first_round_top(cmin, cmax, &kpre, &kmask);
-  for (int hi = hi0; hi > 0; hi -= 11) {
+  uint32_t T = 0, I = 0xFFFFFFFFu;  // selection: key > T, or key == T and index <= I
+  bool done = false;
+  for (int hi = hi0; hi > 0 && !done; hi -= 11) {
     const int lo = max(hi - 11, 0);
     const uint32_t wmask = (1u << (hi - lo)) - 1u;
     for (int i = tid; i < kBins; i += kFinThreads) h[i] = 0u;
@@ -375,18 +401,47 @@ __global__ __launch_bounds__(kFinThreads) void topk_finish_kernel(const float* _
     }
     __syncthreads();
     find_bin_desc<kBins, kFinThreads>(h, need, tmp, res);
-    kpre |= res[0] << lo;
+    const uint32_t bin = res[0];
+    kpre |= bin << lo;
     kmask |= wmask << lo;
     need -= res[1];
+    const uint32_t in_bin = h[bin];
+    __syncthreads();  // h and res are read before the next round rewrites them
+    if (in_bin <= 64u) {
+      // The keys of the boundary bin: the `need` best of them (by key, then
+      // index; indices are distinct, so the order is total) complete the
+      // selection.
+      for (uint32_t j = tid; j < n_c; j += kFinThreads) {
+        const uint2 e = cand(j);
+        if ((e.x & kmask) == kpre) bin_list[atomicAdd(&bin_cnt, 1u)] = e;
+      }
+      __syncthreads();
+      if (tid < (int)in_bin) {
+        // Rank of this lane's key among the bin's keys (larger key first,
+        // then smaller index); the entry of rank need - 1 is the last one
+        // selected.  Every lane reads the same LDS word at a time.
+        const uint2 e = bin_list[tid];
+        uint32_t rank = 0;
+        for (uint32_t m = 0; m < in_bin; ++m) {
+          const uint2 o = bin_list[m];
+          rank += (o.x > e.x || (o.x == e.x && o.y < e.y)) ? 1u : 0u;
+        }
+        if (rank == need - 1) { res[0] = e.x; res[1] = e.y; }
+      }
+      __syncthreads();
+      T = res[0];
+      I = res[1];
+      done = true;
+    }
   }
-  // T = kpre.  Among keys equal to T take the `need` lowest indices (index
-  // threshold I, inclusive).
-  uint32_t I = 0xFFFFFFFFu;
-  {
+  if (!done) {
+    // T = kpre.  Among keys equal to T take the `need` lowest indices (index
+    // threshold I, inclusive).
+    T = kpre;
     for (int i = tid; i < kBins; i += kFinThreads) h[i] = 0u;
     __syncthreads();
     uint32_t n_eq_local = 0;
-    for (uint32_t j = tid; j < n_c; j += kFinThreads) n_eq_local += (cand(j).x == kpre) ? 1u : 0u;
+    for (uint32_t j = tid; j < n_c; j += kFinThreads) n_eq_local += (cand(j).x == T) ? 1u : 0u;
     const uint32_t n_eq = block_incl_scan<kFinThreads>(n_eq_local, tmp);  // last thread holds the total
     if (tid == kFinThreads - 1) res[0] = n_eq;
     __syncthreads();
@@ -401,7 +456,7 @@ __global__ __launch_bounds__(kFinThreads) void topk_finish_kernel(const float* _
         __syncthreads();
         for (uint32_t j = tid; j < n_c; j += kFinThreads) {
           const uint2 e = cand(j);
-          if (e.x == kpre && (e.y & imask) == ipre) atomicAdd(&h[(e.y >> lo) & wmask], 1u);
+          if (e.x == T && (e.y & imask) == ipre) atomicAdd(&h[(e.y >> lo) & wmask], 1u);
         }
         __syncthreads();
         find_bin_asc<kBins, kFinThreads>(h, need, tmp, res);
@@ -412,59 +467,17 @@ __global__ __launch_bounds__(kFinThreads) void topk_finish_kernel(const float* _
       I = ipre;
     }
   }
-  // Gather the k indices: candidates above T, and those equal to T up to index I.
-  if (tid == 0) cnt = 0u;
-  __syncthreads();
-  for (uint32_t j = tid; j < n_c; j += kFinThreads) {
+  // The candidates are in ascending token order, so the selected ones are
+  // written in order by one block scan: thread tid takes a contiguous run.
+  const uint32_t per = (n_c + kFinThreads - 1) / kFinThreads;
+  const uint32_t j0 = min(n_c, tid * per), j1 = min(n_c, j0 + per);
+  auto picked = [&](const uint2 e) { return e.x > T || (e.x == T && e.y <= I); };
+  uint32_t mine = 0;
+  for (uint32_t j = j0; j < j1; ++j) mine += picked(cand(j)) ? 1u : 0u;
+  uint32_t pos = block_incl_scan<kFinThreads>(mine, tmp) - mine;
+  for (uint32_t j = j0; j < j1 && pos < (uint32_t)k; ++j) {
     const uint2 e = cand(j);
-    if (e.x > kpre || (e.x == kpre && e.y <= I)) {
-      const uint32_t p = atomicAdd(&cnt, 1u);
-      if (p < (uint32_t)k) sel[p] = (int32_t)e.y;
-    }
-  }
-  __syncthreads();
-  if ((int64_t)L <= kBitmapBits) {
-    // Ascending order via an LDS bitmap over [0, L) and a prefix popcount.
-    const int words = (int)((L + 31) / 32);
-    for (int i = tid; i < words; i += kFinThreads) big[i] = 0u;
-    __syncthreads();
-    for (int j = tid; j < k; j += kFinThreads) {
-      const int32_t t = sel[j];
-      atomicOr(&big[t >> 5], 1u << (t & 31));
-    }
-    __syncthreads();
-    const int per = (words + kFinThreads - 1) / kFinThreads;
-    const int w0 = min(words, tid * per), w1 = min(words, w0 + per);
-    uint32_t mine = 0;
-    for (int i = w0; i < w1; ++i) mine += __popc(big[i]);
-    uint32_t pos = block_incl_scan<kFinThreads>(mine, tmp) - mine;
-    for (int i = w0; i < w1; ++i) {
-      uint32_t m = big[i];
-      while (m) {
-        const int bit = __ffs(m) - 1;
-        m &= m - 1u;
-        out[pos++] = i * 32 + bit;
-      }
-    }
-  } else {
-    // Bitonic sort of the k entries (padded with INT_MAX) in place.
-    int n2 = 1;
-    while (n2 < k) n2 <<= 1;
-    for (int j = k + tid; j < n2; j += kFinThreads) sel[j] = 0x7FFFFFFF;
-    __syncthreads();
-    for (int size = 2; size <= n2; size <<= 1) {
-      for (int stride = size >> 1; stride > 0; stride >>= 1) {
-        for (int i = tid; i < n2 / 2; i += kFinThreads) {
-          const int lo = 2 * i - (i & (stride - 1));
-          const int hi = lo + stride;
-          const bool up = (lo & size) == 0;
-          const int32_t a = sel[lo], c = sel[hi];
-          if ((a > c) == up) { sel[lo] = c; sel[hi] = a; }
-        }
-        __syncthreads();
-      }
-    }
-    for (int j = tid; j < k; j += kFinThreads) out[j] = sel[j];
+    if (picked(e)) out[pos++] = (int32_t)e.y;
   }
 }
 
