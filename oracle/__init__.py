@@ -244,3 +244,39 @@ def page_check(block_table, bt_tags, lens, page_tags, page_size, max_len=None):
     assert _load().oracle_page_check(_p(bt), _p(tags), bt.shape[1], _p(lens), B, max_len, _p(pt), pt.shape[0],
                                      int(page_size), _p(status)) == 0
     return status
+
+
+def multi_query_step(q, q_idx, w, kv, kv_scale, k_pool, k_scale, block_table, lens, k, n_heads, d_latent, d_rope,
+                     sm_scale, score_stride=None):
+    """Verification step over Q new tokens per request (all already in the
+    cache, at positions L-Q .. L-1), in one pass: the target model checks the
+    gamma+1 drafted positions with one parallel forward, position by position
+    in order [EG, "Speculative Decoding": why it is lossless; KW 5.3].
+    Query i sees only tokens t < L - Q + 1 + i (itself and what precedes it)
+    and has its own indexer scores, its own top-k and its own attention.
+
+    q [B, Q, H, D], q_idx [B, Q, H_I, d_I], w [B, Q, H_I]; a request with
+    L < Q is flagged BAD_LEN and its outputs are NaN.  Returns dict(scores
+    [B, Q, stride], idx [B, Q, k], o [B, Q, H, d_latent], lse [B, Q, H],
+    status [B], vis [B, Q])."""
+    B, Q = q.shape[0], q.shape[1]
+    lens = np.asarray(lens, np.int64)
+    bad = lens < Q
+    vis = np.where(bad[:, None], 0, lens[:, None] - Q + 1 + np.arange(Q)[None, :]).astype(np.int32)
+    stride = max(int(lens.max()), 1) if score_stride is None else int(score_stride)
+    scores = np.full((B, Q, stride), np.nan)
+    idx = np.full((B, Q, k), -1, np.int32)
+    o = np.full((B, Q, n_heads, d_latent), np.nan)
+    lse = np.full((B, Q, n_heads), np.nan)
+    status = np.where(bad, BAD_LEN, 0).astype(np.int32)
+    ok = ~bad
+    if ok.any():
+        for i in range(Q):
+            s, _, st = indexer_scores(q_idx[ok, i], w[ok, i], k_pool, k_scale, block_table[ok], vis[ok, i],
+                                      max_len=int(lens.max()), score_stride=stride)
+            sel = topk(s, vis[ok, i], k)
+            oi, li, st2 = mla_attention(q[ok, i], kv, kv_scale, block_table[ok], vis[ok, i], sel, n_heads, d_latent,
+                                        d_rope, sm_scale, max_len=int(lens.max()))
+            scores[ok, i], idx[ok, i], o[ok, i], lse[ok, i] = s, sel, oi, li
+            status[ok] |= st | st2
+    return dict(scores=scores, idx=idx, o=o, lse=lse, status=status, vis=vis)

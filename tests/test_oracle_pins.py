@@ -619,3 +619,41 @@ def test_page_check_matches_numpy_brute_force():
         bad_tag = used & ~bad_page & (page_tags[safe] != bt_tags)
         want = np.where(bad_page.any(1), oracle.BAD_PAGE, 0) | np.where(bad_tag.any(1), oracle.BAD_TAG, 0)
         np.testing.assert_array_equal(oracle.page_check(bt, bt_tags, lens, page_tags, P), want)
+
+
+# ---------------------------------------------------------- multi-query step
+
+def test_multi_query_step_matches_causal_brute_force():
+    """Q new tokens per request with k >= L (every visible token selected):
+    each query's attention equals a numpy softmax over the tokens a causal
+    mask (numpy tril) leaves it, and its scores equal an einsum brute force on
+    exactly those tokens; a request shorter than Q is flagged."""
+    Q = 3
+    cfg = gen.CONFIGS["c1"].with_(batch=3)
+    inp = gen.make_inputs(cfg, lens=[37, 5, 2], shuffle=True)
+    rng = np.random.default_rng(8)
+    q = rng.standard_normal((3, Q, cfg.n_heads, cfg.dim)).astype(np.float32)
+    q_idx = rng.standard_normal((3, Q, cfg.idx_heads, cfg.idx_dim)).astype(np.float32)
+    w = rng.standard_normal((3, Q, cfg.idx_heads)).astype(np.float32)
+    r = oracle.multi_query_step(q, q_idx, w, inp.kv, inp.kv_scale, inp.k_idx, inp.k_idx_scale, inp.block_table,
+                                inp.lens, 64, cfg.n_heads, cfg.d_latent, cfg.d_rope, cfg.softmax_scale)
+    assert list(r["status"]) == [0, 0, oracle.BAD_LEN]
+    P = cfg.page_size
+    for b in range(2):
+        L = int(inp.lens[b])
+        rows = np.array([int(inp.block_table[b, t // P]) * P + t % P for t in range(L)])
+        c = inp.kv.reshape(-1, cfg.dim)[rows].astype(np.float64)
+        kk = inp.k_idx.reshape(-1, cfg.idx_dim)[rows].astype(np.float64)
+        mask = np.tril(np.ones((L, L), bool))[L - Q:]         # row i: what position L-Q+i may see
+        for i in range(Q):
+            vis = mask[i]
+            assert vis.sum() == L - Q + 1 + i
+            dots = np.einsum("hd,td->ht", q_idx[b, i].astype(np.float64), kk)
+            s_ref = np.einsum("h,ht->t", w[b, i].astype(np.float64), np.maximum(dots, 0.0))
+            np.testing.assert_allclose(r["scores"][b, i, :vis.sum()], s_ref[vis], rtol=1e-12, atol=1e-12)
+            z = cfg.softmax_scale * np.einsum("hd,td->ht", q[b, i].astype(np.float64), c)[:, vis]
+            np.testing.assert_allclose(r["o"][b, i], softmax(z, axis=1) @ c[vis, :cfg.d_latent], rtol=1e-10,
+                                       atol=1e-12)
+            np.testing.assert_allclose(r["lse"][b, i], logsumexp(z, axis=1), rtol=1e-12)
+            assert list(r["idx"][b, i, :vis.sum()]) == list(np.nonzero(vis)[0])
+    assert np.isnan(r["o"][2]).all()
