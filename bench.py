@@ -179,6 +179,45 @@ def time_page_check(cfg, db, inp, steps, flush, run_flush):
             "achieved_GBps": round(nbytes / (us * 1e-6) / 1e9, 1)}
 
 
+def time_multi_query(cfg, db, inp, n_q, splits, steps, flush, run_flush):
+    """A verification step over n_q new tokens per request (query i attends
+    causally, with its own scores and top-k): mq_expand_requests and the four
+    calls on the expanded batch, timed cold like the step."""
+    import numpy as np
+    import torch
+    import spmla_gen as gen
+    from spmla_gen.torch_io import tensor
+    from sparse_paged_mla_amd.step import MultiQueryStep
+    q, qi, w = gen.make_mq_queries(inp, n_q)
+    st = MultiQueryStep(db, tensor(q, "cuda"), tensor(qi, "cuda"), torch.from_numpy(w).cuda(), num_splits=splits)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for _ in range(5):
+        st.run()
+    for e0, e1 in evs:
+        if flush:
+            run_flush()
+        e0.record()
+        st.run()
+        e1.record()
+    torch.cuda.synchronize()
+    assert not st.status.cpu().numpy().any(), "multi-query step flagged a request on clean inputs"
+    us = statistics.fmean(e0.elapsed_time(e1) for e0, e1 in evs) * 1e3
+    # Roofline of the method: every query's scores, top-k and attention, with
+    # the indexer keys read once for all n_q queries (what a fused indexer
+    # would move; this composition reads them once per query).
+    alg = algorithmic(cfg, inp.lens)
+    sumL = int(inp.lens.sum())
+    t_star = (max((alg["indexer"]["bytes"] + (n_q - 1) * 4 * sumL) / (HBM_PEAK_GBS * 1e9),
+                  n_q * alg["indexer"]["flops"] / (BF16_PEAK_TFLOPS * 1e12))
+              + n_q * alg["topk"]["bytes"] / (HBM_PEAK_GBS * 1e9)
+              + max(n_q * alg["decode"]["bytes"] / (HBM_PEAK_GBS * 1e9),
+                    n_q * alg["decode"]["flops"] / (BF16_PEAK_TFLOPS * 1e12)))
+    return {"n_q": n_q, "us_per_step": round(us, 2), "verified_tokens_per_s": round(cfg.batch * n_q / (us * 1e-6), 1),
+            "t_star_us": round(t_star * 1e6, 2), "frac": round(t_star / (us * 1e-6), 4), "num_splits": splits,
+            "note": "expanded batch of batch*n_q requests through the single-query kernels; "
+                    "indexer keys are read once per query"}
+
+
 def cpu_baseline(inp, n_req):
     """The fp64 oracle, as it stands, on the first n_req requests of the same inputs (one thread)."""
     import numpy as np
@@ -288,6 +327,8 @@ def main():
                                                                                  run_flush=lambda: flush_sink.copy_(
                                                                                      flush_buf.amax()))
 
+    mq = None if cfg.dense else time_multi_query(cfg, db, inp, 2, splits, args.steps, flush,
+                                                 run_flush=lambda: flush_sink.copy_(flush_buf.amax()))
     chk = time_page_check(cfg, db, inp, args.steps, flush, run_flush=lambda: flush_sink.copy_(flush_buf.amax()))
     chk["overhead_frac_of_step"] = round(chk["us"] / (mean_ms * 1e3), 4)
 
@@ -350,6 +391,7 @@ def main():
         "ms_per_step_with_kernel_events": round(step_k_ms, 4),
         "cache_append": app,
         "page_check": chk,
+        "multi_query": mq,
         "step_ms_median_min_max": [round(statistics.median(step_ms), 4), round(min(step_ms), 4),
                                    round(max(step_ms), 4)],
         "warm_ms_per_step": None if warm_ms != warm_ms else round(warm_ms, 4),

@@ -253,6 +253,27 @@ int kv_page_check(const int32_t* block_table, const uint64_t* bt_tags, int32_t b
                   const uint64_t* page_tags, int32_t num_pages, int32_t page_size,
                   int32_t* req_status, void* stream);
 
+/*
+ * mq_expand_requests -- bookkeeping for a multi-query verification step.  A
+ * speculative step verifies the gamma+1 drafted positions of each request
+ * in one parallel forward, each position seeing only itself and what
+ * precedes it [EG, "Speculative Decoding"; KW 5.3].  With the n_q new tokens
+ * already in the cache (context_lens counts them), query i of request b is
+ * run as request v = b * n_q + i of an expanded batch: block-table row v is
+ * a copy of row b and its length is L_b - n_q + 1 + i.  The indexer, top-k,
+ * decode and merge calls then take the expanded batch unchanged (queries
+ * laid out [batch, n_q, ...] are already [batch * n_q, ...]), so every query
+ * gets its own scores, its own top-k and its own attention.
+ *
+ *  block_table [batch, bt_stride], context_lens [batch]: the real requests.
+ *  out_block_table [batch * n_q, bt_stride], out_lens [batch * n_q]: written.
+ *  A request with L_b < n_q gets length -1 for all its queries, which the
+ *  later calls flag as SPMLA_REQ_BAD_LEN.  Supported: 1 <= n_q <= 64.
+ */
+int mq_expand_requests(const int32_t* block_table, int32_t bt_stride, const int32_t* context_lens,
+                       int32_t batch, int32_t n_q, int32_t* out_block_table, int32_t* out_lens,
+                       void* stream);
+
 /* Message of the last failing call on this thread (host memory, valid until
  * the next call on this thread). */
 const char* spmla_last_error(void);

@@ -54,6 +54,8 @@ def load_library():
     lib.kv_cache_append.argtypes = [vp, i32, i32, i32, vp, vp, i32, i32, i32, vp, i32, vp, vp, vp]
     lib.kv_page_check.restype = ctypes.c_int
     lib.kv_page_check.argtypes = [vp, vp, i32, vp, i32, i64, vp, i32, i32, vp, vp]
+    lib.mq_expand_requests.restype = ctypes.c_int
+    lib.mq_expand_requests.argtypes = [vp, i32, vp, i32, i32, vp, vp, vp]
     lib.lse_merge.restype = ctypes.c_int
     lib.lse_merge.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp]
     lib.spmla_last_error.restype = ctypes.c_char_p
@@ -166,3 +168,14 @@ def kv_page_check(block_table, bt_tags, context_lens, max_len, page_tags, page_s
     _check(lib.kv_page_check(_ptr(block_table), _ptr(bt_tags), block_table.shape[1], _ptr(context_lens), B,
                              int(max_len), _ptr(page_tags), page_tags.shape[0], int(page_size), _ptr(req_status),
                              _stream(stream)))
+
+
+def mq_expand_requests(block_table, context_lens, n_q, out_block_table, out_lens, stream=None):
+    """Expanded batch of a multi-query step: request b * n_q + i is query i of
+    request b (same block-table row, length L_b - n_q + 1 + i)."""
+    lib = load_library()
+    B = context_lens.shape[0]
+    if out_block_table.shape != (B * n_q, block_table.shape[1]) or out_lens.shape != (B * n_q,):
+        raise ValueError("output shapes must be [B * n_q, bt_stride] and [B * n_q]")
+    _check(lib.mq_expand_requests(_ptr(block_table), block_table.shape[1], _ptr(context_lens), B, int(n_q),
+                                  _ptr(out_block_table), _ptr(out_lens), _stream(stream)))

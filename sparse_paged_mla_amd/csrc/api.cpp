@@ -181,4 +181,16 @@ int kv_page_check(const int32_t* block_table, const uint64_t* bt_tags, int32_t b
   return map_launch(spmla::launch_page_check(a, reinterpret_cast<hipStream_t>(stream)), w);
 }
 
+int mq_expand_requests(const int32_t* block_table, int32_t bt_stride, const int32_t* context_lens, int32_t batch,
+                       int32_t n_q, int32_t* out_block_table, int32_t* out_lens, void* stream) {
+  const char* w = "mq_expand_requests";
+  if (batch < 0) return fail(SPMLA_EINVAL, "%s: batch < 0", w);
+  if (n_q < 1 || n_q > 64) return fail(SPMLA_EUNSUPPORTED, "%s: n_q must be in [1, 64]", w);
+  if (bt_stride < 1) return fail(SPMLA_EINVAL, "%s: bt_stride must be >= 1", w);
+  if (batch == 0) return ok();
+  if (!block_table || !context_lens || !out_block_table || !out_lens) return fail(SPMLA_EINVAL, "%s: null pointer", w);
+  spmla::MqExpandArgs a{block_table, bt_stride, context_lens, batch, n_q, out_block_table, out_lens};
+  return map_launch(spmla::launch_mq_expand(a, reinterpret_cast<hipStream_t>(stream)), w);
+}
+
 }  // extern "C"

@@ -51,4 +51,9 @@ struct PageCheckArgs {
 };
 int launch_page_check(const PageCheckArgs& a, hipStream_t stream);
 
+struct MqExpandArgs {
+  const int32_t* bt; int32_t bt_stride; const int32_t* lens; int32_t batch, n_q; int32_t* out_bt; int32_t* out_lens;
+};
+int launch_mq_expand(const MqExpandArgs& a, hipStream_t stream);
+
 }  // namespace spmla

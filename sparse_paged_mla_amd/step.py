@@ -7,7 +7,8 @@ from typing import Optional
 
 import torch
 
-from . import (dsa_indexer_scores, lse_merge, mla_paged_decode, topk_select, topk_workspace_bytes)
+from . import (dsa_indexer_scores, lse_merge, mla_paged_decode, mq_expand_requests, topk_select,
+               topk_workspace_bytes)
 
 
 @dataclass
@@ -83,3 +84,60 @@ class DecodeStep:
             self.select(stream)
         self.attend(stream)
         self.merge(stream)
+
+
+class MultiQueryStep:
+    """A verification step over n_q new tokens per request (already in the
+    cache): query i of request b attends causally, to the tokens before
+    position L_b - n_q + i + 1, with its own indexer scores and top-k.
+
+    q [B, n_q, H, D], q_idx [B, n_q, H_I, d_I], w [B, n_q, H_I] on the device;
+    `batch` supplies the pools, block table and lengths of the B requests.
+    One mq_expand_requests call builds the expanded batch (B * n_q requests);
+    the four calls of DecodeStep then run on it.  Outputs o [B, n_q, H, d_c],
+    lse [B, n_q, H], idx [B, n_q, k] and status [B, n_q] are views of the
+    expanded step's buffers."""
+
+    def __init__(self, batch: DeviceBatch, q, q_idx, w, num_splits: int = 1):
+        B, n_q = q.shape[0], q.shape[1]
+        dev = q.device
+        self.B, self.n_q = B, n_q
+        self.real_bt, self.real_lens = batch.block_table, batch.lens
+        self.bt = torch.empty(B * n_q, batch.block_table.shape[1], dtype=torch.int32, device=dev)
+        self.lens = torch.empty(B * n_q, dtype=torch.int32, device=dev)
+        ex = DeviceBatch(q=q.reshape(B * n_q, *q.shape[2:]), kv=batch.kv, kv_scale=batch.kv_scale,
+                         block_table=self.bt, lens=self.lens, max_len=batch.max_len,
+                         score_stride=batch.score_stride, d_latent=batch.d_latent, sm_scale=batch.sm_scale,
+                         topk=batch.topk, q_idx=q_idx.reshape(B * n_q, *q_idx.shape[2:]),
+                         w=w.reshape(B * n_q, w.shape[2]), k_idx=batch.k_idx, k_idx_scale=batch.k_idx_scale)
+        self.step = DecodeStep(ex, num_splits=num_splits)
+
+    def expand(self, stream=None):
+        mq_expand_requests(self.real_bt, self.real_lens, self.n_q, self.bt, self.lens, stream)
+
+    def run(self, stream=None):
+        self.expand(stream)
+        self.step.run(stream)
+
+    def _view(self, t):
+        return t.reshape(self.B, self.n_q, *t.shape[1:])
+
+    @property
+    def o(self):
+        return self._view(self.step.o)
+
+    @property
+    def lse(self):
+        return self._view(self.step.lse)
+
+    @property
+    def idx(self):
+        return self._view(self.step.idx)
+
+    @property
+    def scores(self):
+        return self._view(self.step.scores)
+
+    @property
+    def status(self):
+        return self._view(self.step.status)

@@ -24,7 +24,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libspmla_gen.so")
 _lib = None
 
-T_LENS, T_PERM, T_Q, T_KV, T_QIDX, T_W, T_KIDX, T_FILL, T_NEW_KV, T_NEW_KIDX = range(10)
+T_LENS, T_PERM, T_Q, T_KV, T_QIDX, T_W, T_KIDX, T_FILL, T_NEW_KV, T_NEW_KIDX, T_MQ_Q, T_MQ_QIDX, T_MQ_W = range(13)
 
 
 def _load():
@@ -235,3 +235,30 @@ def make_inputs(cfg, poison_tail=False, lens=None, shuffle=True):
         inp.k_idx, inp.k_idx_scale = _fill_pool(cfg, lens, bt, num_pages, dI, T_KIDX, cfg.idx_dtype,
                                                 poison_tail, unassigned)
     return inp
+
+
+def make_mq_queries(inp, n_q):
+    """Queries of n_q new tokens per request for a multi-query step: query
+    n_q - 1 (the newest position) is the workload's own q / q_idx / w, the
+    earlier ones are drawn from sub-stream b * n_q + i of their own tensor
+    ids.  Returns (q [B, n_q, H, D], q_idx [B, n_q, H_I, d_I], w [B, n_q, H_I])
+    in the workload's storage types."""
+    cfg = inp.cfg
+    B, H, D = cfg.batch, cfg.n_heads, cfg.dim
+    HI, dI = cfg.idx_heads, cfg.idx_dim
+    q = np.empty((B, n_q) + inp.q.shape[1:], inp.q.dtype)
+    qi = np.empty((B, n_q) + inp.q_idx.shape[1:], inp.q_idx.dtype)
+    w = np.empty((B, n_q, HI), np.float32)
+    for b in range(B):
+        for i in range(n_q):
+            if i == n_q - 1:
+                q[b, i], qi[b, i], w[b, i] = inp.q[b], inp.q_idx[b], inp.w[b]
+                continue
+            sub = b * n_q + i
+            q[b, i] = _dense_rows(cfg.q_dtype, normals32(cfg.seed, T_MQ_Q, sub, H * D).reshape(1, H, D))[0]
+            qi[b, i] = _dense_rows(cfg.q_dtype, normals32(cfg.seed, T_MQ_QIDX, sub, HI * dI).reshape(1, HI, dI))[0]
+            if cfg.w_dist == "normal":
+                w[b, i] = normals32(cfg.seed, T_MQ_W, sub, HI)
+            else:
+                w[b, i] = uniforms(cfg.seed, T_MQ_W, sub, HI).astype(np.float32)
+    return q, qi, w

@@ -32,7 +32,7 @@ def lib():
 def test_header_declares_the_four_operations():
     names = _declared()
     for n in ("dsa_indexer_scores", "topk_select", "mla_paged_decode", "lse_merge", "topk_workspace_bytes",
-              "kv_cache_append", "kv_page_check", "spmla_last_error"):
+              "kv_cache_append", "kv_page_check", "mq_expand_requests", "spmla_last_error"):
         assert n in names, names
 
 
@@ -175,3 +175,13 @@ def test_page_check_rejects(lib):
     assert f(FAKE, FAKE, 4, FAKE, 2, 100, FAKE, 10, 64, None, None) == EINVAL   # status is the output
     assert f(FAKE, MIS, 4, FAKE, 2, 100, FAKE, 10, 64, FAKE, None) == EINVAL
     assert f(None, None, 4, None, 0, 0, None, 10, 64, None, None) == OK
+
+
+def test_mq_expand_rejects(lib):
+    f = lib.mq_expand_requests
+    assert f(FAKE, 4, FAKE, 2, 0, FAKE, FAKE, None) == EUNSUPPORTED
+    assert f(FAKE, 4, FAKE, 2, 65, FAKE, FAKE, None) == EUNSUPPORTED
+    assert f(FAKE, 0, FAKE, 2, 2, FAKE, FAKE, None) == EINVAL
+    assert f(FAKE, 4, FAKE, -1, 2, FAKE, FAKE, None) == EINVAL
+    assert f(FAKE, 4, FAKE, 2, 2, None, FAKE, None) == EINVAL
+    assert f(None, 4, None, 0, 2, None, None, None) == OK

@@ -1,0 +1,91 @@
+"""GPU parity of the multi-query verification step (n_q new tokens per
+request, causal per query) against the oracle, stage by stage."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import spmla_gen as gen
+from spmla_gen.torch_io import device_batch, tensor
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+
+
+def _lib():
+    import sparse_paged_mla_amd as spm
+    spm.load_library()
+    return spm
+
+
+def _run_mq(cfg, lens, n_q, splits):
+    from sparse_paged_mla_amd.step import MultiQueryStep
+    inp = gen.make_inputs(cfg, lens=lens)
+    q, qi, w = gen.make_mq_queries(inp, n_q)
+    db = device_batch(inp)
+    st = MultiQueryStep(db, tensor(q, "cuda"), tensor(qi, "cuda"), torch.from_numpy(w).cuda(), num_splits=splits)
+    st.run()
+    torch.cuda.synchronize()
+    return inp, q, qi, w, st
+
+
+def _check(cfg, lens, n_q, splits, what):
+    print(f"[mq] {what} lens={lens} n_q={n_q} splits={splits}", flush=True)
+    inp, q, qi, w, st = _run_mq(cfg, lens, n_q, splits)
+    B = cfg.batch
+    lens = np.asarray(lens)
+    vis = np.where(lens[:, None] >= n_q, lens[:, None] - n_q + 1 + np.arange(n_q)[None, :], -1)
+    np.testing.assert_array_equal(st.lens.cpu().numpy().reshape(B, n_q), vis)
+    np.testing.assert_array_equal(st.bt.cpu().numpy(), np.repeat(inp.block_table, n_q, axis=0))
+    status = st.status.cpu().numpy()
+    assert not status[lens >= n_q].any()
+    assert (status[lens < n_q] & oracle.BAD_LEN).all()
+    ok = lens >= n_q
+    s_gpu = st.scores.cpu().numpy()
+    idx = st.idx.cpu().numpy()
+    o, lse = st.o.cpu().numpy(), st.lse.cpu().numpy()
+    for i in range(n_q):
+        sub = np.nonzero(ok)[0]
+        vi = vis[sub, i].astype(np.int32)
+        s_ref, mags, _ = oracle.indexer_scores(qi[sub, i], w[sub, i], inp.k_idx, inp.k_idx_scale,
+                                               inp.block_table[sub], vi, max_len=inp.max_len,
+                                               score_stride=inp.score_stride)
+        for r, b in enumerate(sub):
+            parity.check_scores(s_gpu[b, i, :vi[r]], s_ref[r, :vi[r]], mags[r, :vi[r]], f"{what} scores b={b} q={i}")
+        parity.check_topk_exact(idx[sub, i], s_gpu[sub, i], vi, cfg.topk, f"{what} q={i}")
+        o_ref, lse_ref, st_ref = oracle.mla_attention(q[sub, i], inp.kv, inp.kv_scale, inp.block_table[sub], vi,
+                                                      idx[sub, i], cfg.n_heads, cfg.d_latent, cfg.d_rope,
+                                                      cfg.softmax_scale, max_len=inp.max_len)
+        assert not st_ref.any()
+        parity.check_attention(o[sub, i], lse[sub, i], o_ref, lse_ref, f"{what} q={i}")
+    if (~ok).any():
+        assert (idx[~ok] == -1).all() and np.isnan(o[~ok]).all()
+    return inp, st
+
+
+@pytest.mark.parametrize("splits", [1, 2])
+def test_mq_tiny(splits):
+    """Three queries per request; a request of 2 tokens is shorter than n_q."""
+    _lib()
+    _check(gen.CONFIGS["c1"].with_(batch=3), [37, 5, 2], 3, splits, "c1 mq")
+
+
+@pytest.mark.parametrize("n_q", [2, 4])
+def test_mq_fp8(n_q):
+    """The c3f shapes (FP8 latent rows and indexer keys, top-k 2048) with a
+    request below k, one just above and a long one."""
+    _lib()
+    _check(gen.CONFIGS["c3f"].with_(batch=3), [2049, 70, 9000], n_q, 2, "c3f mq")
+
+
+def test_mq_one_query_equals_single_step():
+    """n_q = 1 is the ordinary step, bit for bit."""
+    _lib()
+    from sparse_paged_mla_amd.step import DecodeStep
+    cfg = gen.CONFIGS["c3f"].with_(batch=2)
+    inp, st = _check(cfg, [5000, 3000], 1, 2, "c3f n_q=1")
+    single = DecodeStep(device_batch(inp), num_splits=2)
+    single.run()
+    torch.cuda.synchronize()
+    assert torch.equal(single.idx, st.idx[:, 0]) and torch.equal(single.o, st.o[:, 0])
+    assert torch.equal(single.lse, st.lse[:, 0])
