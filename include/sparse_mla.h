@@ -96,7 +96,8 @@ enum { SPMLA_REQ_BAD_PAGE = 1, SPMLA_REQ_BAD_LEN = 2, SPMLA_REQ_BAD_INDEX = 4, S
  *               page_size] fp32 when k_dtype is FP8, else ignored (may be NULL).
  *  block_table  [batch, bt_stride] int32 physical page ids.
  *  context_lens [batch] int32; max_len (host value) bounds every context_lens[b].
- *  scores       [batch, score_stride] fp32, score_stride >= max_len.
+ *  scores       [batch, score_stride] fp32, score_stride >= max_len, rows
+ *               16-byte aligned (scores aligned, score_stride a multiple of 4).
  *  req_status   [batch] int32 or NULL.
  * Supported: n_heads <= 128; d in {16, 32, 64, 128, 256} (bf16: d >= 32);
  * page_size in {16, 32, 64, 128}.
@@ -109,6 +110,28 @@ int dsa_indexer_scores(const void* q_idx, int32_t q_dtype, const float* weights,
                        int32_t n_heads, int32_t d,
                        float* scores, int64_t score_stride,
                        int32_t* req_status, void* stream);
+
+/*
+ * dsa_indexer_scores_mq -- the indexer for a multi-query verification step
+ * (see mq_expand_requests): all n_q queries of a request are scored against
+ * each key as it is read, so the key pool is read once for all of them.
+ * Same arguments and arithmetic as dsa_indexer_scores, except:
+ *  q_idx   [batch, n_q, n_heads, d], weights [batch, n_q, n_heads];
+ *  scores  [batch * n_q, score_stride]: row b * n_q + i holds query i's
+ *          scores for every t < context_lens[b] (the tokens that query may
+ *          not see are computed too and must be ignored: the expanded
+ *          lengths of mq_expand_requests bound what the top-k reads);
+ *  req_status [batch * n_q] or NULL: a request's bits go to all its entries.
+ * Supported: n_q = 1, or n_q = 2 with bf16 queries and n_heads 16, 32 or 64.
+ */
+int dsa_indexer_scores_mq(const void* q_idx, int32_t q_dtype, const float* weights,
+                          const void* k_pool, const float* k_scale, int32_t k_dtype,
+                          int32_t num_pages, int32_t page_size,
+                          const int32_t* block_table, int32_t bt_stride,
+                          const int32_t* context_lens, int32_t batch, int64_t max_len,
+                          int32_t n_q, int32_t n_heads, int32_t d,
+                          float* scores, int64_t score_stride,
+                          int32_t* req_status, void* stream);
 
 /*
  * topk_workspace_bytes -- device workspace topk_select needs for these sizes

@@ -43,6 +43,9 @@ def load_library():
     lib.dsa_indexer_scores.restype = ctypes.c_int
     lib.dsa_indexer_scores.argtypes = [vp, i32, vp, vp, vp, i32, i32, i32, vp, i32, vp, i32, i64, i32, i32, vp, i64,
                                        vp, vp]
+    lib.dsa_indexer_scores_mq.restype = ctypes.c_int
+    lib.dsa_indexer_scores_mq.argtypes = [vp, i32, vp, vp, vp, i32, i32, i32, vp, i32, vp, i32, i64, i32, i32, i32,
+                                          vp, i64, vp, vp]
     lib.topk_workspace_bytes.restype = ctypes.c_size_t
     lib.topk_workspace_bytes.argtypes = [i32, i64, i32]
     lib.topk_select.restype = ctypes.c_int
@@ -104,6 +107,19 @@ def dsa_indexer_scores(q_idx, weights, k_pool, k_scale, block_table, context_len
                                   _dtype_code(k_pool), num_pages, page_size, _ptr(block_table),
                                   block_table.shape[1], _ptr(context_lens), B, int(max_len), H, d, _ptr(scores),
                                   scores.stride(0), _ptr(req_status), _stream(stream)))
+
+
+def dsa_indexer_scores_mq(q_idx, weights, k_pool, k_scale, block_table, context_lens, max_len, scores,
+                          req_status=None, stream=None):
+    """Multi-query indexer: q_idx [B, n_q, H, d], weights [B, n_q, H] -> scores
+    [B * n_q, stride] (row b * n_q + i: query i, every t < context_lens[b])."""
+    lib = load_library()
+    B, n_q, H, d = q_idx.shape
+    num_pages, page_size = k_pool.shape[0], k_pool.shape[1]
+    _check(lib.dsa_indexer_scores_mq(_ptr(q_idx), _dtype_code(q_idx), _ptr(weights), _ptr(k_pool), _ptr(k_scale),
+                                     _dtype_code(k_pool), num_pages, page_size, _ptr(block_table),
+                                     block_table.shape[1], _ptr(context_lens), B, int(max_len), n_q, H, d,
+                                     _ptr(scores), scores.stride(0), _ptr(req_status), _stream(stream)))
 
 
 def topk_workspace_bytes(batch, max_len, k):

@@ -72,9 +72,41 @@ int dsa_indexer_scores(const void* q_idx, int32_t q_dtype, const float* weights,
     if (!q_idx || !weights || !k_pool || !scores) return fail(SPMLA_EINVAL, "%s: null pointer", w);
     if (k_dtype == SPMLA_FP8_E4M3 && !k_scale) return fail(SPMLA_EINVAL, "%s: FP8 keys need k_scale", w);
     if (!aligned16(q_idx) || !aligned16(k_pool)) return fail(SPMLA_EINVAL, "%s: q_idx and k_pool must be 16-byte aligned", w);
+    if (score_stride % 4 != 0 || !aligned16(scores))
+      return fail(SPMLA_EINVAL, "%s: score rows must be 16-byte aligned (scores aligned, score_stride % 4 == 0)", w);
   }
   spmla::IndexerArgs a{q_idx, q_dtype, weights, k_pool, k_scale, k_dtype, num_pages, page_size, block_table,
                        bt_stride, context_lens, batch, max_len, n_heads, d, scores, score_stride, req_status};
+  return map_launch(spmla::launch_indexer(a, reinterpret_cast<hipStream_t>(stream)), w);
+}
+
+int dsa_indexer_scores_mq(const void* q_idx, int32_t q_dtype, const float* weights, const void* k_pool,
+                          const float* k_scale, int32_t k_dtype, int32_t num_pages, int32_t page_size,
+                          const int32_t* block_table, int32_t bt_stride, const int32_t* context_lens, int32_t batch,
+                          int64_t max_len, int32_t n_q, int32_t n_heads, int32_t d, float* scores,
+                          int64_t score_stride, int32_t* req_status, void* stream) {
+  const char* w = "dsa_indexer_scores_mq";
+  if (n_q < 1 || n_q > 2) return fail(SPMLA_EUNSUPPORTED, "%s: n_q must be 1 or 2", w);
+  if (n_q == 2 && ((n_heads != 16 && n_heads != 32 && n_heads != 64) || q_dtype != SPMLA_BF16))
+    return fail(SPMLA_EUNSUPPORTED, "%s: two queries need bf16 queries and n_heads of 16, 32 or 64", w);
+  if (int rc = check_paging(w, num_pages, page_size, block_table, bt_stride, context_lens, batch, max_len)) return rc;
+  if (q_dtype != SPMLA_F32 && q_dtype != SPMLA_BF16) return fail(SPMLA_EUNSUPPORTED, "%s: q_dtype must be F32 or BF16", w);
+  if (k_dtype < SPMLA_F32 || k_dtype > SPMLA_FP8_E4M3) return fail(SPMLA_EINVAL, "%s: bad k_dtype", w);
+  if (q_dtype == SPMLA_BF16 && k_dtype == SPMLA_F32)
+    return fail(SPMLA_EUNSUPPORTED, "%s: bf16 queries need bf16 or FP8 keys", w);
+  if (n_heads < 1 || n_heads > 128) return fail(SPMLA_EUNSUPPORTED, "%s: n_heads must be in [1, 128]", w);
+  if (!(d == 16 || d == 32 || d == 64 || d == 128 || d == 256) || (q_dtype == SPMLA_BF16 && d < 32))
+    return fail(SPMLA_EUNSUPPORTED, "%s: d must be 16/32/64/128/256 (>= 32 with bf16)", w);
+  if (score_stride < max_len) return fail(SPMLA_EINVAL, "%s: score_stride < max_len", w);
+  if (batch > 0) {
+    if (!q_idx || !weights || !k_pool || !scores) return fail(SPMLA_EINVAL, "%s: null pointer", w);
+    if (k_dtype == SPMLA_FP8_E4M3 && !k_scale) return fail(SPMLA_EINVAL, "%s: FP8 keys need k_scale", w);
+    if (!aligned16(q_idx) || !aligned16(k_pool)) return fail(SPMLA_EINVAL, "%s: q_idx and k_pool must be 16-byte aligned", w);
+    if (score_stride % 4 != 0 || !aligned16(scores))
+      return fail(SPMLA_EINVAL, "%s: score rows must be 16-byte aligned (scores aligned, score_stride % 4 == 0)", w);
+  }
+  spmla::IndexerArgs a{q_idx, q_dtype, weights, k_pool, k_scale, k_dtype, num_pages, page_size, block_table,
+                       bt_stride, context_lens, batch, max_len, n_heads, d, scores, score_stride, req_status, n_q};
   return map_launch(spmla::launch_indexer(a, reinterpret_cast<hipStream_t>(stream)), w);
 }
 

@@ -29,8 +29,13 @@ namespace spmla {
 
 constexpr int kIdxThreads = 256;
 constexpr int kIdxStepBytes = 8192;     // key bytes a wave fetches per step
-constexpr int kIdxWgPerCu = 2;          // resident workgroups per compute unit
-constexpr int kIdxLdsPerWg = 160 * 1024 / kIdxWgPerCu;
+// Resident workgroups per compute unit: two, except for kernels holding 8
+// M-tiles of queries (more than 256 registers per lane: one wave per SIMD).
+template <int MT>
+struct IdxWg {
+  static constexpr int per_cu = MT >= 8 ? 1 : 2;
+  static constexpr int lds = 160 * 1024 / per_cu;
+};
 constexpr int kIdxMaxHeldSteps = 40;    // steps of scores a wave holds in LDS before writing them
 constexpr int kNumCu = 256;
 
@@ -67,7 +72,11 @@ __device__ __forceinline__ int64_t wave_incl_scan_i64(int64_t v, int lane) {
 // MULTI: pages shorter than a step (a step's tokens span several pages).
 // A compile-time choice: with both paths in one kernel the compiler's
 // memory-wait accounting merges them and waits far more than either needs.
-template <class Op, int KDT, int KSTEPS, int MT, bool MULTI>
+// NQ: queries scored per key read (a multi-query step): the request's NQ
+// queries of n_heads heads each are NQ * n_heads consecutive rows, query i
+// takes M-tiles [i * MT / NQ, (i + 1) * MT / NQ) and writes score row
+// b * NQ + i (status entries likewise).
+template <class Op, int KDT, int KSTEPS, int MT, bool MULTI, int NQ>
 __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(
     const void* __restrict__ q_idx, const float* __restrict__ w, const uint8_t* __restrict__ k_pool,
     const float* __restrict__ k_scale, int32_t num_pages, int32_t page_shift,
@@ -98,10 +107,13 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(
   // nearly all of the grid's key reads instead of between them, where each
   // small write costs the reads far more than its bytes.
   constexpr int STAGE_BYTES = 4 * STEP_TOK * LROW;
-  constexpr int HELD_FIT = (kIdxLdsPerWg - STAGE_BYTES) / (4 * STEP_TOK * 4);
+  constexpr int HELD_FIT = (IdxWg<MT>::lds - STAGE_BYTES) / (NQ * 4 * STEP_TOK * 4);
   constexpr int HELD = HELD_FIT < 1 ? 1 : HELD_FIT > kIdxMaxHeldSteps ? kIdxMaxHeldSteps : HELD_FIT;
+  constexpr int MTQ = MT / NQ;  // M-tiles per query
+  static_assert(MT % NQ == 0, "queries split the M-tiles evenly");
   __shared__ __attribute__((aligned(16))) uint8_t stage[4][STEP_TOK * LROW];
-  __shared__ __attribute__((aligned(16))) float held[4][HELD * STEP_TOK];
+  __shared__ __attribute__((aligned(16))) float held[NQ][4][HELD * STEP_TOK];
+  const int32_t rows = NQ * n_heads;  // query rows of one request
 
   const int lane = threadIdx.x & 63;
   // Wave-uniform values are kept in scalar registers: the run bounds, the
@@ -121,7 +133,8 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(
   for (int i = lane; i < batch; i += 64) {
     const int32_t Lb = lens[i];
     mine += steps_of(Lb);
-    if (gw == 0 && !len_ok(Lb) && status) atomicOr(status + i, kBadLen);
+    if (gw == 0 && !len_ok(Lb) && status)
+      for (int qi = 0; qi < NQ; ++qi) atomicOr(status + (int64_t)i * NQ + qi, kBadLen);
   }
   int64_t total = wave_sum_i64(mine);
   total = ((int64_t)__builtin_amdgcn_readfirstlane((int32_t)(total >> 32)) << 32) |
@@ -158,10 +171,10 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       const int h = mt * 16 + r16;
-      if (h < n_heads) {
+      if (h < rows) {
         uint32_t raw[(GROUP_ELEMS * QE + 3) / 4];
         const uint8_t* qp =
-            reinterpret_cast<const uint8_t*>(q_idx) + (((int64_t)rb * n_heads + h) * D + g * GROUP_ELEMS) * QE;
+            reinterpret_cast<const uint8_t*>(q_idx) + (((int64_t)rb * rows + h) * D + g * GROUP_ELEMS) * QE;
         load_raw<GROUP_ELEMS * QE>(qp, raw);
         raw_to_frags<Op, kBf ? kBF16 : kF32, KSTEPS>(raw, qa[mt]);
       } else {
@@ -171,7 +184,7 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int hh = mt * 16 + g * 4 + i;
-        wr[mt][i] = hh < n_heads ? w[(int64_t)rb * n_heads + hh] : 0.f;
+        wr[mt][i] = hh < rows ? w[(int64_t)rb * rows + hh] : 0.f;
       }
     }
   };
@@ -196,7 +209,7 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(
     int n_held = 0;     // steps whose scores wait in held[wv]
     int64_t t_held = 0; // first token of those steps (they are consecutive)
     const int32_t* btb = bt + (int64_t)b * bt_stride;
-    float* sc_out = scores + (int64_t)b * score_stride;
+    float* sc_out = scores + (int64_t)b * NQ * score_stride;  // query qi's row: sc_out + qi * score_stride
     const int64_t last_page = ((int64_t)L - 1) >> page_shift;
 
     // Block-table entries of step si: lane j < 4 loads the entry of the
@@ -261,21 +274,26 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(
         else sc = 1.f;
       }
       bad_tok = bad;
-      if (__builtin_expect(__any(bad), 0) && bad && status) atomicOr(status + b, kBadPage);
+      if (__builtin_expect(__any(bad), 0) && bad && status)
+        for (int qi = 0; qi < NQ; ++qi) atomicOr(status + (int64_t)b * NQ + qi, kBadPage);
     };
     // The whole wave writes the held scores with 16-byte stores.
     auto write_held = [&]() __attribute__((always_inline)) {
       __builtin_amdgcn_wave_barrier();
       const int cnt = n_held * STEP_TOK;
-      for (int i = lane * 4; i < cnt; i += 256) {
-        const int64_t t = t_held + i;
-        const float4 v4 = *reinterpret_cast<const float4*>(&held[wv][i]);
-        if (t + 3 < L) {
-          *reinterpret_cast<float4*>(sc_out + t) = v4;
-        } else {
-          if (t < L) sc_out[t] = v4.x;
-          if (t + 1 < L) sc_out[t + 1] = v4.y;
-          if (t + 2 < L) sc_out[t + 2] = v4.z;
+#pragma unroll
+      for (int qi = 0; qi < NQ; ++qi) {
+        float* out = sc_out + qi * score_stride;
+        for (int i = lane * 4; i < cnt; i += 256) {
+          const int64_t t = t_held + i;
+          const float4 v4 = *reinterpret_cast<const float4*>(&held[qi][wv][i]);
+          if (t + 3 < L) {
+            *reinterpret_cast<float4*>(out + t) = v4;
+          } else {
+            if (t < L) out[t] = v4.x;
+            if (t + 1 < L) out[t + 1] = v4.y;
+            if (t + 2 < L) out[t + 2] = v4.z;
+          }
         }
       }
       __builtin_amdgcn_wave_barrier();
@@ -317,21 +335,24 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt) acc[mt] = Op::mma(qa[mt][st], kb[st], acc[mt]);
         }
-        float v = 0.f;
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            // ReLU as an integer max on the bit pattern (one instruction: a
-            // negative float has a negative integer pattern).
-            const float r = __int_as_float(max(__float_as_int(acc[mt][i]), 0));
-            v += wr[mt][i] * r;
-          }
-        }
-        v = wave_sum_xor16_32(v);
         const float tsc = __shfl(sc, tok);
         const bool bad = __shfl(bad_tok, tok) != 0;
-        if (g == 0) held[wv][n_held * STEP_TOK + tok] = bad ? __uint_as_float(0x7FC00000u) : v * tsc;
+#pragma unroll
+        for (int qi = 0; qi < NQ; ++qi) {
+          float v = 0.f;
+#pragma unroll
+          for (int mt = qi * MTQ; mt < (qi + 1) * MTQ; ++mt) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              // ReLU as an integer max on the bit pattern (one instruction: a
+              // negative float has a negative integer pattern).
+              const float r = __int_as_float(max(__float_as_int(acc[mt][i]), 0));
+              v += wr[mt][i] * r;
+            }
+          }
+          v = wave_sum_xor16_32(v);
+          if (g == 0) held[qi][wv][n_held * STEP_TOK + tok] = bad ? __uint_as_float(0x7FC00000u) : v * tsc;
+        }
       }
       if (n_held == 0) t_held = t0;
       if (++n_held == HELD) write_held();
@@ -374,7 +395,7 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(
   }
 }
 
-template <class Op, int KDT, int KSTEPS, int MT>
+template <class Op, int KDT, int KSTEPS, int MT, int NQ>
 static int launch_one(const IndexerArgs& a, hipStream_t stream) {
   int page_shift = 0;
   while ((1 << page_shift) < a.page_size) ++page_shift;
@@ -383,24 +404,37 @@ static int launch_one(const IndexerArgs& a, hipStream_t stream) {
   constexpr int ROW_BYTES = KSTEPS * 4 * Op::KPL * Storage<KDT>::bytes;
   constexpr int STEP_TOK = IdxStep<ROW_BYTES>::tok;
   const int64_t max_steps = (int64_t)a.batch * ((a.max_len + STEP_TOK - 1) / STEP_TOK);
-  const int64_t grid = std::min<int64_t>((int64_t)kNumCu * kIdxWgPerCu, (max_steps + 3) / 4);
+  const int64_t grid = std::min<int64_t>((int64_t)kNumCu * IdxWg<MT>::per_cu, (max_steps + 3) / 4);
   if (a.page_size < STEP_TOK)
-    hipLaunchKernelGGL((indexer_kernel<Op, KDT, KSTEPS, MT, true>), dim3((unsigned)grid), dim3(kIdxThreads), 0, stream,
-                       a.q_idx, a.w, reinterpret_cast<const uint8_t*>(a.k_pool), a.k_scale, a.num_pages, page_shift,
-                       a.bt, a.bt_stride, a.lens, a.batch, a.max_len, a.n_heads, a.scores, a.score_stride, a.status);
+    hipLaunchKernelGGL((indexer_kernel<Op, KDT, KSTEPS, MT, true, NQ>), dim3((unsigned)grid), dim3(kIdxThreads), 0,
+                       stream, a.q_idx, a.w, reinterpret_cast<const uint8_t*>(a.k_pool), a.k_scale, a.num_pages,
+                       page_shift, a.bt, a.bt_stride, a.lens, a.batch, a.max_len, a.n_heads, a.scores,
+                       a.score_stride, a.status);
   else
-    hipLaunchKernelGGL((indexer_kernel<Op, KDT, KSTEPS, MT, false>), dim3((unsigned)grid), dim3(kIdxThreads), 0, stream,
-                       a.q_idx, a.w, reinterpret_cast<const uint8_t*>(a.k_pool), a.k_scale, a.num_pages, page_shift,
-                       a.bt, a.bt_stride, a.lens, a.batch, a.max_len, a.n_heads, a.scores, a.score_stride, a.status);
+    hipLaunchKernelGGL((indexer_kernel<Op, KDT, KSTEPS, MT, false, NQ>), dim3((unsigned)grid), dim3(kIdxThreads), 0,
+                       stream, a.q_idx, a.w, reinterpret_cast<const uint8_t*>(a.k_pool), a.k_scale, a.num_pages,
+                       page_shift, a.bt, a.bt_stride, a.lens, a.batch, a.max_len, a.n_heads, a.scores,
+                       a.score_stride, a.status);
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 
 template <class Op, int KDT, int KSTEPS>
 static int dispatch_heads(const IndexerArgs& a, hipStream_t s) {
-  if (a.n_heads <= 16) return launch_one<Op, KDT, KSTEPS, 1>(a, s);
-  if (a.n_heads <= 32) return launch_one<Op, KDT, KSTEPS, 2>(a, s);
-  if (a.n_heads <= 64) return launch_one<Op, KDT, KSTEPS, 4>(a, s);
-  if (a.n_heads <= 128) return launch_one<Op, KDT, KSTEPS, 8>(a, s);
+  if (a.n_q == 2) {
+    // Two queries per key read (bf16 queries): the M-tiles split evenly
+    // between them.
+    if constexpr (std::is_same<Op, OpBF16>::value) {
+      if (a.n_heads == 16) return launch_one<Op, KDT, KSTEPS, 2, 2>(a, s);
+      if (a.n_heads == 32) return launch_one<Op, KDT, KSTEPS, 4, 2>(a, s);
+      if (a.n_heads == 64) return launch_one<Op, KDT, KSTEPS, 8, 2>(a, s);
+    }
+    return -2;
+  }
+  if (a.n_q != 1) return -2;
+  if (a.n_heads <= 16) return launch_one<Op, KDT, KSTEPS, 1, 1>(a, s);
+  if (a.n_heads <= 32) return launch_one<Op, KDT, KSTEPS, 2, 1>(a, s);
+  if (a.n_heads <= 64) return launch_one<Op, KDT, KSTEPS, 4, 1>(a, s);
+  if (a.n_heads <= 128) return launch_one<Op, KDT, KSTEPS, 8, 1>(a, s);
   return -2;
 }
 

@@ -14,6 +14,7 @@ struct IndexerArgs {
   int32_t num_pages, page_size; const int32_t* bt; int32_t bt_stride;
   const int32_t* lens; int32_t batch; int64_t max_len; int32_t n_heads, d;
   float* scores; int64_t score_stride; int32_t* status;
+  int32_t n_q = 1;  // queries per request scored per key read (1 or 2)
 };
 // Returns 0 on success, -2 unsupported combination, -3 launch failure.
 int launch_indexer(const IndexerArgs& a, hipStream_t stream);

@@ -7,8 +7,8 @@ from typing import Optional
 
 import torch
 
-from . import (dsa_indexer_scores, lse_merge, mla_paged_decode, mq_expand_requests, topk_select,
-               topk_workspace_bytes)
+from . import (dsa_indexer_scores, dsa_indexer_scores_mq, lse_merge, mla_paged_decode, mq_expand_requests,
+               topk_select, topk_workspace_bytes)
 
 
 @dataclass
@@ -94,7 +94,9 @@ class MultiQueryStep:
     q [B, n_q, H, D], q_idx [B, n_q, H_I, d_I], w [B, n_q, H_I] on the device;
     `batch` supplies the pools, block table and lengths of the B requests.
     One mq_expand_requests call builds the expanded batch (B * n_q requests);
-    the four calls of DecodeStep then run on it.  Outputs o [B, n_q, H, d_c],
+    the indexer scores both queries per key read when n_q is 2
+    (dsa_indexer_scores_mq on the real requests), else runs on the expanded
+    batch; top-k, decode and merge run on the expanded batch.  Outputs o [B, n_q, H, d_c],
     lse [B, n_q, H], idx [B, n_q, k] and status [B, n_q] are views of the
     expanded step's buffers."""
 
@@ -111,13 +113,29 @@ class MultiQueryStep:
                          topk=batch.topk, q_idx=q_idx.reshape(B * n_q, *q_idx.shape[2:]),
                          w=w.reshape(B * n_q, w.shape[2]), k_idx=batch.k_idx, k_idx_scale=batch.k_idx_scale)
         self.step = DecodeStep(ex, num_splits=num_splits)
+        self.real = batch
+        self.q_idx_mq, self.w_mq = q_idx, w
+        H_I = q_idx.shape[2]
+        self.fused_indexer = batch.topk > 0 and n_q == 2 and H_I in (16, 32, 64) and q_idx.dtype == torch.bfloat16
 
     def expand(self, stream=None):
         mq_expand_requests(self.real_bt, self.real_lens, self.n_q, self.bt, self.lens, stream)
 
+    def indexer(self, stream=None):
+        if self.fused_indexer:
+            r = self.real
+            dsa_indexer_scores_mq(self.q_idx_mq, self.w_mq, r.k_idx, r.k_idx_scale, r.block_table, r.lens, r.max_len,
+                                  self.step.scores, self.step.status, stream)
+        else:
+            self.step.indexer(stream)
+
     def run(self, stream=None):
         self.expand(stream)
-        self.step.run(stream)
+        if self.step.sparse:
+            self.indexer(stream)
+            self.step.select(stream)
+        self.step.attend(stream)
+        self.step.merge(stream)
 
     def _view(self, t):
         return t.reshape(self.B, self.n_q, *t.shape[1:])

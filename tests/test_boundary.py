@@ -86,6 +86,8 @@ def test_indexer_rejects(lib):
     assert _idx(lib, num_pages=0) == EINVAL
     assert _idx(lib, max_len=-5) == EINVAL
     assert _idx(lib, batch=0, q_idx=None, scores=None) == OK  # empty batch: nothing to do
+    assert _idx(lib, score_stride=258) == EINVAL              # rows not 16-byte aligned
+    assert _idx(lib, scores=MIS) == EINVAL
 
 
 def test_topk_rejects(lib):
@@ -185,3 +187,18 @@ def test_mq_expand_rejects(lib):
     assert f(FAKE, 4, FAKE, -1, 2, FAKE, FAKE, None) == EINVAL
     assert f(FAKE, 4, FAKE, 2, 2, None, FAKE, None) == EINVAL
     assert f(None, 4, None, 0, 2, None, None, None) == OK
+
+
+def test_indexer_mq_rejects(lib):
+    f = lib.dsa_indexer_scores_mq
+
+    def call(n_q=2, n_heads=64, q_dtype=BF16, d=128, score_stride=256, scores=FAKE):
+        return f(FAKE, q_dtype, FAKE, FAKE, FAKE, FP8, 10, 64, FAKE, 4, FAKE, 2, 256, n_q, n_heads, d, scores,
+                 score_stride, None, None)
+    assert call(n_q=3) == EUNSUPPORTED
+    assert call(n_q=0) == EUNSUPPORTED
+    assert call(n_heads=48) == EUNSUPPORTED
+    assert call(q_dtype=F32) == EUNSUPPORTED
+    assert call(d=96) == EUNSUPPORTED
+    assert call(score_stride=258) == EINVAL
+    assert call(scores=MIS) == EINVAL
