@@ -280,3 +280,40 @@ def multi_query_step(q, q_idx, w, kv, kv_scale, k_pool, k_scale, block_table, le
             scores[ok, i], idx[ok, i], o[ok, i], lse[ok, i] = s, sel, oi, li
             status[ok] |= st | st2
     return dict(scores=scores, idx=idx, o=o, lse=lse, status=status, vis=vis)
+
+
+def prefill_chunk_attention(q, kv, kv_scale, block_table, lens, n_heads, d_latent, d_rope, sm_scale, blocks=None):
+    """Dense causal attention of n_q new tokens per request (positions
+    L-n_q .. L-1, already cached): query i attends to every t < L - n_q + 1 + i.
+    With `blocks`, the context of each query is cut into that many equal
+    blocks, each attended alone, and the block partials are merged with the
+    online-softmax state, as a ring pass computes it block by block [KW
+    5.2.2]; without, in one piece.  Returns o [B, n_q, H, d_latent], lse
+    [B, n_q, H], status [B]."""
+    B, Q = q.shape[0], q.shape[1]
+    lens = np.asarray(lens, np.int64)
+    bad = lens < Q
+    o = np.full((B, Q, n_heads, d_latent), np.nan)
+    lse = np.full((B, Q, n_heads), np.nan)
+    status = np.where(bad, BAD_LEN, 0).astype(np.int32)
+    ok = np.nonzero(~bad)[0]
+    for i in range(Q):
+        for b in ok:
+            vis = int(lens[b] - Q + 1 + i)
+            if blocks is None:
+                oi, li, st = mla_attention(q[b:b + 1, i], kv, kv_scale, block_table[b:b + 1], [vis], None, n_heads,
+                                           d_latent, d_rope, sm_scale, max_len=int(lens.max()))
+            else:
+                edges = [vis * j // blocks for j in range(blocks + 1)]
+                parts = [mla_attention(q[b:b + 1, i], kv, kv_scale, block_table[b:b + 1], [vis],
+                                       np.arange(edges[j], edges[j + 1], dtype=np.int32)[None, :]
+                                       if edges[j + 1] > edges[j] else np.full((1, 1), -1, np.int32),
+                                       n_heads, d_latent, d_rope, sm_scale, max_len=int(lens.max()))
+                         for j in range(blocks)]
+                oi, li = lse_merge(np.stack([p[0] for p in parts], 1), np.stack([p[1] for p in parts], 1))
+                st = np.zeros(1, np.int32)
+                for p in parts:
+                    st |= p[2]
+            o[b, i], lse[b, i] = oi[0], li[0]
+            status[b] |= st[0]
+    return o, lse, status

@@ -657,3 +657,34 @@ def test_multi_query_step_matches_causal_brute_force():
             np.testing.assert_allclose(r["lse"][b, i], logsumexp(z, axis=1), rtol=1e-12)
             assert list(r["idx"][b, i, :vis.sum()]) == list(np.nonzero(vis)[0])
     assert np.isnan(r["o"][2]).all()
+
+
+# ------------------------------------------------------------ prefill chunk
+
+def test_prefill_chunk_matches_causal_brute_force_and_blocks_merge():
+    """Dense causal attention of a chunk of new tokens: each query equals a
+    numpy softmax over the tokens a tril mask leaves it; computing the context
+    in 3 blocks and merging the block partials gives the same result."""
+    Q = 4
+    cfg = gen.CONFIGS["c1"].with_(batch=2)
+    inp = gen.make_inputs(cfg, lens=[37, 100], shuffle=True)
+    rng = np.random.default_rng(9)
+    q = rng.standard_normal((2, Q, cfg.n_heads, cfg.dim)).astype(np.float32)
+    o1, l1, st = oracle.prefill_chunk_attention(q, inp.kv, inp.kv_scale, inp.block_table, inp.lens, cfg.n_heads,
+                                                cfg.d_latent, cfg.d_rope, cfg.softmax_scale)
+    o3, l3, _ = oracle.prefill_chunk_attention(q, inp.kv, inp.kv_scale, inp.block_table, inp.lens, cfg.n_heads,
+                                               cfg.d_latent, cfg.d_rope, cfg.softmax_scale, blocks=3)
+    assert not st.any()
+    np.testing.assert_allclose(o3, o1, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(l3, l1, rtol=1e-13)
+    P = cfg.page_size
+    for b in range(2):
+        L = int(inp.lens[b])
+        rows = np.array([int(inp.block_table[b, t // P]) * P + t % P for t in range(L)])
+        c = inp.kv.reshape(-1, cfg.dim)[rows].astype(np.float64)
+        mask = np.tril(np.ones((L, L), bool))[L - Q:]
+        for i in range(Q):
+            z = cfg.softmax_scale * np.einsum("hd,td->ht", q[b, i].astype(np.float64), c)[:, mask[i]]
+            np.testing.assert_allclose(o1[b, i], softmax(z, axis=1) @ c[mask[i], :cfg.d_latent], rtol=1e-10,
+                                       atol=1e-12)
+            np.testing.assert_allclose(l1[b, i], logsumexp(z, axis=1), rtol=1e-12)
