@@ -214,8 +214,47 @@ def time_multi_query(cfg, db, inp, n_q, splits, steps, flush, run_flush):
                     n_q * alg["decode"]["flops"] / (BF16_PEAK_TFLOPS * 1e12)))
     return {"n_q": n_q, "us_per_step": round(us, 2), "verified_tokens_per_s": round(cfg.batch * n_q / (us * 1e-6), 1),
             "t_star_us": round(t_star * 1e6, 2), "frac": round(t_star / (us * 1e-6), 4), "num_splits": splits,
-            "note": "expanded batch of batch*n_q requests through the single-query kernels; "
-                    "indexer keys are read once per query"}
+            "note": "indexer scores both queries per key read; top-k, decode and merge run on the expanded "
+                    "batch of batch*n_q requests"}
+
+
+def time_prefill_chunk(cfg, db, inp, n_req, n_q, blocks, steps, flush, run_flush):
+    """Attention of a prefill chunk: n_q new tokens at the end of each of the
+    first n_req requests, each attending densely and causally to its context,
+    computed in `blocks` KV blocks merged by the online-softmax algebra."""
+    import dataclasses
+    import numpy as np
+    import torch
+    import spmla_gen as gen
+    from spmla_gen.torch_io import tensor
+    from sparse_paged_mla_amd.step import PrefillChunkStep
+    q = gen.make_chunk_queries(inp, n_req, n_q)
+    sub = dataclasses.replace(db, q=db.q[:n_req], block_table=db.block_table[:n_req], lens=db.lens[:n_req])
+    st = PrefillChunkStep(sub, tensor(q, "cuda"), num_blocks=blocks)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for _ in range(2):
+        st.run()
+    for e0, e1 in evs:
+        if flush:
+            run_flush()
+        e0.record()
+        st.run()
+        e1.record()
+    torch.cuda.synchronize()
+    assert not st.status.cpu().numpy().any(), "prefill chunk flagged a request on clean inputs"
+    us = statistics.fmean(e0.elapsed_time(e1) for e0, e1 in evs) * 1e3
+    lens = inp.lens[:n_req].astype(np.int64)
+    vis = (lens[:, None] - n_q + 1 + np.arange(n_q)[None, :]).sum()
+    flops = 2.0 * int(vis) * cfg.n_heads * (cfg.dim + cfg.d_latent)
+    e_c = {0: 4, 1: 2, 2: 1}[cfg.cache_dtype] * cfg.dim + (4 if cfg.cache_dtype == 2 else 0)
+    nbytes = int(lens.sum()) * e_c + n_req * n_q * cfg.n_heads * (cfg.dim * 2 + 4 * (cfg.d_latent + 1))
+    t_star = max(flops / (BF16_PEAK_TFLOPS * 1e12), nbytes / (HBM_PEAK_GBS * 1e9))
+    return {"requests": n_req, "n_q": n_q, "kv_blocks": blocks, "context_tokens": int(lens.sum()),
+            "us_per_step": round(us, 1), "prefill_tokens_per_s": round(n_req * n_q / (us * 1e-6), 1),
+            "tflops": round(flops / (us * 1e-6) / 1e12, 1), "t_star_us": round(t_star * 1e6, 1),
+            "frac": round(t_star / (us * 1e-6), 4), "bound": "mfma (bf16 peak)",
+            "note": "each chunk query runs as its own request through the decode kernel: its KV is re-read per query "
+                    "(from L2/MALL)"}
 
 
 def cpu_baseline(inp, n_req):
@@ -329,6 +368,8 @@ def main():
 
     mq = None if cfg.dense else time_multi_query(cfg, db, inp, 2, splits, args.steps, flush,
                                                  run_flush=lambda: flush_sink.copy_(flush_buf.amax()))
+    pre = time_prefill_chunk(cfg, db, inp, 2, 64, 2, min(args.steps, 10), flush,
+                             run_flush=lambda: flush_sink.copy_(flush_buf.amax()))
     chk = time_page_check(cfg, db, inp, args.steps, flush, run_flush=lambda: flush_sink.copy_(flush_buf.amax()))
     chk["overhead_frac_of_step"] = round(chk["us"] / (mean_ms * 1e3), 4)
 
@@ -392,6 +433,7 @@ def main():
         "cache_append": app,
         "page_check": chk,
         "multi_query": mq,
+        "prefill_chunk": pre,
         "step_ms_median_min_max": [round(statistics.median(step_ms), 4), round(min(step_ms), 4),
                                    round(max(step_ms), 4)],
         "warm_ms_per_step": None if warm_ms != warm_ms else round(warm_ms, 4),

@@ -291,7 +291,13 @@ int kv_page_check(const int32_t* block_table, const uint64_t* bt_tags, int32_t b
  *  block_table [batch, bt_stride], context_lens [batch]: the real requests.
  *  out_block_table [batch * n_q, bt_stride], out_lens [batch * n_q]: written.
  *  A request with L_b < n_q gets length -1 for all its queries, which the
- *  later calls flag as SPMLA_REQ_BAD_LEN.  Supported: 1 <= n_q <= 64.
+ *  later calls flag as SPMLA_REQ_BAD_LEN.  Supported: 1 <= n_q <= 65536.
+ *
+ * The same expansion serves a prefill chunk of n_q new tokens attending
+ * densely and causally: mla_paged_decode with indices = NULL over the
+ * expanded batch computes, for every query, one partial per KV split (a
+ * block of the context), and lse_merge combines the blocks with the online
+ * softmax state, the single-GPU form of blockwise ring attention [KW 5.2.2].
  */
 int mq_expand_requests(const int32_t* block_table, int32_t bt_stride, const int32_t* context_lens,
                        int32_t batch, int32_t n_q, int32_t* out_block_table, int32_t* out_lens,

@@ -217,7 +217,7 @@ int mq_expand_requests(const int32_t* block_table, int32_t bt_stride, const int3
                        int32_t n_q, int32_t* out_block_table, int32_t* out_lens, void* stream) {
   const char* w = "mq_expand_requests";
   if (batch < 0) return fail(SPMLA_EINVAL, "%s: batch < 0", w);
-  if (n_q < 1 || n_q > 64) return fail(SPMLA_EUNSUPPORTED, "%s: n_q must be in [1, 64]", w);
+  if (n_q < 1 || n_q > 65536) return fail(SPMLA_EUNSUPPORTED, "%s: n_q must be in [1, 65536]", w);
   if (bt_stride < 1) return fail(SPMLA_EINVAL, "%s: bt_stride must be >= 1", w);
   if (batch == 0) return ok();
   if (!block_table || !context_lens || !out_block_table || !out_lens) return fail(SPMLA_EINVAL, "%s: null pointer", w);

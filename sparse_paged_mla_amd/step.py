@@ -159,3 +159,48 @@ class MultiQueryStep:
     @property
     def status(self):
         return self._view(self.step.status)
+
+
+class PrefillChunkStep:
+    """Attention of a prefill chunk: n_q new tokens per request (already in
+    the cache, at positions L - n_q .. L - 1), each attending densely and
+    causally to the tokens up to itself, computed block by block: the context
+    of every query is cut into num_blocks KV splits, each giving a partial
+    (o, lse), and the partials are merged with the online-softmax algebra
+    (the blockwise ring-attention structure on one GPU).
+
+    q [B, n_q, H, D] on the device; `batch` supplies the latent pool, block
+    table and lengths.  Outputs o [B, n_q, H, d_c], lse [B, n_q, H] and
+    status [B, n_q]."""
+
+    def __init__(self, batch: DeviceBatch, q, num_blocks: int = 1):
+        B, n_q = q.shape[0], q.shape[1]
+        dev = q.device
+        self.B, self.n_q = B, n_q
+        self.real_bt, self.real_lens = batch.block_table, batch.lens
+        self.bt = torch.empty(B * n_q, batch.block_table.shape[1], dtype=torch.int32, device=dev)
+        self.lens = torch.empty(B * n_q, dtype=torch.int32, device=dev)
+        ex = DeviceBatch(q=q.reshape(B * n_q, *q.shape[2:]), kv=batch.kv, kv_scale=batch.kv_scale,
+                         block_table=self.bt, lens=self.lens, max_len=batch.max_len,
+                         score_stride=batch.score_stride, d_latent=batch.d_latent, sm_scale=batch.sm_scale, topk=0)
+        self.step = DecodeStep(ex, num_splits=num_blocks)
+
+    def run(self, stream=None):
+        mq_expand_requests(self.real_bt, self.real_lens, self.n_q, self.bt, self.lens, stream)
+        self.step.attend(stream)
+        self.step.merge(stream)
+
+    def _view(self, t):
+        return t.reshape(self.B, self.n_q, *t.shape[1:])
+
+    @property
+    def o(self):
+        return self._view(self.step.o)
+
+    @property
+    def lse(self):
+        return self._view(self.step.lse)
+
+    @property
+    def status(self):
+        return self._view(self.step.status)

@@ -24,7 +24,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libspmla_gen.so")
 _lib = None
 
-T_LENS, T_PERM, T_Q, T_KV, T_QIDX, T_W, T_KIDX, T_FILL, T_NEW_KV, T_NEW_KIDX, T_MQ_Q, T_MQ_QIDX, T_MQ_W = range(13)
+(T_LENS, T_PERM, T_Q, T_KV, T_QIDX, T_W, T_KIDX, T_FILL, T_NEW_KV, T_NEW_KIDX, T_MQ_Q, T_MQ_QIDX, T_MQ_W,
+ T_CHUNK_Q) = range(14)
 
 
 def _load():
@@ -262,3 +263,16 @@ def make_mq_queries(inp, n_q):
             else:
                 w[b, i] = uniforms(cfg.seed, T_MQ_W, sub, HI).astype(np.float32)
     return q, qi, w
+
+
+def make_chunk_queries(inp, n_req, n_q):
+    """Queries of a prefill chunk: n_q new tokens for each of the first n_req
+    requests, query (b, i) from sub-stream b * n_q + i of its own tensor id,
+    in the workload's query type.  Returns q [n_req, n_q, H, D]."""
+    cfg = inp.cfg
+    H, D = cfg.n_heads, cfg.dim
+    q = np.empty((n_req, n_q, H, D), np.float32)
+    for b in range(n_req):
+        for i in range(n_q):
+            q[b, i] = normals32(cfg.seed, T_CHUNK_Q, b * n_q + i, H * D).reshape(H, D)
+    return _dense_rows(cfg.q_dtype, q.reshape(n_req * n_q, H, D)).reshape(n_req, n_q, H, D)

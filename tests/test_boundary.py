@@ -182,7 +182,7 @@ def test_page_check_rejects(lib):
 def test_mq_expand_rejects(lib):
     f = lib.mq_expand_requests
     assert f(FAKE, 4, FAKE, 2, 0, FAKE, FAKE, None) == EUNSUPPORTED
-    assert f(FAKE, 4, FAKE, 2, 65, FAKE, FAKE, None) == EUNSUPPORTED
+    assert f(FAKE, 4, FAKE, 2, 65537, FAKE, FAKE, None) == EUNSUPPORTED
     assert f(FAKE, 0, FAKE, 2, 2, FAKE, FAKE, None) == EINVAL
     assert f(FAKE, 4, FAKE, -1, 2, FAKE, FAKE, None) == EINVAL
     assert f(FAKE, 4, FAKE, 2, 2, None, FAKE, None) == EINVAL
