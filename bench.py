@@ -362,16 +362,21 @@ def main():
         torch.cuda.synchronize()
         warm_ms = e0.elapsed_time(e1) / args.steps
 
-    app = None if cfg.dense or cfg.cache_dtype != gen.FP8 else time_cache_append(cfg, db, inp, args.steps, flush,
+    # The legs of the next rows (skipped under --profile-only, so that a
+    # profile's per-kernel figures cover the step's launches only).
+    legs = not args.profile_only
+    app = None if not legs or cfg.dense or cfg.cache_dtype != gen.FP8 else time_cache_append(cfg, db, inp, args.steps, flush,
                                                                                  run_flush=lambda: flush_sink.copy_(
                                                                                      flush_buf.amax()))
 
-    mq = None if cfg.dense else time_multi_query(cfg, db, inp, 2, splits, args.steps, flush,
+    mq = None if not legs or cfg.dense else time_multi_query(cfg, db, inp, 2, splits, args.steps, flush,
                                                  run_flush=lambda: flush_sink.copy_(flush_buf.amax()))
-    pre = time_prefill_chunk(cfg, db, inp, 2, 64, 2, min(args.steps, 10), flush,
-                             run_flush=lambda: flush_sink.copy_(flush_buf.amax()))
-    chk = time_page_check(cfg, db, inp, args.steps, flush, run_flush=lambda: flush_sink.copy_(flush_buf.amax()))
-    chk["overhead_frac_of_step"] = round(chk["us"] / (mean_ms * 1e3), 4)
+    pre = None if not legs else time_prefill_chunk(cfg, db, inp, 2, 64, 2, min(args.steps, 10), flush,
+                                                   run_flush=lambda: flush_sink.copy_(flush_buf.amax()))
+    chk = None
+    if legs:
+        chk = time_page_check(cfg, db, inp, args.steps, flush, run_flush=lambda: flush_sink.copy_(flush_buf.amax()))
+        chk["overhead_frac_of_step"] = round(chk["us"] / (mean_ms * 1e3), 4)
 
     alg = algorithmic(cfg, inp.lens)
     t_star = roofline_time_s(alg)
