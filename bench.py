@@ -371,7 +371,9 @@ def main():
 
     mq = None if not legs or cfg.dense else time_multi_query(cfg, db, inp, 2, splits, args.steps, flush,
                                                  run_flush=lambda: flush_sink.copy_(flush_buf.amax()))
-    pre = None if not legs else time_prefill_chunk(cfg, db, inp, 2, 64, 2, min(args.steps, 10), flush,
+    n_pre = min(2, cfg.batch)
+    pre = None if not legs else time_prefill_chunk(cfg, db, inp, n_pre, min(64, int(inp.lens[:n_pre].min())), 2,
+                                                   min(args.steps, 10), flush,
                                                    run_flush=lambda: flush_sink.copy_(flush_buf.amax()))
     chk = None
     if legs:

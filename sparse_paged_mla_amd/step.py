@@ -32,7 +32,10 @@ class DeviceBatch:
 
 # KV splits per workload as timed: enough (request, split, head group)
 # workgroups to fill 256 compute units without splitting short token lists.
-DEFAULT_SPLITS = {"c1": 1, "c2": 4, "c3": 2, "c3f": 2, "c4": 2, "c5": 8}
+# Measured on the box: c4 (128 requests) runs 201 µs per step with one split
+# (256 workgroups, one round) against 224 with two; c2 is best at 4 and c5 at
+# 8 of {2, 4, 8} and {4, 8, 16}.
+DEFAULT_SPLITS = {"c1": 1, "c2": 4, "c3": 2, "c3f": 2, "c4": 1, "c5": 8}
 
 
 class DecodeStep:
