@@ -68,3 +68,73 @@ def test_full_size_step(name):
     parity.check_attention(step.o.cpu().numpy()[sel], step.lse.cpu().numpy()[sel], o_ref, lse_ref,
                            f"{name} attention requests {reqs}")
     _say(f"{name}: attention of requests {reqs} matches")
+
+
+def test_full_size_multi_query_c3f():
+    """The two-query verification step at the c3f size, as the benchmark
+    times it (two queries per key read in the indexer): sampled scores of
+    both queries, every query's top-k exactly against the GPU's scores with
+    its causal length, attention of sampled requests."""
+    import sparse_paged_mla_amd as spm
+    from spmla_gen.torch_io import tensor
+    from sparse_paged_mla_amd.step import DEFAULT_SPLITS, MultiQueryStep
+    spm.load_library()
+    n_q = 2
+    inp = gen.make_inputs("c3f")
+    cfg = inp.cfg
+    q, qi, w = gen.make_mq_queries(inp, n_q)
+    st = MultiQueryStep(device_batch(inp), tensor(q, "cuda"), tensor(qi, "cuda"), torch.from_numpy(w).cuda(),
+                        num_splits=DEFAULT_SPLITS["c3f"])
+    assert st.fused_indexer
+    _say("c3f n_q=2: running the multi-query step")
+    st.run()
+    torch.cuda.synchronize()
+    assert not st.status.cpu().numpy().any()
+    s_gpu, idx = st.scores.cpu().numpy(), st.idx.cpu().numpy()
+    vis = inp.lens[:, None] - n_q + 1 + np.arange(n_q)[None, :]
+    rng = np.random.default_rng(77)
+    for i in range(n_q):
+        sb = rng.integers(0, cfg.batch, 256).astype(np.int32)
+        tt = (rng.random(256) * vis[sb, i]).astype(np.int64)
+        tt[::5] = vis[sb[::5], i] - 1
+        s_ref, mags = oracle.indexer_scores_at(qi[:, i], w[:, i], inp.k_idx, inp.k_idx_scale, inp.block_table, sb, tt)
+        parity.check_scores(s_gpu[sb, i, tt], s_ref, mags, f"mq scores q={i}")
+        parity.check_topk_exact(idx[:, i], s_gpu[:, i], vis[:, i], cfg.topk, f"mq top-k q={i}")
+        sel = np.array(sorted({int(np.argmax(inp.lens)), int(rng.integers(0, cfg.batch))}), np.int32)
+        o_ref, lse_ref, _ = oracle.mla_attention(q[sel, i], inp.kv, inp.kv_scale, inp.block_table[sel],
+                                                 vis[sel, i].astype(np.int32), idx[sel, i], cfg.n_heads,
+                                                 cfg.d_latent, cfg.d_rope, cfg.softmax_scale, max_len=inp.max_len)
+        parity.check_attention(st.o.cpu().numpy()[sel, i], st.lse.cpu().numpy()[sel, i], o_ref, lse_ref,
+                               f"mq attention q={i} requests {list(sel)}")
+    _say("c3f n_q=2: sampled scores, all top-k and sampled attention match")
+
+
+def test_full_size_prefill_chunk_sampled():
+    """The prefill chunk as the benchmark times it (64 new tokens on each of
+    the first two c3f requests, 2 KV blocks): the newest query of the first
+    request and the oldest of the second against the oracle's dense causal
+    attention (each one is tens of GFLOP in the fp64 oracle)."""
+    import sparse_paged_mla_amd as spm
+    from spmla_gen.torch_io import tensor
+    from sparse_paged_mla_amd.step import PrefillChunkStep
+    spm.load_library()
+    inp = gen.make_inputs("c3f")
+    cfg = inp.cfg
+    n_req, n_q = 2, 64
+    q = gen.make_chunk_queries(inp, n_req, n_q)
+    db = device_batch(inp)
+    import dataclasses
+    sub = dataclasses.replace(db, q=db.q[:n_req], block_table=db.block_table[:n_req], lens=db.lens[:n_req])
+    st = PrefillChunkStep(sub, tensor(q, "cuda"), num_blocks=2)
+    _say("c3f prefill chunk: running")
+    st.run()
+    torch.cuda.synchronize()
+    assert not st.status.cpu().numpy().any()
+    o, lse = st.o.cpu().numpy(), st.lse.cpu().numpy()
+    for b, i in ((0, n_q - 1), (1, 0)):
+        vis = int(inp.lens[b]) - n_q + 1 + i
+        o_ref, lse_ref, _ = oracle.mla_attention(q[b:b + 1, i], inp.kv, inp.kv_scale, inp.block_table[b:b + 1],
+                                                 np.array([vis], np.int32), None, cfg.n_heads, cfg.d_latent,
+                                                 cfg.d_rope, cfg.softmax_scale, max_len=inp.max_len)
+        parity.check_attention(o[b:b + 1, i], lse[b:b + 1, i], o_ref, lse_ref, f"prefill b={b} q={i}")
+    _say("c3f prefill chunk: sampled queries match")
