@@ -250,6 +250,21 @@ int kv_cache_append(const void* rows, int32_t row_dtype, int32_t batch, int32_t 
                     const int32_t* positions, int32_t* req_status, void* stream);
 
 /*
+ * kv_cache_append_pair -- kv_cache_append for the latent pool and the
+ * indexer-key pool of the same new tokens in one launch: the two pools share
+ * page ids, so one block table, one positions array and one num_pages serve
+ * both.  kv_rows [batch, kv_dim] go to kv_pool (scales kv_scale), idx_rows
+ * [batch, idx_dim] to idx_pool (scales idx_scale); both use row_dtype and
+ * pool_dtype.  Same arithmetic, status bits and limits as kv_cache_append.
+ */
+int kv_cache_append_pair(const void* kv_rows, int32_t kv_dim, void* kv_pool, float* kv_scale,
+                         const void* idx_rows, int32_t idx_dim, void* idx_pool, float* idx_scale,
+                         int32_t row_dtype, int32_t pool_dtype, int32_t batch,
+                         int32_t num_pages, int32_t page_size,
+                         const int32_t* block_table, int32_t bt_stride,
+                         const int32_t* positions, int32_t* req_status, void* stream);
+
+/*
  * kv_page_check -- the KV-page integrity check, a separate batched pass run
  * before a step reads the cache.  Every physical page carries a tag that is
  * new on each reallocation; before decode reads the cache the mapping of

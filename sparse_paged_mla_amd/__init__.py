@@ -55,6 +55,8 @@ def load_library():
                                      f32, i32, vp, vp, vp, vp]
     lib.kv_cache_append.restype = ctypes.c_int
     lib.kv_cache_append.argtypes = [vp, i32, i32, i32, vp, vp, i32, i32, i32, vp, i32, vp, vp, vp]
+    lib.kv_cache_append_pair.restype = ctypes.c_int
+    lib.kv_cache_append_pair.argtypes = [vp, i32, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, vp, i32, vp, vp, vp]
     lib.kv_page_check.restype = ctypes.c_int
     lib.kv_page_check.argtypes = [vp, vp, i32, vp, i32, i64, vp, i32, i32, vp, vp]
     lib.mq_expand_requests.restype = ctypes.c_int
@@ -195,3 +197,21 @@ def mq_expand_requests(block_table, context_lens, n_q, out_block_table, out_lens
         raise ValueError("output shapes must be [B * n_q, bt_stride] and [B * n_q]")
     _check(lib.mq_expand_requests(_ptr(block_table), block_table.shape[1], _ptr(context_lens), B, int(n_q),
                                   _ptr(out_block_table), _ptr(out_lens), _stream(stream)))
+
+
+def kv_cache_append_pair(kv_rows, kv_pool, kv_scale, idx_rows, idx_pool, idx_scale, block_table, positions,
+                         req_status=None, stream=None):
+    """kv_cache_append of the latent rows and the indexer keys of the same new
+    tokens in one launch (the pools share page ids)."""
+    lib = load_library()
+    B = kv_rows.shape[0]
+    if idx_rows.shape[0] != B or _dtype_code(kv_rows) != _dtype_code(idx_rows):
+        raise ValueError("both row arrays need the same batch and dtype")
+    if _dtype_code(kv_pool) != _dtype_code(idx_pool) or kv_pool.shape[:2] != idx_pool.shape[:2]:
+        raise ValueError("both pools need the same dtype, page count and page size")
+    if kv_pool.shape[2] != kv_rows.shape[1] or idx_pool.shape[2] != idx_rows.shape[1]:
+        raise ValueError("pool row lengths differ from the rows'")
+    _check(lib.kv_cache_append_pair(_ptr(kv_rows), kv_rows.shape[1], _ptr(kv_pool), _ptr(kv_scale), _ptr(idx_rows),
+                                    idx_rows.shape[1], _ptr(idx_pool), _ptr(idx_scale), _dtype_code(kv_rows),
+                                    _dtype_code(kv_pool), B, kv_pool.shape[0], kv_pool.shape[1], _ptr(block_table),
+                                    block_table.shape[1], _ptr(positions), _ptr(req_status), _stream(stream)))

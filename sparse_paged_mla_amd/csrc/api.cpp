@@ -199,6 +199,33 @@ int kv_cache_append(const void* rows, int32_t row_dtype, int32_t batch, int32_t 
   return map_launch(spmla::launch_cache_append(a, reinterpret_cast<hipStream_t>(stream)), w);
 }
 
+int kv_cache_append_pair(const void* kv_rows, int32_t kv_dim, void* kv_pool, float* kv_scale, const void* idx_rows,
+                         int32_t idx_dim, void* idx_pool, float* idx_scale, int32_t row_dtype, int32_t pool_dtype,
+                         int32_t batch, int32_t num_pages, int32_t page_size, const int32_t* block_table,
+                         int32_t bt_stride, const int32_t* positions, int32_t* req_status, void* stream) {
+  const char* w = "kv_cache_append_pair";
+  if (batch < 0) return fail(SPMLA_EINVAL, "%s: batch < 0", w);
+  if (row_dtype != SPMLA_F32 && row_dtype != SPMLA_BF16)
+    return fail(SPMLA_EUNSUPPORTED, "%s: row_dtype must be F32 or BF16", w);
+  if (pool_dtype < SPMLA_F32 || pool_dtype > SPMLA_FP8_E4M3) return fail(SPMLA_EINVAL, "%s: bad pool_dtype", w);
+  for (int32_t d : {kv_dim, idx_dim})
+    if (d < 8 || d > 4096 || d % 8 != 0)
+      return fail(SPMLA_EUNSUPPORTED, "%s: row dims must be multiples of 8 in [8, 4096]", w);
+  if (num_pages < 1) return fail(SPMLA_EINVAL, "%s: num_pages must be >= 1", w);
+  if (!is_pow2_page(page_size)) return fail(SPMLA_EUNSUPPORTED, "%s: page_size must be 16, 32, 64 or 128", w);
+  if (bt_stride < 1) return fail(SPMLA_EINVAL, "%s: bt_stride must be >= 1", w);
+  if (batch == 0) return ok();
+  if (!kv_rows || !kv_pool || !idx_rows || !idx_pool || !block_table || !positions)
+    return fail(SPMLA_EINVAL, "%s: null pointer", w);
+  if (pool_dtype == SPMLA_FP8_E4M3 && (!kv_scale || !idx_scale))
+    return fail(SPMLA_EINVAL, "%s: FP8 pools need their scales", w);
+  if (!aligned16(kv_rows) || !aligned16(kv_pool) || !aligned16(idx_rows) || !aligned16(idx_pool))
+    return fail(SPMLA_EINVAL, "%s: rows and pools must be 16-byte aligned", w);
+  spmla::AppendArgs a{kv_rows, row_dtype, batch, kv_dim, kv_pool, kv_scale, pool_dtype, num_pages, page_size,
+                      block_table, bt_stride, positions, req_status, idx_rows, idx_dim, idx_pool, idx_scale};
+  return map_launch(spmla::launch_cache_append(a, reinterpret_cast<hipStream_t>(stream)), w);
+}
+
 int kv_page_check(const int32_t* block_table, const uint64_t* bt_tags, int32_t bt_stride, const int32_t* context_lens,
                   int32_t batch, int64_t max_len, const uint64_t* page_tags, int32_t num_pages, int32_t page_size,
                   int32_t* req_status, void* stream) {

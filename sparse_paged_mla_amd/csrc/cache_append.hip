@@ -1,5 +1,6 @@
 // kv_cache_append kernel: writes each request's new token row into its page
-// slot, quantising to OCP e4m3 with a per-token scale when the pool is FP8.
+// slot (of one pool, or of two pools that share page ids in one launch),
+// quantising to OCP e4m3 with a per-token scale when the pool is FP8.
 //
 // One wave per request.  The row is read in 8-element chunks (lane c takes
 // chunks c, c + 64, ...) and kept in registers; the wave's absolute maximum
@@ -16,14 +17,31 @@ namespace spmla {
 constexpr int kAppThreads = 256;
 constexpr int kAppMaxChunksPerLane = 8;  // row_dim <= 8 * 8 * 64 = 4096
 
+// One pool: its new rows, row length, storage and scales.
+struct AppendPool {
+  const void* rows;
+  int32_t dim;
+  void* pool;
+  float* scale;
+};
+
+// Waves [0, batch) append to pool p0 and, when npools is 2, waves
+// [batch, 2 * batch) to pool p1 (the latent rows and the indexer keys of the
+// same tokens, which share page ids and so the block table).
 template <int RDT, int PDT>
 __global__ __launch_bounds__(kAppThreads) void cache_append_kernel(
-    const void* __restrict__ rows, int32_t batch, int32_t dim, void* __restrict__ pool, float* __restrict__ pool_scale,
-    int32_t num_pages, int32_t page_shift, const int32_t* __restrict__ bt, int32_t bt_stride,
-    const int32_t* __restrict__ positions, int32_t* __restrict__ status) {
+    AppendPool p0, AppendPool p1, int32_t npools, int32_t batch, int32_t num_pages, int32_t page_shift,
+    const int32_t* __restrict__ bt, int32_t bt_stride, const int32_t* __restrict__ positions,
+    int32_t* __restrict__ status) {
   const int lane = threadIdx.x & 63;
-  const int b = blockIdx.x * (kAppThreads / 64) + (threadIdx.x >> 6);
-  if (b >= batch) return;
+  const int v = blockIdx.x * (kAppThreads / 64) + (threadIdx.x >> 6);
+  if (v >= npools * batch) return;
+  const bool second = v >= batch;
+  const int b = second ? v - batch : v;
+  const void* __restrict__ rows = second ? p1.rows : p0.rows;
+  const int32_t dim = second ? p1.dim : p0.dim;
+  void* __restrict__ pool = second ? p1.pool : p0.pool;
+  float* __restrict__ pool_scale = second ? p1.scale : p0.scale;
   const int32_t t = positions[b];
   if (t < 0) return;
   const int page_size = 1 << page_shift;
@@ -121,13 +139,17 @@ __global__ __launch_bounds__(kAppThreads) void cache_append_kernel(
 
 int launch_cache_append(const AppendArgs& a, hipStream_t s) {
   if (a.batch == 0) return 0;
-  if (a.dim % 8 != 0 || a.dim < 8 || a.dim > 8 * 64 * kAppMaxChunksPerLane) return -2;
+  const int npools = a.rows2 ? 2 : 1;
+  for (int d : {a.dim, npools == 2 ? a.dim2 : a.dim})
+    if (d % 8 != 0 || d < 8 || d > 8 * 64 * kAppMaxChunksPerLane) return -2;
   int page_shift = 0;
   while ((1 << page_shift) < a.page_size) ++page_shift;
-  const unsigned grid = (unsigned)((a.batch + kAppThreads / 64 - 1) / (kAppThreads / 64));
-#define SPMLA_APPEND(R, P)                                                                                      \
-  hipLaunchKernelGGL((cache_append_kernel<R, P>), dim3(grid), dim3(kAppThreads), 0, s, a.rows, a.batch, a.dim, \
-                     a.pool, a.pool_scale, a.num_pages, page_shift, a.bt, a.bt_stride, a.positions, a.status)
+  const AppendPool p0{a.rows, a.dim, a.pool, a.pool_scale};
+  const AppendPool p1{a.rows2, a.dim2, a.pool2, a.pool_scale2};
+  const unsigned grid = (unsigned)(((int64_t)npools * a.batch + kAppThreads / 64 - 1) / (kAppThreads / 64));
+#define SPMLA_APPEND(R, P)                                                                                        \
+  hipLaunchKernelGGL((cache_append_kernel<R, P>), dim3(grid), dim3(kAppThreads), 0, s, p0, p1, npools, a.batch, \
+                     a.num_pages, page_shift, a.bt, a.bt_stride, a.positions, a.status)
   if (a.row_dtype == kBF16) {
     if (a.pool_dtype == kFP8) SPMLA_APPEND(kBF16, kFP8);
     else if (a.pool_dtype == kBF16) SPMLA_APPEND(kBF16, kBF16);

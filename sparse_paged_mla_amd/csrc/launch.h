@@ -43,6 +43,8 @@ int launch_merge(const MergeArgs& a, hipStream_t stream);
 struct AppendArgs {
   const void* rows; int row_dtype; int32_t batch, dim; void* pool; float* pool_scale; int pool_dtype;
   int32_t num_pages, page_size; const int32_t* bt; int32_t bt_stride; const int32_t* positions; int32_t* status;
+  // A second pool with the same page ids, row and pool types (rows2 == nullptr: none).
+  const void* rows2 = nullptr; int32_t dim2 = 0; void* pool2 = nullptr; float* pool_scale2 = nullptr;
 };
 int launch_cache_append(const AppendArgs& a, hipStream_t stream);
 

@@ -32,7 +32,7 @@ def lib():
 def test_header_declares_the_four_operations():
     names = _declared()
     for n in ("dsa_indexer_scores", "topk_select", "mla_paged_decode", "lse_merge", "topk_workspace_bytes",
-              "kv_cache_append", "kv_page_check", "mq_expand_requests", "spmla_last_error"):
+              "kv_cache_append", "kv_cache_append_pair", "kv_page_check", "mq_expand_requests", "spmla_last_error"):
         assert n in names, names
 
 
@@ -202,3 +202,18 @@ def test_indexer_mq_rejects(lib):
     assert call(d=96) == EUNSUPPORTED
     assert call(score_stride=258) == EINVAL
     assert call(scores=MIS) == EINVAL
+
+
+def test_append_pair_rejects(lib):
+    f = lib.kv_cache_append_pair
+
+    def call(kv_dim=576, idx_dim=128, kv_scale=FAKE, idx_rows=FAKE, idx_pool=FAKE, row_dtype=1, pool_dtype=2, P=64):
+        return f(FAKE, kv_dim, FAKE, kv_scale, idx_rows, idx_dim, idx_pool, FAKE, row_dtype, pool_dtype, 4, 10, P,
+                 FAKE, 4, FAKE, None, None)
+    assert call(idx_dim=12) == EUNSUPPORTED
+    assert call(kv_dim=4104) == EUNSUPPORTED
+    assert call(row_dtype=2) == EUNSUPPORTED
+    assert call(P=48) == EUNSUPPORTED
+    assert call(kv_scale=None) == EINVAL
+    assert call(idx_rows=None) == EINVAL
+    assert call(idx_pool=MIS) == EINVAL

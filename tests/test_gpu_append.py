@@ -138,3 +138,47 @@ def test_append_flags_bad_requests_and_writes_nothing_for_them():
     print("[append] bad requests", flush=True)
     st = _run(spm, rows, "fp32", "fp8", bt, num_pages, P, pos, seed=9)
     assert list(st) == [0, oracle.BAD_PAGE, oracle.BAD_PAGE, oracle.BAD_LEN, 0, 0]
+
+
+def test_append_pair_one_launch_bit_exact():
+    """Latent rows and indexer keys of the same tokens in one launch (the c3f
+    shapes), each pool bit for bit against the oracle; a bad page and a
+    skipped request."""
+    spm = _lib()
+    B, P = 64, 64
+    rng, bt, num_pages = _layout(B, 3, P, seed=31)
+    bt = bt.copy()
+    bt[5, 1] = num_pages + 2
+    rows_kv, rows_ix = _rows(rng, B, 576), _rows(rng, B, 128)
+    pos = rng.integers(0, 3 * P, B).astype(np.int32)
+    pos[5] = 70                               # page 1 of request 5: not a pool page
+    pos[6] = -1
+    bits_kv, bits_ix = gen_bits(rows_kv), gen_bits(rows_ix)
+    pools, scales, refs = [], [], []
+    for dim, bits in ((576, bits_kv), (128, bits_ix)):
+        pool = rng.integers(0, 256, (num_pages, P, dim), dtype=np.uint8)
+        sc = rng.standard_normal((num_pages, P)).astype(np.float32)
+        rp, rs = pool.copy(), sc.copy()
+        st_ref = oracle.cache_append(bits, rp, rs, bt, pos)
+        pools.append(torch.from_numpy(pool).cuda())
+        scales.append(torch.from_numpy(sc).cuda())
+        refs.append((rp, rs, st_ref))
+    status = torch.zeros(B, dtype=torch.int32, device="cuda")
+    print("[append] pair", flush=True)
+    spm.kv_cache_append_pair(bf16_tensor(bits_kv), pools[0], scales[0], bf16_tensor(bits_ix), pools[1], scales[1],
+                             torch.from_numpy(bt).cuda(), torch.from_numpy(pos).cuda(), status)
+    torch.cuda.synchronize()
+    for k in range(2):
+        rp, rs, st_ref = refs[k]
+        assert np.array_equal(pools[k].cpu().numpy(), rp)
+        assert np.array_equal(scales[k].cpu().numpy().view(np.uint32), rs.view(np.uint32))
+        assert np.array_equal(status.cpu().numpy(), st_ref)
+    assert status.cpu().numpy()[5] == oracle.BAD_PAGE
+
+
+def gen_bits(rows):
+    return (rows.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def bf16_tensor(bits):
+    return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
