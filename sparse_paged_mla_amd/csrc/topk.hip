@@ -6,23 +6,23 @@
 // entries under (key desc, index asc), a total order, so the result is unique
 // whatever order atomics land in.
 //
-// Launches per call (both on the caller's stream):
-//  1. collect: (request, 4096-key chunk) workgroups.  Each first derives the
-//     request's threshold key tau from a sample of its keys (all of them
-//     when the request has at most 4096, else 16 evenly spread runs of 256):
+// Launches per call (all on the caller's stream):
+//  1. tau: one workgroup per request derives its threshold key tau from a
+//     sample of its keys (all of them when the request has at most 4096,
+//     else 16 evenly spread runs of 256):
 //     one histogram of the sample over the 11 bits below the bits its keys
 //     share, and tau the lower edge of the bin holding the sample key of
 //     rank r: k when the sample is the whole request, else e + 4 sqrt(e) + 4
 //     where e = k * 4096 / L is the expected count of sampled keys at or
 //     above the request's k-th largest key, so somewhat more than k keys of
 //     the request reach tau (fewer only if the sample count falls four
-//     deviations short).  Every workgroup of a
-//     request reads the same sample and derives the same tau.  It then
-//     copies its chunk's keys >= tau, with their indices and in token order,
-//     to the chunk's own slice of the candidate buffer, and writes their
-//     count and smallest and largest key (no atomics, so nothing needs
-//     clearing between calls).
-//  2. finish: one workgroup per request gathers the chunks' candidates into
+//     deviations short).
+//  2. collect: (request, 4096-key chunk) workgroups.  Each copies its
+//     chunk's keys >= tau, with their indices and in token order, to the
+//     chunk's own slice of the candidate buffer, and writes their count and
+//     smallest and largest key (no atomics, so nothing needs clearing
+//     between calls).
+//  3. finish: one workgroup per request gathers the chunks' candidates into
 //     LDS (still in token order) and selects the k_eff best exactly: 11-bit
 //     rounds over the key from the highest bit in which the candidates
 //     differ; once the bin holding the k-th best key has at most 64 keys,
@@ -54,6 +54,7 @@ constexpr int kCandLds = kFinLdsWords / 2;       // candidates that fit in LDS (
 static_assert(kSample == kTkChunk, "a collect workgroup holds one sample key per chunk key");
 
 struct TopkWs {
+  uint32_t* tau;    // [B] threshold key of each request longer than k
   uint4* meta;      // [B, chunks] (candidate count, smallest key, largest key, 0) of each chunk
   uint2* cand;      // [B, chunks, kTkChunk] (key, index), chunk c's in its own slice, ascending index
   int32_t chunks;
@@ -66,7 +67,7 @@ size_t topk_workspace_size(int32_t batch, int64_t max_len, int32_t k) {
   (void)k;
   if (batch <= 0 || max_len < 0) return 0;
   const size_t bc = (size_t)batch * (size_t)n_chunks(max_len);
-  return align_up(bc * 16, 256) + bc * kTkChunk * 8;
+  return align_up((size_t)batch * 4, 256) + align_up(bc * 16, 256) + bc * kTkChunk * 8;
 }
 
 static TopkWs carve(void* ws, int32_t batch, int64_t max_len) {
@@ -74,6 +75,8 @@ static TopkWs carve(void* ws, int32_t batch, int64_t max_len) {
   uint8_t* p = reinterpret_cast<uint8_t*>(ws);
   w.chunks = n_chunks(max_len);
   const size_t bc = (size_t)batch * (size_t)w.chunks;
+  w.tau = reinterpret_cast<uint32_t*>(p);
+  p += align_up((size_t)batch * 4, 256);
   w.meta = reinterpret_cast<uint4*>(p);
   w.cand = reinterpret_cast<uint2*>(p + align_up(bc * 16, 256));
   return w;
@@ -256,6 +259,21 @@ __device__ uint32_t request_tau(const float* __restrict__ s, int32_t L, int32_t 
   return pre | (res[0] << lo);
 }
 
+// One workgroup per request longer than k: its tau into the workspace.
+__global__ __launch_bounds__(kTkThreads) void topk_tau_kernel(const float* __restrict__ scores, int64_t stride,
+                                                              const int32_t* __restrict__ lens, int64_t max_len,
+                                                              int32_t k, TopkWs ws) {
+  __shared__ uint32_t h[kBins];
+  __shared__ uint32_t tmp[kTkThreads / 64];
+  __shared__ uint32_t res[2];
+  __shared__ uint32_t s_mm[2];
+  const int b = blockIdx.x;
+  const int32_t L = lens[b];
+  if (!len_ok(L, max_len) || L <= k) return;
+  const uint32_t tau = request_tau(scores + (int64_t)b * stride, L, k, h, tmp, res, s_mm);
+  if (threadIdx.x == 0) ws.tau[b] = tau;
+}
+
 // (request, chunk) workgroups: every key >= tau goes to the chunk's slice of
 // the candidate buffer in ascending token order, and the chunk's count and
 // smallest and largest candidate keys to its metadata slot.  Key j of
@@ -265,8 +283,6 @@ __device__ uint32_t request_tau(const float* __restrict__ s, int32_t L, int32_t 
 __global__ __launch_bounds__(kTkThreads) void topk_collect_kernel(const float* __restrict__ scores, int64_t stride,
                                                                   const int32_t* __restrict__ lens, int64_t max_len,
                                                                   int32_t k, TopkWs ws) {
-  __shared__ uint32_t h[kBins];
-  __shared__ uint32_t tmp[kTkThreads / 64];
   __shared__ uint32_t res[2];
   __shared__ uint32_t s_mm[2];
   __shared__ uint32_t rw[kTkPer * (kTkThreads / 64)];  // (row, wave) counts, then their exclusive scan
@@ -282,7 +298,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_collect_kernel(const float* _
   uint32_t key[kTkPer];
   bool in[kTkPer];
   load_chunk(s, t0, t1, key, in);
-  const uint32_t tau = request_tau(s, L, k, h, tmp, res, s_mm);
+  const uint32_t tau = ws.tau[b];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const uint64_t below = (1ull << lane) - 1ull;
   uint32_t rank[kTkPer];
@@ -487,6 +503,8 @@ int launch_topk(const TopkArgs& a, hipStream_t s) {
   TopkWs ws = carve(a.workspace, a.batch, a.max_len);
   const int64_t grid = (int64_t)a.batch * ws.chunks;
   if (grid > 0x7FFFFFFF) return -2;
+  hipLaunchKernelGGL(topk_tau_kernel, dim3((unsigned)a.batch), dim3(kTkThreads), 0, s, a.scores, a.score_stride,
+                     a.lens, a.max_len, a.k, ws);
   hipLaunchKernelGGL(topk_collect_kernel, dim3((unsigned)grid), dim3(kTkThreads), 0, s, a.scores, a.score_stride,
                      a.lens, a.max_len, a.k, ws);
   hipLaunchKernelGGL(topk_finish_kernel, dim3((unsigned)a.batch), dim3(kFinThreads), 0, s, a.scores, a.score_stride,
