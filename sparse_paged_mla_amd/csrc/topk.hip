@@ -204,18 +204,20 @@ __device__ void find_bin_asc(const uint32_t* h, uint32_t need, uint32_t* tmp, ui
 }
 
 // Threshold key tau of a request whose length exceeds k (see the top of the
-// file); called by all kTkThreads threads, barriers inside.
+// file); called by all NT threads, barriers inside.
+template <int NT>
 __device__ uint32_t request_tau(const float* __restrict__ s, int32_t L, int32_t k, uint32_t* h, uint32_t* tmp,
                                 uint32_t* res, uint32_t* s_mm) {
+  constexpr int PER = kSample / NT;
   const int tid = threadIdx.x;
   const bool whole = L <= kSample;
-  uint32_t key[kTkPer];
-  bool in[kTkPer];
+  uint32_t key[PER];
+  bool in[PER];
   {
-    float v[kTkPer];
+    float v[PER];
 #pragma unroll
-    for (int j = 0; j < kTkPer; ++j) {
-      const int e = j * kTkThreads + tid;
+    for (int j = 0; j < PER; ++j) {
+      const int e = j * NT + tid;
       int64_t t;
       if (whole) {
         t = e;
@@ -227,16 +229,16 @@ __device__ uint32_t request_tau(const float* __restrict__ s, int32_t L, int32_t 
       v[j] = s[in[j] ? t : 0];
     }
 #pragma unroll
-    for (int j = 0; j < kTkPer; ++j) key[j] = order_key(v[j]);
+    for (int j = 0; j < PER; ++j) key[j] = order_key(v[j]);
   }
   uint32_t lo_k = 0xFFFFFFFFu, hi_k = 0u;
 #pragma unroll
-  for (int j = 0; j < kTkPer; ++j)
+  for (int j = 0; j < PER; ++j)
     if (in[j]) { lo_k = min(lo_k, key[j]); hi_k = max(hi_k, key[j]); }
   lo_k = wave_min_u32(lo_k);
   hi_k = wave_max_u32(hi_k);
   if (tid == 0) { s_mm[0] = 0xFFFFFFFFu; s_mm[1] = 0u; }
-  for (int i = tid; i < kBins; i += kTkThreads) h[i] = 0u;
+  for (int i = tid; i < kBins; i += NT) h[i] = 0u;
   __syncthreads();
   if ((tid & 63) == 0) { atomicMin(&s_mm[0], lo_k); atomicMax(&s_mm[1], hi_k); }
   __syncthreads();
@@ -252,10 +254,10 @@ __device__ uint32_t request_tau(const float* __restrict__ s, int32_t L, int32_t 
     need = (uint32_t)min((int64_t)kSample, (int64_t)ceilf(r));
   }
 #pragma unroll
-  for (int j = 0; j < kTkPer; ++j)
+  for (int j = 0; j < PER; ++j)
     if (in[j]) atomicAdd(&h[(key[j] >> lo) & 2047u], 1u);
   __syncthreads();
-  find_bin_desc<kBins, kTkThreads>(h, need, tmp, res);
+  find_bin_desc<kBins, NT>(h, need, tmp, res);
   return pre | (res[0] << lo);
 }
 
@@ -270,7 +272,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_tau_kernel(const float* __res
   const int b = blockIdx.x;
   const int32_t L = lens[b];
   if (!len_ok(L, max_len) || L <= k) return;
-  const uint32_t tau = request_tau(scores + (int64_t)b * stride, L, k, h, tmp, res, s_mm);
+  const uint32_t tau = request_tau<kTkThreads>(scores + (int64_t)b * stride, L, k, h, tmp, res, s_mm);
   if (threadIdx.x == 0) ws.tau[b] = tau;
 }
 
@@ -333,68 +335,16 @@ __global__ __launch_bounds__(kTkThreads) void topk_collect_kernel(const float* _
   }
 }
 
-__global__ __launch_bounds__(kFinThreads) void topk_finish_kernel(const float* __restrict__ scores, int64_t stride,
-                                                                  const int32_t* __restrict__ lens, int64_t max_len,
-                                                                  int32_t k, TopkWs ws, int32_t* __restrict__ out_idx,
-                                                                  int32_t* __restrict__ status) {
-  __shared__ uint32_t big[kFinLdsWords];   // gathered candidates (uint2)
-  __shared__ uint32_t h[kBins];
-  __shared__ uint32_t tmp[kFinThreads / 64];
-  __shared__ uint32_t res[2];
-  __shared__ uint32_t coff[kFinThreads];  // chunk offsets in the gathered candidate list
-  __shared__ uint32_t ccnt[kFinThreads];  // chunk candidate counts
-  __shared__ uint32_t s_mm[2];
-  __shared__ uint2 bin_list[64];           // members of the boundary bin, when few
-  __shared__ uint32_t bin_cnt;
-  const int b = blockIdx.x;
+// Exact selection of the k best of n_c candidates held in ascending token
+// order -- the (key, index) list `lc` in LDS or, when `whole`, every key of
+// the score row `srow` -- with their indices written to `out` in that order.
+// [cmin, cmax] bounds the listed keys.  Called by all kFinThreads threads
+// after a barrier that follows *bin_cnt = 0; barriers inside.
+__device__ void select_k_best(const uint2* lc, const float* __restrict__ srow, bool whole, uint32_t n_c,
+                              uint32_t cmin, uint32_t cmax, int32_t k, int32_t* __restrict__ out, uint32_t* h,
+                              uint32_t* tmp, uint32_t* res, uint2* bin_list, uint32_t* bin_cnt) {
   const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int32_t L = lens[b];
-  int32_t* out = out_idx + (int64_t)b * k;
-  if (!len_ok(L, max_len)) {
-    if (tid == 0 && status) atomicOr(status + b, kBadLen);
-    for (int j = tid; j < k; j += kFinThreads) out[j] = -1;
-    return;
-  }
-  if (L <= k) {
-    for (int j = tid; j < k; j += kFinThreads) out[j] = j < L ? j : -1;
-    return;
-  }
-  // Candidates: the chunks' keys >= tau gathered into LDS in token order, or,
-  // should fewer than k or more than LDS holds have reached tau (or the
-  // request have more chunks than this workgroup has threads), every key of
-  // the request read from the scores.
-  const int n_act = (int)((L + kTkChunk - 1) / kTkChunk);
-  const int64_t slot0 = (int64_t)b * ws.chunks;
-  const uint4 meta = (tid < n_act) ? ws.meta[slot0 + tid] : make_uint4(0u, 0xFFFFFFFFu, 0u, 0u);
-  if (tid == 0) { s_mm[0] = 0xFFFFFFFFu; s_mm[1] = 0u; }
-  const uint32_t c_incl = block_incl_scan<kFinThreads>(meta.x, tmp);
-  if (tid < n_act) { coff[tid] = c_incl - meta.x; ccnt[tid] = meta.x; }
-  if (tid == kFinThreads - 1) res[0] = c_incl;
-  {
-    const uint32_t wmin = wave_min_u32(meta.y), wmax = wave_max_u32(meta.z);
-    if (lane == 0) { atomicMin(&s_mm[0], wmin); atomicMax(&s_mm[1], wmax); }
-  }
-  __syncthreads();
-  const uint32_t n_cand = res[0];
-  const bool whole = n_cand < (uint32_t)k || n_cand > (uint32_t)kCandLds || n_act > kFinThreads;
-  const uint32_t n_c = whole ? (uint32_t)L : n_cand;
-  const float* srow = scores + (int64_t)b * stride;
-  uint2* lc = reinterpret_cast<uint2*>(big);
-  if (!whole) {
-    // Wave w copies chunks w, w + 16, ...: each chunk's slice goes to its
-    // offset in the gathered list.
-    for (int c = tid >> 6; c < n_act; c += kFinThreads / 64) {
-      const uint32_t n = ccnt[c], off = coff[c];
-      const uint2* src = ws.cand + (slot0 + c) * kTkChunk;
-      for (uint32_t i = lane; i < n; i += 64) lc[off + i] = src[i];
-    }
-  }
-  const uint32_t cmin = s_mm[0], cmax = s_mm[1];
-  if (tid == 0) bin_cnt = 0u;
-  __syncthreads();
-  const uint2* cb = lc;
-  auto cand = [&](uint32_t j) -> uint2 { return whole ? make_uint2(order_key(srow[j]), j) : cb[j]; };
+  auto cand = [&](uint32_t j) -> uint2 { return whole ? make_uint2(order_key(srow[j]), j) : lc[j]; };
   uint32_t need = (uint32_t)k;
   // Key rounds, 11 bits at a time from the highest bit in which the
   // candidates can differ (they lie in [smallest, largest collected key];
@@ -429,7 +379,7 @@ __global__ __launch_bounds__(kFinThreads) void topk_finish_kernel(const float* _
       // selection.
       for (uint32_t j = tid; j < n_c; j += kFinThreads) {
         const uint2 e = cand(j);
-        if ((e.x & kmask) == kpre) bin_list[atomicAdd(&bin_cnt, 1u)] = e;
+        if ((e.x & kmask) == kpre) bin_list[atomicAdd(bin_cnt, 1u)] = e;
       }
       __syncthreads();
       if (tid < (int)in_bin) {
@@ -497,9 +447,203 @@ __global__ __launch_bounds__(kFinThreads) void topk_finish_kernel(const float* _
   }
 }
 
+__global__ __launch_bounds__(kFinThreads) void topk_finish_kernel(const float* __restrict__ scores, int64_t stride,
+                                                                  const int32_t* __restrict__ lens, int64_t max_len,
+                                                                  int32_t k, TopkWs ws, int32_t* __restrict__ out_idx,
+                                                                  int32_t* __restrict__ status) {
+  __shared__ uint32_t big[kFinLdsWords];   // gathered candidates (uint2)
+  __shared__ uint32_t h[kBins];
+  __shared__ uint32_t tmp[kFinThreads / 64];
+  __shared__ uint32_t res[2];
+  __shared__ uint32_t coff[kFinThreads];  // chunk offsets in the gathered candidate list
+  __shared__ uint32_t ccnt[kFinThreads];  // chunk candidate counts
+  __shared__ uint32_t s_mm[2];
+  __shared__ uint2 bin_list[64];           // members of the boundary bin, when few
+  __shared__ uint32_t bin_cnt;
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int32_t L = lens[b];
+  int32_t* out = out_idx + (int64_t)b * k;
+  if (!len_ok(L, max_len)) {
+    if (tid == 0 && status) atomicOr(status + b, kBadLen);
+    for (int j = tid; j < k; j += kFinThreads) out[j] = -1;
+    return;
+  }
+  if (L <= k) {
+    for (int j = tid; j < k; j += kFinThreads) out[j] = j < L ? j : -1;
+    return;
+  }
+  // Candidates: the chunks' keys >= tau gathered into LDS in token order, or,
+  // should fewer than k or more than LDS holds have reached tau (or the
+  // request have more chunks than this workgroup has threads), every key of
+  // the request read from the scores.
+  const int n_act = (int)((L + kTkChunk - 1) / kTkChunk);
+  const int64_t slot0 = (int64_t)b * ws.chunks;
+  const uint4 meta = (tid < n_act) ? ws.meta[slot0 + tid] : make_uint4(0u, 0xFFFFFFFFu, 0u, 0u);
+  if (tid == 0) { s_mm[0] = 0xFFFFFFFFu; s_mm[1] = 0u; }
+  const uint32_t c_incl = block_incl_scan<kFinThreads>(meta.x, tmp);
+  if (tid < n_act) { coff[tid] = c_incl - meta.x; ccnt[tid] = meta.x; }
+  if (tid == kFinThreads - 1) res[0] = c_incl;
+  {
+    const uint32_t wmin = wave_min_u32(meta.y), wmax = wave_max_u32(meta.z);
+    if (lane == 0) { atomicMin(&s_mm[0], wmin); atomicMax(&s_mm[1], wmax); }
+  }
+  __syncthreads();
+  const uint32_t n_cand = res[0];
+  const bool whole = n_cand < (uint32_t)k || n_cand > (uint32_t)kCandLds || n_act > kFinThreads;
+  const uint32_t n_c = whole ? (uint32_t)L : n_cand;
+  const float* srow = scores + (int64_t)b * stride;
+  uint2* lc = reinterpret_cast<uint2*>(big);
+  if (!whole) {
+    // Wave w copies chunks w, w + 16, ...: each chunk's slice goes to its
+    // offset in the gathered list.
+    for (int c = tid >> 6; c < n_act; c += kFinThreads / 64) {
+      const uint32_t n = ccnt[c], off = coff[c];
+      const uint2* src = ws.cand + (slot0 + c) * kTkChunk;
+      for (uint32_t i = lane; i < n; i += 64) lc[off + i] = src[i];
+    }
+  }
+  const uint32_t cmin = s_mm[0], cmax = s_mm[1];
+  if (tid == 0) bin_cnt = 0u;
+  __syncthreads();
+  select_k_best(lc, srow, whole, n_c, cmin, cmax, k, out, h, tmp, res, bin_list, &bin_cnt);
+}
+
+// Single-launch form for rows of up to kFusedMaxLen keys: one workgroup per
+// request derives tau, gathers the request's keys >= tau into LDS in token
+// order and selects.  Wave w streams the w-th of 16 equal token segments
+// (multiples of 256 tokens; 4 consecutive keys per lane and 16-byte load,
+// kFusedUnroll loads in flight) and appends its candidates, in token order,
+// to its own kWaveCand-entry LDS region; the regions are then packed into
+// one list.  Fewer than k candidates in all, or more than kWaveCand in one
+// segment, make the selection run over the whole request read from the
+// scores.  Score rows must be 16-byte aligned.
+constexpr int kWaveCand = kCandLds / (kFinThreads / 64);
+constexpr int kFusedUnroll = 8;
+// One CU streams a whole row here: past 64K keys (256 KB) the three launches,
+// which spread a row over many CUs, are faster (c3f, rows to 128K: 41.6
+// against 31.7 us; c4, rows to 64K: 30.0 against 35.1 us).
+constexpr int64_t kFusedMaxLen = 65536;
+
+__global__ __launch_bounds__(kFinThreads) void topk_fused_kernel(const float* __restrict__ scores, int64_t stride,
+                                                                 const int32_t* __restrict__ lens, int64_t max_len,
+                                                                 int32_t k, int32_t* __restrict__ out_idx,
+                                                                 int32_t* __restrict__ status) {
+  __shared__ uint32_t big[kFinLdsWords];   // wave regions, then the packed candidate list (uint2)
+  __shared__ uint32_t h[kBins];
+  __shared__ uint32_t tmp[kFinThreads / 64];
+  __shared__ uint32_t res[2];
+  __shared__ uint32_t s_mm[2];
+  __shared__ uint32_t c_mm[2];             // smallest and largest candidate key
+  __shared__ uint32_t wcnt[kFinThreads / 64];
+  __shared__ uint32_t ovf;
+  __shared__ uint2 bin_list[64];
+  __shared__ uint32_t bin_cnt;
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int32_t L = lens[b];
+  int32_t* out = out_idx + (int64_t)b * k;
+  if (!len_ok(L, max_len)) {
+    if (tid == 0 && status) atomicOr(status + b, kBadLen);
+    for (int j = tid; j < k; j += kFinThreads) out[j] = -1;
+    return;
+  }
+  if (L <= k) {
+    for (int j = tid; j < k; j += kFinThreads) out[j] = j < L ? j : -1;
+    return;
+  }
+  const float* srow = scores + (int64_t)b * stride;
+  if (tid == 0) { c_mm[0] = 0xFFFFFFFFu; c_mm[1] = 0u; ovf = 0u; bin_cnt = 0u; }
+  const uint32_t tau = request_tau<kFinThreads>(srow, L, k, h, tmp, res, s_mm);  // barriers inside
+
+  const int64_t seg = ((int64_t)(L + 15) / 16 + 255) / 256 * 256;
+  const int64_t s0 = (int64_t)wv * seg, s1 = min((int64_t)L, s0 + seg);
+  uint2* region = reinterpret_cast<uint2*>(big) + wv * kWaveCand;
+  const uint64_t below = (1ull << lane) - 1ull;
+  uint32_t cnt = 0, kmin = 0xFFFFFFFFu, kmax = 0u;
+  for (int64_t g = s0; g < s1; g += 256 * kFusedUnroll) {
+    float4 v[kFusedUnroll];
+#pragma unroll
+    for (int u = 0; u < kFusedUnroll; ++u) {
+      const int64_t t = g + u * 256 + lane * 4;
+      v[u] = t < s1 ? *reinterpret_cast<const float4*>(srow + t) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int u = 0; u < kFusedUnroll; ++u) {
+      const int64_t t = g + u * 256 + lane * 4;
+      const float f[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+      uint32_t key[4];
+      bool sel[4];
+      uint32_t before = 0, total = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        key[e] = order_key(f[e]);
+        sel[e] = t + e < s1 && key[e] >= tau;
+        const uint64_t m = __ballot(sel[e]);
+        before += (uint32_t)__popcll(m & below);
+        total += (uint32_t)__popcll(m);
+      }
+      uint32_t pos = cnt + before;  // token order: lanes below first, then this lane's earlier keys
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (sel[e]) {
+          if (pos < (uint32_t)kWaveCand) region[pos] = make_uint2(key[e], (uint32_t)(t + e));
+          kmin = min(kmin, key[e]);
+          kmax = max(kmax, key[e]);
+          ++pos;
+        }
+      }
+      cnt += total;
+    }
+  }
+  kmin = wave_min_u32(kmin);
+  kmax = wave_max_u32(kmax);
+  if (lane == 0) {
+    wcnt[wv] = cnt;
+    atomicMin(&c_mm[0], kmin);
+    atomicMax(&c_mm[1], kmax);
+    if (cnt > (uint32_t)kWaveCand) ovf = 1u;
+  }
+  __syncthreads();
+  uint32_t off = 0, n_cand = 0;
+#pragma unroll
+  for (int w = 0; w < kFinThreads / 64; ++w) {
+    const uint32_t c = wcnt[w];
+    off += w < wv ? c : 0u;
+    n_cand += c;
+  }
+  const bool whole = ovf != 0u || n_cand < (uint32_t)k;
+  uint2* lc = reinterpret_cast<uint2*>(big);
+  if (!whole) {
+    // Pack the regions: every wave takes its entries into registers, then
+    // (after the barrier) writes them at its offset in the list.
+    uint2 e[kWaveCand / 64];
+#pragma unroll
+    for (int r = 0; r < kWaveCand / 64; ++r) {
+      const uint32_t i = (uint32_t)(r * 64 + lane);
+      if (i < cnt) e[r] = region[i];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < kWaveCand / 64; ++r) {
+      const uint32_t i = (uint32_t)(r * 64 + lane);
+      if (i < cnt) lc[off + i] = e[r];
+    }
+    __syncthreads();
+  }
+  select_k_best(lc, srow, whole, whole ? (uint32_t)L : n_cand, c_mm[0], c_mm[1], k, out, h, tmp, res, bin_list,
+                &bin_cnt);
+}
+
 int launch_topk(const TopkArgs& a, hipStream_t s) {
   if (a.batch == 0) return 0;
   if (a.k > kMaxK || a.k < 1) return -2;
+  if (a.max_len <= kFusedMaxLen && reinterpret_cast<uintptr_t>(a.scores) % 16 == 0 && a.score_stride % 4 == 0) {
+    hipLaunchKernelGGL(topk_fused_kernel, dim3((unsigned)a.batch), dim3(kFinThreads), 0, s, a.scores,
+                       a.score_stride, a.lens, a.max_len, a.k, a.out_idx, a.status);
+    return hipGetLastError() == hipSuccess ? 0 : -3;
+  }
   TopkWs ws = carve(a.workspace, a.batch, a.max_len);
   const int64_t grid = (int64_t)a.batch * ws.chunks;
   if (grid > 0x7FFFFFFF) return -2;

@@ -97,12 +97,21 @@ def test_poisoned_tails_are_never_read():
 
 # ----------------------------------------------------------------- top-k only
 
-def _gpu_topk(scores, lens, k, max_len=None):
+def _gpu_topk(scores, lens, k, max_len=None, form="single"):
+    """form "single": 16-byte aligned score rows, which rows of up to 256K keys
+    send through the one-launch kernel; "launches": a row stride that is not
+    a multiple of 4 floats, which always takes the three-launch form."""
     spm = _lib()
     B, stride = scores.shape
     if max_len is None:
         max_len = int(max(lens)) if len(lens) else 0
-    s = torch.from_numpy(np.ascontiguousarray(scores, np.float32)).cuda()
+    if form == "launches":
+        pad = 5 - stride % 4                        # stride + pad is 1 mod 4
+        s = torch.from_numpy(np.pad(np.ascontiguousarray(scores, np.float32), ((0, 0), (0, pad)))).cuda()
+        assert s.stride(0) % 4 != 0                 # padding past the rows' keys is never read
+    else:
+        s = torch.from_numpy(np.ascontiguousarray(scores, np.float32)).cuda()
+        assert s.stride(0) % 4 == 0 and s.data_ptr() % 16 == 0
     l = torch.tensor(lens, dtype=torch.int32, device="cuda")
     out = torch.full((B, k), -7, dtype=torch.int32, device="cuda")
     ws = torch.empty(max(spm.topk_workspace_bytes(B, max_len, k), 256), dtype=torch.uint8, device="cuda")
@@ -112,8 +121,12 @@ def _gpu_topk(scores, lens, k, max_len=None):
     return out.cpu().numpy(), st.cpu().numpy()
 
 
+FORMS = pytest.mark.parametrize("form", ["single", "launches"])
+
+
+@FORMS
 @pytest.mark.parametrize("k", [1, 32, 2048, 4096])
-def test_topk_ties_nan_negzero(k):
+def test_topk_ties_nan_negzero(k, form):
     rng = np.random.default_rng(k)
     lens = [0, 1, 31, 2048, 5000, 70000]
     S = np.zeros((len(lens), 70016), np.float32)
@@ -123,21 +136,26 @@ def test_topk_ties_nan_negzero(k):
     S[3, ::7] = np.nan
     S[4, :] = 1.25                                                         # all equal
     S[5, ::3] = -0.0
-    idx, st = _gpu_topk(S, lens, k)
+    idx, st = _gpu_topk(S, lens, k, form=form)
     assert not st.any()
-    parity.check_topk_exact(idx, S, np.array(lens), k, f"ties k={k}")
+    parity.check_topk_exact(idx, S, np.array(lens), k, f"ties k={k} {form}")
 
 
-def test_topk_large_continuous():
+@FORMS
+@pytest.mark.parametrize("long_len", [300000, 65536])
+def test_topk_large_continuous(long_len, form):
+    """Rows past and at the one-launch kernel's 64K limit (the first go
+    through the three launches whatever the stride)."""
     rng = np.random.default_rng(11)
-    lens = [300000, 131072, 2047, 2049]
-    S = rng.standard_normal((4, 300032)).astype(np.float32) * 30 + 144
-    idx, st = _gpu_topk(S, lens, 2048)
-    parity.check_topk_exact(idx, S, np.array(lens), 2048, "continuous")
+    lens = [long_len, long_len // 2 + 1, 2047, 2049]
+    S = rng.standard_normal((4, long_len + 32)).astype(np.float32) * 30 + 144
+    idx, st = _gpu_topk(S, lens, 2048, form=form)
+    parity.check_topk_exact(idx, S, np.array(lens), 2048, f"continuous {long_len} {form}")
 
 
+@FORMS
 @pytest.mark.parametrize("max_len", [None, 300000])
-def test_topk_big_tie_groups(max_len):
+def test_topk_big_tie_groups(max_len, form):
     """Tie groups larger than what a workgroup holds on chip (every key equal;
     two values with the k-th falling inside ~15000 equal ones), plus a plain
     row; max_len 300000 sends the same rows through the multi-workgroup
@@ -148,31 +166,32 @@ def test_topk_big_tie_groups(max_len):
     S[0, :] = 1.25
     S[1, :] = (rng.random(S.shape[1]) < 0.5).astype(np.float32)
     S[2, :] = rng.standard_normal(S.shape[1]).astype(np.float32)
-    idx, st = _gpu_topk(S, lens, 2048, max_len)
+    idx, st = _gpu_topk(S, lens, 2048, max_len, form=form)
     assert not st.any()
-    parity.check_topk_exact(idx, S, np.array(lens), 2048, f"big ties max_len={max_len}")
+    parity.check_topk_exact(idx, S, np.array(lens), 2048, f"big ties max_len={max_len} {form}")
 
 
-def test_topk_sample_miss_falls_back():
+@FORMS
+@pytest.mark.parametrize("lens", [[100000, 250000, 90000, 90000], [60000, 65536, 50000, 50000]])
+def test_topk_sample_miss_falls_back(form, lens):
     """Rows whose sampled positions hold the largest keys: the threshold from
     the sample then admits fewer than k keys, and the finish must select over
     the whole request.  The sample positions are the top-k kernel's own (16
     runs of 256 keys starting evenly over [0, L - 256]); also a row sorted in
     decreasing order and one sorted in increasing order."""
     rng = np.random.default_rng(23)
-    lens = [100000, 250000, 90000, 90000]
-    S = rng.random((4, 250048)).astype(np.float32)
+    S = rng.random((4, max(lens) + 48)).astype(np.float32)
     for r in (0, 1):
         L = lens[r]
         for run in range(16):
             t0 = run * (L - 256) // 15
             S[r, t0:t0 + 256] = 10.0 + rng.random(256).astype(np.float32)
-    S[2, :90000] = np.sort(S[2, :90000])[::-1]
-    S[3, :90000] = np.sort(S[3, :90000])
+    S[2, :lens[2]] = np.sort(S[2, :lens[2]])[::-1]  # all candidates in the first segment
+    S[3, :lens[3]] = np.sort(S[3, :lens[3]])
     for k in (2048, 32):
-        idx, st = _gpu_topk(S, lens, k)
+        idx, st = _gpu_topk(S, lens, k, form=form)
         assert not st.any()
-        parity.check_topk_exact(idx, S, np.array(lens), k, f"sample miss k={k}")
+        parity.check_topk_exact(idx, S, np.array(lens), k, f"sample miss k={k} {form}")
 
 
 def test_topk_bad_len_flags_request():
