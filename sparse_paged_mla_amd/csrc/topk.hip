@@ -206,7 +206,7 @@ __device__ void find_bin_asc(const uint32_t* h, uint32_t need, uint32_t* tmp, ui
 // Threshold key tau of a request whose length exceeds k (see the top of the
 // file); called by all NT threads, barriers inside.
 template <int NT>
-__device__ uint32_t request_tau(const float* __restrict__ s, int32_t L, int32_t k, uint32_t* h, uint32_t* tmp,
+__device__ __forceinline__ uint32_t request_tau(const float* __restrict__ s, int32_t L, int32_t k, uint32_t* h, uint32_t* tmp,
                                 uint32_t* res, uint32_t* s_mm) {
   constexpr int PER = kSample / NT;
   const int tid = threadIdx.x;
@@ -340,7 +340,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_collect_kernel(const float* _
 // the score row `srow` -- with their indices written to `out` in that order.
 // [cmin, cmax] bounds the listed keys.  Called by all kFinThreads threads
 // after a barrier that follows *bin_cnt = 0; barriers inside.
-__device__ void select_k_best(const uint2* lc, const float* __restrict__ srow, bool whole, uint32_t n_c,
+__device__ __forceinline__ void select_k_best(const uint2* lc, const float* __restrict__ srow, bool whole, uint32_t n_c,
                               uint32_t cmin, uint32_t cmax, int32_t k, int32_t* __restrict__ out, uint32_t* h,
                               uint32_t* tmp, uint32_t* res, uint2* bin_list, uint32_t* bin_cnt) {
   const int tid = threadIdx.x;
