@@ -155,6 +155,9 @@ size_t topk_workspace_bytes(int32_t batch, int64_t max_len, int32_t k);
  *               uses).  Calls that share a workspace must not overlap.
  *  req_status   [batch] int32 or NULL.
  * Supported: 1 <= k <= 4096; max_len < 2^31.
+ * Launches: one when max_len <= 65536 and the score rows are 16-byte aligned
+ * (scores aligned, score_stride a multiple of 4), else three; the result is
+ * the same either way.
  */
 int topk_select(const float* scores, int64_t score_stride,
                 const int32_t* context_lens, int32_t batch, int64_t max_len, int32_t k,
