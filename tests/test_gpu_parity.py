@@ -194,6 +194,23 @@ def test_topk_sample_miss_falls_back(form, lens):
         parity.check_topk_exact(idx, S, np.array(lens), k, f"sample miss k={k} {form}")
 
 
+@FORMS
+def test_topk_clustered_candidates(form):
+    """The largest keys (distinct) packed into the first 3000 tokens: the
+    sample's first run sits inside the cluster, so about 2600 keys reach the
+    threshold, all in the first of the one-launch kernel's 16 segments (more
+    than its 1024-entry region: the whole-row selection takes over); also the
+    cluster in the middle of the row, and a row of ordinary keys."""
+    rng = np.random.default_rng(41)
+    lens = [50000, 50000, 50000]
+    S = rng.random((3, 50048)).astype(np.float32)
+    S[0, :3000] += 10.0
+    S[1, 20000:23000] += 10.0
+    idx, st = _gpu_topk(S, lens, 2048, form=form)
+    assert not st.any()
+    parity.check_topk_exact(idx, S, np.array(lens), 2048, f"clustered {form}")
+
+
 def test_topk_bad_len_flags_request():
     S = np.random.default_rng(0).standard_normal((3, 256)).astype(np.float32)
     spm = _lib()
