@@ -34,6 +34,11 @@
 //     spread of scores, but adversarial orders can do it), or more than fit
 //     in LDS (huge tie groups), the same steps run over the whole request
 //     read from the scores, so the result is exact in every case.
+//
+// Rows of at most 64K keys (max_len), 16-byte aligned, take one launch
+// instead (topk_fused_kernel): one workgroup per request does all three
+// steps, with the candidates going straight to LDS; same candidates, same
+// selection, same result.
 #include "common.h"
 #include "launch.h"
 
