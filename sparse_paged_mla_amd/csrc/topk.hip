@@ -51,6 +51,7 @@ constexpr int kTkPer = 16;                       // keys per thread per chunk
 constexpr int kTkChunk = kTkThreads * kTkPer;    // 4096 keys per workgroup
 constexpr int kBins = 2048;
 constexpr int kFinThreads = 1024;
+constexpr int kTauThreads = 1024;                // 4 sample keys per thread
 constexpr int kMaxK = 4096;
 constexpr int kSampleRuns = 16, kSampleRun = 256;
 constexpr int kSample = kSampleRuns * kSampleRun;  // keys sampled from a long request
@@ -267,17 +268,17 @@ __device__ __forceinline__ uint32_t request_tau(const float* __restrict__ s, int
 }
 
 // One workgroup per request longer than k: its tau into the workspace.
-__global__ __launch_bounds__(kTkThreads) void topk_tau_kernel(const float* __restrict__ scores, int64_t stride,
-                                                              const int32_t* __restrict__ lens, int64_t max_len,
-                                                              int32_t k, TopkWs ws) {
+__global__ __launch_bounds__(kTauThreads) void topk_tau_kernel(const float* __restrict__ scores, int64_t stride,
+                                                               const int32_t* __restrict__ lens, int64_t max_len,
+                                                               int32_t k, TopkWs ws) {
   __shared__ uint32_t h[kBins];
-  __shared__ uint32_t tmp[kTkThreads / 64];
+  __shared__ uint32_t tmp[kTauThreads / 64];
   __shared__ uint32_t res[2];
   __shared__ uint32_t s_mm[2];
   const int b = blockIdx.x;
   const int32_t L = lens[b];
   if (!len_ok(L, max_len) || L <= k) return;
-  const uint32_t tau = request_tau<kTkThreads>(scores + (int64_t)b * stride, L, k, h, tmp, res, s_mm);
+  const uint32_t tau = request_tau<kTauThreads>(scores + (int64_t)b * stride, L, k, h, tmp, res, s_mm);
   if (threadIdx.x == 0) ws.tau[b] = tau;
 }
 
@@ -652,7 +653,7 @@ int launch_topk(const TopkArgs& a, hipStream_t s) {
   TopkWs ws = carve(a.workspace, a.batch, a.max_len);
   const int64_t grid = (int64_t)a.batch * ws.chunks;
   if (grid > 0x7FFFFFFF) return -2;
-  hipLaunchKernelGGL(topk_tau_kernel, dim3((unsigned)a.batch), dim3(kTkThreads), 0, s, a.scores, a.score_stride,
+  hipLaunchKernelGGL(topk_tau_kernel, dim3((unsigned)a.batch), dim3(kTauThreads), 0, s, a.scores, a.score_stride,
                      a.lens, a.max_len, a.k, ws);
   hipLaunchKernelGGL(topk_collect_kernel, dim3((unsigned)grid), dim3(kTkThreads), 0, s, a.scores, a.score_stride,
                      a.lens, a.max_len, a.k, ws);
