@@ -518,18 +518,19 @@ __global__ __launch_bounds__(kFinThreads) void topk_finish_kernel(const float* _
 
 // Single-launch form for rows of up to kFusedMaxLen keys: one workgroup per
 // request derives tau, gathers the request's keys >= tau into LDS in token
-// order and selects.  Wave w streams the w-th of 16 equal token segments
-// (multiples of 256 tokens; 4 consecutive keys per lane and 16-byte load,
-// kFusedUnroll loads in flight) and appends its candidates, in token order,
-// to its own kWaveCand-entry LDS region; the regions are then packed into
-// one list.  Fewer than k candidates in all, or more than kWaveCand in one
+// order and selects.  Wave w streams the w-th of kFinThreads / 64 (16)
+// equal token segments (multiples of 256 tokens that together cover the
+// row; 4 consecutive keys per lane and 16-byte load, kFusedUnroll loads in
+// flight) and appends its candidates, in token order, to its own
+// kWaveCand-entry LDS region; the regions are then packed into one list.  Fewer than k candidates in all, or more than kWaveCand in one
 // segment, make the selection run over the whole request read from the
 // scores.  Score rows must be 16-byte aligned.
 constexpr int kWaveCand = kCandLds / (kFinThreads / 64);
+static_assert(kWaveCand % 64 == 0, "a wave packs its region in whole 64-entry rows");
 constexpr int kFusedUnroll = 8;
 // One CU streams a whole row here: past 64K keys (256 KB) the three launches,
 // which spread a row over many CUs, are faster (c3f, rows to 128K: 41.6
-// against 31.7 us; c4, rows to 64K: 30.0 against 35.1 us).
+// against 31.7 us; c4, rows to 64K: 28.0 against 35.1 us).
 constexpr int64_t kFusedMaxLen = 65536;
 
 __global__ __launch_bounds__(kFinThreads) void topk_fused_kernel(const float* __restrict__ scores, int64_t stride,
@@ -563,7 +564,8 @@ __global__ __launch_bounds__(kFinThreads) void topk_fused_kernel(const float* __
   if (tid == 0) { c_mm[0] = 0xFFFFFFFFu; c_mm[1] = 0u; ovf = 0u; bin_cnt = 0u; }
   const uint32_t tau = request_tau<kFinThreads>(srow, L, k, h, tmp, res, s_mm);  // barriers inside
 
-  const int64_t seg = ((int64_t)(L + 15) / 16 + 255) / 256 * 256;
+  constexpr int kWaves = kFinThreads / 64;  // one token segment per wave
+  const int64_t seg = ((int64_t)(L + kWaves - 1) / kWaves + 255) / 256 * 256;
   const int64_t s0 = (int64_t)wv * seg, s1 = min((int64_t)L, s0 + seg);
   uint2* region = reinterpret_cast<uint2*>(big) + wv * kWaveCand;
   const uint64_t below = (1ull << lane) - 1ull;
