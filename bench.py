@@ -369,7 +369,9 @@ def main():
                                                                                  run_flush=lambda: flush_sink.copy_(
                                                                                      flush_buf.amax()))
 
-    mq = None if not legs or cfg.dense else time_multi_query(cfg, db, inp, 2, splits, args.steps, flush,
+    # The expanded batch has n_q times the requests, so the same workgroup
+    # count comes from n_q times fewer KV splits.
+    mq = None if not legs or cfg.dense else time_multi_query(cfg, db, inp, 2, max(1, splits // 2), args.steps, flush,
                                                  run_flush=lambda: flush_sink.copy_(flush_buf.amax()))
     n_pre = min(2, cfg.batch)
     pre = None if not legs else time_prefill_chunk(cfg, db, inp, n_pre, min(64, int(inp.lens[:n_pre].min())), 2,
