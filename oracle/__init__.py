@@ -13,7 +13,8 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "liboracle_spmla.so")
+# SPMLA_ORACLE_LIB names another build of oracle.c (the sanitizer test's).
+_LIB_PATH = os.environ.get("SPMLA_ORACLE_LIB") or os.path.join(_HERE, "liboracle_spmla.so")
 _lib = None
 
 BAD_PAGE, BAD_LEN, BAD_INDEX, BAD_TAG = 1, 2, 4, 8
@@ -248,12 +249,12 @@ def page_check(block_table, bt_tags, lens, page_tags, page_size, max_len=None):
 
 def multi_query_step(q, q_idx, w, kv, kv_scale, k_pool, k_scale, block_table, lens, k, n_heads, d_latent, d_rope,
                      sm_scale, score_stride=None):
-    """Verification step over Q new tokens per request (all already in the
-    cache, at positions L-Q .. L-1), in one pass: the target model checks the
-    gamma+1 drafted positions with one parallel forward, position by position
-    in order [EG, "Speculative Decoding": why it is lossless; KW 5.3].
-    Query i sees only tokens t < L - Q + 1 + i (itself and what precedes it)
-    and has its own indexer scores, its own top-k and its own attention.
+    """Multi-query verification step [EG, "Speculative Decoding"; KW 5.3].
+
+    Q new tokens per request are already in the cache, at positions
+    L-Q .. L-1.  Query i has the causal limit L - Q + 1 + i (it sees itself
+    and every earlier token), and gets its own indexer scores, its own top-k
+    over that limit and its own attention over the selected tokens.
 
     q [B, Q, H, D], q_idx [B, Q, H_I, d_I], w [B, Q, H_I]; a request with
     L < Q is flagged BAD_LEN and its outputs are NaN.  Returns dict(scores

@@ -38,7 +38,12 @@ def load_library():
         return _lib
     if not os.path.exists(LIB_PATH):
         raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m sparse_paged_mla_amd.build`")
-    lib = ctypes.CDLL(LIB_PATH)
+    _lib = declare(ctypes.CDLL(LIB_PATH))
+    return _lib
+
+
+def declare(lib):
+    """Set the C signatures of every exported call on a loaded library handle."""
     vp, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
     lib.dsa_indexer_scores.restype = ctypes.c_int
     lib.dsa_indexer_scores.argtypes = [vp, i32, vp, vp, vp, i32, i32, i32, vp, i32, vp, i32, i64, i32, i32, vp, i64,
@@ -65,7 +70,6 @@ def load_library():
     lib.lse_merge.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp]
     lib.spmla_last_error.restype = ctypes.c_char_p
     lib.spmla_last_error.argtypes = []
-    _lib = lib
     return lib
 
 

@@ -9,6 +9,7 @@
 
 #include "../../include/sparse_mla.h"
 #include "launch.h"
+#include "topk_layout.h"
 
 namespace {
 

@@ -399,12 +399,15 @@ template <class Op, int KDT, int KSTEPS, int MT, int NQ>
 static int launch_one(const IndexerArgs& a, hipStream_t stream) {
   int page_shift = 0;
   while ((1 << page_shift) < a.page_size) ++page_shift;
-  if (a.batch == 0 || a.max_len == 0) return 0;
+  if (a.batch == 0) return 0;
   // Enough waves to fill the GPU, but not more than there are steps at most.
+  // At least one workgroup runs even when max_len is 0: its first wave is
+  // the one that flags requests whose length is out of range.
   constexpr int ROW_BYTES = KSTEPS * 4 * Op::KPL * Storage<KDT>::bytes;
   constexpr int STEP_TOK = IdxStep<ROW_BYTES>::tok;
   const int64_t max_steps = (int64_t)a.batch * ((a.max_len + STEP_TOK - 1) / STEP_TOK);
-  const int64_t grid = std::min<int64_t>((int64_t)kNumCu * IdxWg<MT>::per_cu, (max_steps + 3) / 4);
+  const int64_t grid =
+      std::max<int64_t>(1, std::min<int64_t>((int64_t)kNumCu * IdxWg<MT>::per_cu, (max_steps + 3) / 4));
   if (a.page_size < STEP_TOK)
     hipLaunchKernelGGL((indexer_kernel<Op, KDT, KSTEPS, MT, true, NQ>), dim3((unsigned)grid), dim3(kIdxThreads), 0,
                        stream, a.q_idx, a.w, reinterpret_cast<const uint8_t*>(a.k_pool), a.k_scale, a.num_pages,

@@ -23,7 +23,6 @@ struct TopkArgs {
   const float* scores; int64_t score_stride; const int32_t* lens; int32_t batch; int64_t max_len;
   int32_t k; int32_t* out_idx; void* workspace; int32_t* status;
 };
-size_t topk_workspace_size(int32_t batch, int64_t max_len, int32_t k);
 int launch_topk(const TopkArgs& a, hipStream_t stream);
 
 struct DecodeArgs {

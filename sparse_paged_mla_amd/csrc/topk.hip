@@ -41,14 +41,12 @@
 // selection, same result.
 #include "common.h"
 #include "launch.h"
+#include "topk_layout.h"
 
 #include <algorithm>
 
 namespace spmla {
 
-constexpr int kTkThreads = 256;
-constexpr int kTkPer = 16;                       // keys per thread per chunk
-constexpr int kTkChunk = kTkThreads * kTkPer;    // 4096 keys per workgroup
 constexpr int kBins = 2048;
 constexpr int kFinThreads = 1024;
 constexpr int kTauThreads = 1024;                // 4 sample keys per thread
@@ -65,16 +63,6 @@ struct TopkWs {
   uint2* cand;      // [B, chunks, kTkChunk] (key, index), chunk c's in its own slice, ascending index
   int32_t chunks;
 };
-
-static inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
-static inline int32_t n_chunks(int64_t max_len) { return (int32_t)std::max<int64_t>(1, (max_len + kTkChunk - 1) / kTkChunk); }
-
-size_t topk_workspace_size(int32_t batch, int64_t max_len, int32_t k) {
-  (void)k;
-  if (batch <= 0 || max_len < 0) return 0;
-  const size_t bc = (size_t)batch * (size_t)n_chunks(max_len);
-  return align_up((size_t)batch * 4, 256) + align_up(bc * 16, 256) + bc * kTkChunk * 8;
-}
 
 static TopkWs carve(void* ws, int32_t batch, int64_t max_len) {
   TopkWs w;

@@ -21,11 +21,19 @@ def _declared():
     return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\**\s+\**([a-z_0-9]+)\s*\(", text, flags=re.M)))
 
 
+# SPMLA_BOUNDARY_LIB names a host-only build of the same validation layer
+# with the launchers stubbed out (the sanitizer test's); it also exports
+# spmla_stub_launches(), the number of calls that got past validation.
+STUB_LIB = os.environ.get("SPMLA_BOUNDARY_LIB")
+
+
 @pytest.fixture(scope="module")
 def lib():
+    import sparse_paged_mla_amd as spm
+    if STUB_LIB:
+        return spm.declare(ctypes.CDLL(STUB_LIB))
     if not os.path.exists(LIB):
         pytest.fail("libsparse_mla.so is not built (run __graft_entry__.build())")
-    import sparse_paged_mla_amd as spm
     return spm.load_library()
 
 
@@ -39,6 +47,12 @@ def test_header_declares_the_four_operations():
 def test_library_exports_every_declared_symbol(lib):
     for n in _declared():
         assert hasattr(lib, n), f"{n} not exported"
+
+
+def _launches(lib):
+    f = lib.spmla_stub_launches
+    f.restype = ctypes.c_int
+    return f()
 
 
 def test_product_never_loads_the_oracle():
@@ -217,3 +231,26 @@ def test_append_pair_rejects(lib):
     assert call(kv_scale=None) == EINVAL
     assert call(idx_rows=None) == EINVAL
     assert call(idx_pool=MIS) == EINVAL
+
+
+@pytest.mark.skipif(not STUB_LIB, reason="needs the host-only build with stubbed launchers")
+def test_valid_calls_reach_the_launcher_and_rejected_ones_do_not(lib):
+    """With the launchers stubbed, every call that passes validation reaches
+    its launcher exactly once and every rejected call reaches none."""
+    n0 = _launches(lib)
+    assert _idx(lib) == OK
+    assert _dec(lib) == OK
+    assert lib.lse_merge(FAKE, FAKE, 2, 4, 4, 512, FAKE, FAKE, None) == OK
+    assert _app(lib) == OK
+    assert lib.kv_page_check(FAKE, FAKE, 4, FAKE, 2, 100, FAKE, 10, 64, FAKE, None) == OK
+    assert lib.mq_expand_requests(FAKE, 4, FAKE, 2, 2, FAKE, FAKE, None) == OK
+    need = lib.topk_workspace_bytes(4, 100000, 2048)
+    assert lib.topk_select(FAKE, 100000, FAKE, 4, 100000, 2048, FAKE, ctypes.c_void_p(0x100000), need, None,
+                           None) == OK
+    assert lib.spmla_last_error() == b""
+    assert _launches(lib) == n0 + 7
+    assert _idx(lib, d=96) == EUNSUPPORTED
+    assert _dec(lib, splits=0) == EUNSUPPORTED
+    assert lib.topk_select(FAKE, 100000, FAKE, 4, 100000, 2048, FAKE, ctypes.c_void_p(0x100000), need - 1, None,
+                           None) == EWORKSPACE
+    assert _launches(lib) == n0 + 7

@@ -65,9 +65,28 @@ def test_full_size_step(name):
                                                   None if idx is None else idx[sel], cfg.n_heads, cfg.d_latent,
                                                   cfg.d_rope, cfg.softmax_scale, max_len=inp.max_len)
     assert not st_ref.any()
-    parity.check_attention(step.o.cpu().numpy()[sel], step.lse.cpu().numpy()[sel], o_ref, lse_ref,
-                           f"{name} attention requests {reqs}")
-    _say(f"{name}: attention of requests {reqs} matches")
+    o_gpu = step.o.cpu().numpy()
+    d_o = parity.check_attention(o_gpu[sel], step.lse.cpu().numpy()[sel], o_ref, lse_ref,
+                                 f"{name} attention requests {reqs}")
+    _say(f"{name}: attention of requests {reqs} matches (max |do| {d_o:.2e}, "
+         f"relative RMS {parity.rel_rms(o_gpu[sel], o_ref):.2e})")
+    if not cfg.dense and name != "c5":
+        # Diagnostic: the oracle's own fp64 scores and top-k for the shortest
+        # request, against what the GPU selected and produced.
+        b = np.array([int(np.argmin(L))], np.int32)
+        s_full, _, _ = oracle.indexer_scores(inp.q_idx[b], inp.w[b], inp.k_idx, inp.k_idx_scale,
+                                             inp.block_table[b], L[b], max_len=inp.max_len,
+                                             score_stride=int(L[b][0]))
+
+        def att(ix):
+            o, l, _ = oracle.mla_attention(inp.q[b], inp.kv, inp.kv_scale, inp.block_table[b], L[b], ix,
+                                           cfg.n_heads, cfg.d_latent, cfg.d_rope, cfg.softmax_scale,
+                                           max_len=inp.max_len)
+            return o, l
+        e2e = parity.end_to_end(idx[b], o_gpu[b], s_full, L[b], cfg.topk, att)
+        _say(f"{name}: end to end (request {int(b[0])}, L={int(L[b][0])}): {e2e['swaps']} of {e2e['selected']} "
+             f"selected tokens differ from the fp64 ranking; max |do| {e2e['max_abs_do']:.2e}, "
+             f"relative RMS {e2e['rel_rms_o']:.2e}")
 
 
 def test_full_size_multi_query_c3f():

@@ -361,6 +361,47 @@ def test_page_permutation_and_determinism():
         assert np.array_equal(x1, x2), f"{name} changes under a page permutation"
 
 
+def test_request_order_does_not_change_results():
+    """Reordering the requests of a batch permutes the outputs and changes
+    no bit of any request's scores, selection, o or lse (each request's work
+    is independent of where it sits in the batch and of which waves share a
+    workgroup with it)."""
+    import dataclasses
+    _lib()
+    cfg = gen.CONFIGS["c3f"].with_(batch=5)
+    lens = [3000, 70, 9000, 2049, 4100]
+    a = gen.make_inputs(cfg, lens=lens)
+    perm = np.array([3, 0, 4, 2, 1])
+    b = dataclasses.replace(a, lens=a.lens[perm].copy(), block_table=a.block_table[perm].copy(),
+                            q=a.q[perm].copy(), q_idx=a.q_idx[perm].copy(), w=a.w[perm].copy())
+    for splits in (1, 2):
+        _, s1 = _step(a, splits)
+        _, s2 = _step(b, splits)
+        for name in ("idx", "o", "lse", "status"):
+            x1, x2 = getattr(s1, name).cpu().numpy(), getattr(s2, name).cpu().numpy()
+            assert np.array_equal(x1[perm], x2), f"{name} changes when the requests are reordered"
+        sc1, sc2 = s1.scores.cpu().numpy(), s2.scores.cpu().numpy()
+        for j, i in enumerate(perm):
+            assert np.array_equal(sc1[i, :lens[i]], sc2[j, :lens[i]]), "scores change when the requests are reordered"
+
+
+def test_indexer_flags_bad_length_when_max_len_is_zero():
+    """max_len 0 with a request of length 5: the indexer has nothing to
+    score but still flags the request (a length above max_len is bad)."""
+    spm = _lib()
+    cfg = gen.CONFIGS["c3f"].with_(batch=2)
+    inp = gen.make_inputs(cfg, lens=[0, 5])
+    db = device_batch(inp)
+    scores = torch.zeros(2, 64, dtype=torch.float32, device="cuda")
+    st = torch.zeros(2, dtype=torch.int32, device="cuda")
+    spm.dsa_indexer_scores(db.q_idx, db.w, db.k_idx, db.k_idx_scale, db.block_table, db.lens, 0, scores, st)
+    torch.cuda.synchronize()
+    assert list(st.cpu().numpy()) == [0, spm.BAD_LEN]
+    _, _, st_ref = oracle.indexer_scores(inp.q_idx, inp.w, inp.k_idx, inp.k_idx_scale, inp.block_table, inp.lens,
+                                         max_len=0, score_stride=64)
+    assert list(st_ref) == [0, spm.BAD_LEN]
+
+
 # Different split boundaries change the running max each probability is taken
 # against before it is rounded to bf16 for the value contraction, so outputs
 # agree to the bf16 rounding of the weights (relative 2^-9 each), not bit for
