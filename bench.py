@@ -317,7 +317,7 @@ def cpu_baseline(inp, n_single, n_multi, gpu_pass, step):
     import numpy as np
     cfg = inp.cfg
     model, n_logical, usable = _host_cpu()
-    threads = max(1, min(16, usable))
+    threads = max(1, min(16, usable, n_multi))
     single_s, multi_s, gpu_ms = [], [], []
     out_single = None
     for _ in range(3):
@@ -488,16 +488,13 @@ def main():
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic, kernel=dom,
                     algorithmic_bytes=int(dk["bytes"]), avg_launch_us=round(t_dom * 1e6, 2))
-    roof_scope = (f"one kernel ({dom}, the largest roofline time of the step), not the whole step: "
-                  f"the whole step's fraction of its roofline is step_roofline.frac")
     else:
         achieved = dk["flops"] / t_dom / 1e12
         roof = dict(bound="mfma", achieved=round(achieved, 2), peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
                     frac=round(achieved / BF16_PEAK_TFLOPS, 4), traffic=traffic, kernel=dom,
                     algorithmic_flops=int(dk["flops"]), avg_launch_us=round(t_dom * 1e6, 2))
-        roof_scope = (f"one kernel ({dom}, the largest roofline time of the step), not the whole step: "
-                      f"the whole step's fraction of its roofline is step_roofline.frac")
-    roof["scope"] = roof_scope
+    roof["scope"] = (f"one kernel ({dom}, the largest roofline time of the step), not the whole step: "
+                     f"the whole step's fraction of its roofline is step_roofline.frac")
 
     if args.profile_only:
         # A plain device-to-device copy of known size: the HBM counters read for
