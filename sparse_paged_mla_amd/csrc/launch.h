@@ -33,6 +33,8 @@ struct DecodeArgs {
   float* o_part; float* lse_part; int32_t* status;
 };
 int launch_decode(const DecodeArgs& a, hipStream_t stream);
+// FP8 cache, bf16 query, 512 + 64 dims (mla_decode_f8.hip).
+int launch_decode_f8(const DecodeArgs& a, hipStream_t stream);
 
 struct MergeArgs {
   const float* o_part; const float* lse_part; int32_t batch, num_splits, n_heads, d; float* o; float* lse;

@@ -948,7 +948,7 @@ int launch_decode(const DecodeArgs& a, hipStream_t s) {
   const int D = a.d_latent + a.d_rope;
   if (a.q_dtype == kBF16 && D == 576 && a.d_latent == 512) {
     if (a.kv_dtype == kBF16) return launch_one<OpBF16, kBF16, 18, 32>(a, s);
-    if (a.kv_dtype == kFP8) return launch_f8(a, s);
+    if (a.kv_dtype == kFP8) return launch_decode_f8(a, s);
     return -2;
   }
   if (a.q_dtype == kF32 && D == 80 && a.d_latent == 64) {

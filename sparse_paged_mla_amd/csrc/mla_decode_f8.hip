@@ -1,0 +1,674 @@
+// mla_paged_decode for an FP8 e4m3 latent cache with a per-token scale, bf16
+// query, 512 latent + 64 rope dims: split-KV MLA decode over the selected
+// tokens, both contractions on MFMA, with the waves of a workgroup
+// specialised by role so that vector work on one wave of a SIMD overlaps
+// matrix work on the other.
+//
+// Workgroup = (request b, split s, group of 64 query heads); 8 waves.
+//  - Waves 0-3, score waves: wave (hq, th) holds the query of heads
+//    32hq..32hq+31 of the group and computes, for every 32-token tile, the
+//    scores of those heads against the tile's tokens 16th..16th+15 over all
+//    576 dims, then their softmax weights.  Latent dims: the scaled FP8 MFMA
+//    (16x16x128, tokens on M, heads on N) against the query written as two
+//    scaled e4m3 terms per 128-dim block (the cache codes are used as they
+//    are); rope dims: the bf16 MFMA with the codes widened exactly in
+//    registers.  The weights go to LDS as bf16, already multiplied by each
+//    token's FP8 scale.
+//  - Waves 4-7, value waves: wave (hq, dh) accumulates O[32 heads x 256 dims]
+//    (heads 32hq.., dims 256dh..) += P[32 heads x 32 tokens] . V[32 tokens x
+//    256 dims] on the 32x32x16 bf16 MFMA, one tile behind the score waves.
+//    V comes from the same LDS tile through gfx950's 8-bit transposing LDS
+//    read and is widened exactly to bf16 in registers.  These waves also
+//    fetch the tiles: every lane's 16-byte piece of a tile goes straight from
+//    HBM into LDS (global_load_lds_dwordx4), so a tile costs no registers and
+//    no vector instructions to stage.
+// With waves w and w + 4 on the same SIMD, each SIMD runs one wave of each
+// role.  Tiles rotate through kNB LDS buffers and are requested kPF tiles
+// ahead of the one being scored; one barrier per tile.
+//
+// LDS tile layout: 608-byte rows (36 16-byte chunks of codes, 2 spare), and
+// bit 0 of a row's chunk index flipped on rows r with bit 3 of r differing
+// from bit 4: the score reads, the rope reads and the transposing value
+// reads are then free of bank conflicts.  The direct loads fill whole 1 KiB
+// blocks (one per wave instruction), so the spare chunks are filled with a
+// repeat of the row's last chunk.
+//
+// The waits for the direct loads are explicit (the compiler does not track
+// them): each value wave issues exactly kLoads loads per tile, so "tile i + 1
+// has landed" is "at most kLoads * (kPF - 1) loads outstanding".  Barriers
+// are s_barrier with the wave's LDS operations drained first, without the
+// fence __syncthreads() carries (that fence would also wait for every direct
+// load in flight).
+//
+// Softmax: weights are taken against a fixed reference per head, the
+// largest logit of the split's first tile (both score waves of a head meet
+// in LDS once, before the loop).  Later weights are exp2(z - m_ref) <=
+// 2^kHeadroom unless a logit exceeds m_ref by more than kHeadroom; if that
+// happens anywhere in the workgroup the split is recomputed once with the
+// true maximum.  The reference cancels in o = O / l, so this is the same
+// quantity as the running-max form, and the accumulators are never rescaled.
+#include "common.h"
+#include "launch.h"
+
+#include <utility>
+
+#pragma clang diagnostic ignored "-Winline-asm"  // m0 is clobbered on purpose: the direct loads set it
+
+namespace spmla {
+namespace {
+
+constexpr int kThreads = 512;
+constexpr int kTileTok = 32;
+constexpr int kD = 576, kDC = 512;
+constexpr int kRS = 608;                          // LDS row stride (bytes)
+constexpr int kRowChunks = kRS / 16;              // 38 chunk slots per row
+constexpr int kTileBytes = kTileTok * kRS;        // 19456
+constexpr int kRowLoads = kTileBytes / 1024;      // 19 wave loads of 1 KiB per tile
+constexpr int kLoads = 5;                         // per value wave per tile: 19 row loads + 1 scale load
+constexpr int kNB = 6;                            // tile buffers
+constexpr int kPF = 4;                            // tiles requested ahead of the scored one
+constexpr int kSeg = 1024;                        // positions resolved at once
+constexpr int kHeadsWg = 64;
+constexpr int kPStride = 40;                      // bf16 per weight row (32 tokens + 8 pad)
+constexpr float kHeadroom = 16.f;
+static_assert(kTileBytes % 1024 == 0 && kRowLoads + 1 == 4 * kLoads, "tile loads split evenly");
+static_assert(kNB >= kPF + 2, "a tile buffer is refilled only after both roles are done with it");
+static_assert(kLoads * (kPF - 1) <= 63, "vmcnt range");
+
+typedef int v8i_t __attribute__((ext_vector_type(8)));
+typedef int v2i_t __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) v2i_t lds_v2i;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// A zero row and a unit scale: what a masked position loads, so every load
+// is unconditional and a masked token scores exactly 0 before its -inf bias.
+__device__ __attribute__((aligned(16))) uint8_t g_zero_row[kD];
+__device__ __attribute__((aligned(16))) float g_unit_scale[4] = {1.f, 1.f, 1.f, 1.f};
+
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+__device__ __forceinline__ int swz(int r) { return ((r >> 3) ^ (r >> 4)) & 1; }
+
+// Wait until at most N vector-memory operations of this wave are in flight
+// (gfx9 s_waitcnt: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt left at
+// their maxima).  The empty asm statements keep memory operations from being
+// moved across the wait.
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N <= 63, "vmcnt");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+  asm volatile("" ::: "memory");
+}
+
+// Workgroup barrier: this wave's LDS reads and writes complete, then
+// s_barrier.  No fence: direct loads in flight are left alone.
+__device__ __forceinline__ void wg_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Direct loads into LDS: each lane's 16 (or 4) bytes at gptr land at LDS
+// byte address lds + 16 * lane (4 * lane) of the issuing wave; lds must be
+// the same in every lane.  Written as asm so that the compiler does not
+// treat later LDS reads as waiting on them (it would wait for every load in
+// flight); the waits are the explicit vm_wait calls.  An asm load issued
+// before one of the compiler's own loads only makes the compiler's count
+// for that load conservative, since loads complete in order.
+__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const void* gptr, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(gptr), "s"(lds) : "memory", "m0");
+}
+template <class T>
+__device__ __forceinline__ uint32_t lds_addr(T* p) {
+  return (uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) T*)p);
+}
+
+__device__ __forceinline__ int xcd_remap(int bid, int n) {
+  const int q = n >> 3, r = n & 7;
+  const int xcd = bid & 7, slot = bid >> 3;
+  return xcd < r ? xcd * (q + 1) + slot : r * (q + 1) + (xcd - r) * q + slot;
+}
+
+// Writes this lane's 32 values v (bf16 values held in fp32) as
+// v = 2^(E-7) * (hi + lo/16), hi and lo e4m3 codes, where E = floor(log2 M)
+// and M is the largest |v| over the four lanes of the row (lanes l, l^16,
+// l^32, l^48: the 128 k-slots of one MFMA row), so one scale per row and
+// term serves the block.  hi is v scaled below 256 and rounded to 4
+// significant bits; the remainder of an element within 2^14 of M is a
+// multiple of its last bf16 bit below half an e4m3 step, so 16 times it is
+// an e4m3 value and the sum is exact; a smaller element keeps an error below
+// 2^-22 of M.  A non-finite element turns the hi codes of its lane into NaN,
+// so the scores it feeds come out NaN.  Call with the whole wave active.
+__device__ __forceinline__ void split_q32(const float* v, v8i_t& hi, v8i_t& lo, int& shi, int& slo) {
+  float amax = 0.f;
+  bool bad = false;
+#pragma unroll
+  for (int j = 0; j < 32; ++j) {
+    const float a = fabsf(v[j]);
+    bad |= !(a <= 3.402823466e38f);
+    amax = fmaxf(amax, a);
+  }
+  amax = fmaxf(amax, __shfl_xor(amax, 16));
+  amax = fmaxf(amax, __shfl_xor(amax, 32));
+  int E = (int)((__float_as_uint(amax) >> 23) & 0xFF) - 127;
+  E = max(E, -115);
+  const float mul = __uint_as_float((uint32_t)(134 - E) << 23);  // 2^(7 - E)
+  shi = E + 120;
+  slo = E + 116;
+#pragma unroll
+  for (int w = 0; w < 8; ++w) {
+    __builtin_amdgcn_sched_barrier(0);  // four elements at a time: few temporaries beside the outputs
+    int h = 0, l = 0;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const float x0 = v[4 * w + 2 * p] * mul, x1 = v[4 * w + 2 * p + 1] * mul;
+      const int hp = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
+      const f32x2 d = __builtin_amdgcn_cvt_pk_f32_fp8(hp, false);
+      const int lp = __builtin_amdgcn_cvt_pk_fp8_f32((x0 - d[0]) * 16.f, (x1 - d[1]) * 16.f, 0, false);
+      h |= (hp & 0xFFFF) << (16 * p);
+      l |= (lp & 0xFFFF) << (16 * p);
+    }
+    hi[w] = bad ? 0x7F7F7F7F : h;
+    lo[w] = l;
+  }
+}
+
+// Four FP8 codes per dword, two dwords -> 8 bf16 values, exactly.
+__device__ __forceinline__ bf16x8 widen8(uint32_t w0, uint32_t w1) {
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w0, 1.0f, false);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w0, 1.0f, true);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w1, 1.0f, false);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w1, 1.0f, true);
+  const bf16x8 r = {a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+  return r;
+}
+
+__global__ __launch_bounds__(kThreads) void mla_decode_f8ws_kernel(
+    const __bf16* __restrict__ q, const uint8_t* __restrict__ kv, const float* __restrict__ kv_scale,
+    int32_t num_pages, int32_t page_shift, const int32_t* __restrict__ bt, int32_t bt_stride,
+    const int32_t* __restrict__ lens, int64_t max_len, const int32_t* __restrict__ indices, int32_t k,
+    int32_t n_heads, float sm_scale_log2, int32_t num_splits, int32_t n_hg, float* __restrict__ o_part,
+    float* __restrict__ lse_part, int32_t* __restrict__ status) {
+  __shared__ __attribute__((aligned(16))) uint8_t Kbuf[kNB][kTileBytes];
+  __shared__ __attribute__((aligned(16))) float Tsc[kNB][64];          // FP8 scales of a tile's rows (32 used)
+  __shared__ __attribute__((aligned(16))) int32_t seg_row[kSeg];        // cache row, or -1 when masked
+  __shared__ __attribute__((aligned(16))) float seg_bias[kSeg];         // 0, or -inf when masked
+  __shared__ __attribute__((aligned(16))) __bf16 Pbuf[2][kHeadsWg * kPStride];
+  __shared__ __attribute__((aligned(16))) float red[2][kHeadsWg];       // per token half: head maxima / sums
+  __shared__ __attribute__((aligned(16))) bf16x8 Qrope[2][2][2][64];    // [hq][nt][ks][lane]: rope dims of the query
+  __shared__ int redo_flag;
+  __shared__ int bad_flag;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool score_wave = wv < 4;
+  const int role = wv & 3;
+  const int hq = role >> 1;            // head tile: heads 32hq..32hq+31 of the group
+  const int th = role & 1;             // score waves: token half of each tile
+  const int dh = role & 1;             // value waves: dim half
+  const int g = lane >> 4;
+  const int r16 = lane & 15;
+  const int page_size = 1 << page_shift;
+  const float kNaN = __uint_as_float(0x7FC00000u);
+
+  const int logical = xcd_remap(blockIdx.x, gridDim.x);
+  const int hg = logical % n_hg;
+  const int s = (logical / n_hg) % num_splits;
+  const int b = logical / (n_hg * num_splits);
+  const int head_base = hg * kHeadsWg;
+
+  auto out_o = [&](int h, int dim) -> float* {
+    return o_part + ((((int64_t)b * num_splits + s) * n_heads + h) * kDC + dim);
+  };
+  auto out_lse = [&](int h) -> float* { return lse_part + (((int64_t)b * num_splits + s) * n_heads + h); };
+
+  const int32_t L = lens[b];
+  if (L < 0 || (int64_t)L > max_len || (int64_t)L > (int64_t)bt_stride * page_size) {
+    if (tid == 0 && status) atomicOr(status + b, kBadLen);
+    for (int i = tid; i < kHeadsWg * kDC; i += kThreads) {
+      const int h = head_base + i / kDC;
+      if (h < n_heads) *out_o(h, i % kDC) = kNaN;
+    }
+    if (tid < kHeadsWg && head_base + tid < n_heads) *out_lse(head_base + tid) = kNaN;
+    return;
+  }
+  const int64_t n = indices ? (int64_t)k : (int64_t)L;
+  const int64_t per = ((n + num_splits - 1) / num_splits + kTileTok - 1) / kTileTok * kTileTok;
+  const int64_t p_begin = (int64_t)s * per;
+  const int64_t p_end = min(n, p_begin + per);
+  const int32_t* btb = bt + (int64_t)b * bt_stride;
+  const int32_t* idxb = indices ? indices + (int64_t)b * k : nullptr;
+  if (tid == 0) bad_flag = 0;
+  wg_barrier();  // bad_flag is cleared before any table entry may set it
+
+  // Resolve positions [seg, seg_end) of the split (index -> page -> row);
+  // entries past seg_end are masked.
+  auto build_table = [&](int64_t seg, int64_t seg_end) __attribute__((always_inline)) {
+    int64_t t[kSeg / kThreads];
+#pragma unroll
+    for (int u = 0; u < kSeg / kThreads; ++u) {
+      const int64_t p = seg + tid + u * kThreads;
+      t[u] = p < seg_end ? (idxb ? (int64_t)idxb[p] : p) : -1;
+    }
+    int32_t page[kSeg / kThreads];
+#pragma unroll
+    for (int u = 0; u < kSeg / kThreads; ++u) page[u] = (t[u] >= 0 && t[u] < L) ? btb[t[u] >> page_shift] : -1;
+#pragma unroll
+    for (int u = 0; u < kSeg / kThreads; ++u) {
+      int32_t row = -1;
+      if (t[u] < -1 || t[u] >= L) {
+        bad_flag = 1;
+        if (status) atomicOr(status + b, kBadIndex);
+      } else if (t[u] >= 0) {
+        if (page[u] < 0 || page[u] >= num_pages) {
+          bad_flag = 1;
+          if (status) atomicOr(status + b, kBadPage);
+        } else {
+          row = (int32_t)(((int64_t)page[u] << page_shift) + (t[u] & (page_size - 1)));
+        }
+      }
+      seg_row[tid + u * kThreads] = row;
+      seg_bias[tid + u * kThreads] = row >= 0 ? 0.f : -INFINITY;
+    }
+  };
+
+  // ---- the query of the group's 64 heads, staged in LDS (buffer space,
+  // free until the first tile is requested) by direct loads: 64 rows of
+  // 1152 bytes, 72 wave loads of 1 KiB, 9 per wave.  The score waves then
+  // hold heads head_base + 32hq + 16nt + r16 as two scaled FP8 terms per
+  // 128-dim latent block (lane group g holds dims 16g..16g+15 and
+  // 64+16g..64+16g+15 of a block, the k-slot order of the scaled MFMA) plus
+  // the rope dims in bf16 (dims 512 + 32ks + 8g..+7).  The E8M0 scales of
+  // the four blocks share one register per term, one byte each (selected
+  // per MFMA).  The rope part waits in LDS and is read per tile (registers
+  // are the score waves' scarce resource).
+  const bool any_token = p_begin < p_end;
+  if (any_token) {
+    const uint32_t qbase = lds_addr(&Kbuf[0][0]);
+#pragma unroll
+    for (int u = 0; u < 9; ++u) {
+      const int ld = 9 * wv + u;
+      const int piece = 64 * ld + lane;
+      const int h = head_base + piece / 72;
+      const __bf16* src = q + ((int64_t)b * n_heads + (h < n_heads ? h : 0)) * kD + 8 * (piece % 72);
+      dma16(src, qbase + 1024 * ld);
+    }
+  }
+  // The first segment's table is resolved while the query is in flight.
+  if (any_token) build_table(p_begin, min(p_end, p_begin + kSeg));
+  if (any_token) {
+    vm_wait<0>();
+    wg_barrier();  // the query and the first table are in LDS
+  }
+
+  int64_t built = any_token ? p_begin : -1;  // segment whose table is in LDS
+  // Both roles run the same sequence of barriers: per segment two around
+  // the table, one when tile 0 has landed, one more when the reference is
+  // set, one when tile 1 has landed, and one per tile; per pass one for the
+  // recompute decision (and one more when it recomputes); two to finish.
+  if (score_wave) {
+    v8i_t qhi[2][4], qlo[2][4];
+    int qs_hi[2] = {0, 0}, qs_lo[2] = {0, 0};
+    if (any_token) {
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const int hl = hq * 32 + nt * 16 + r16;
+      const bool ok = head_base + hl < n_heads;
+      const uint8_t* qrow = &Kbuf[0][0] + hl * (2 * kD);
+#pragma unroll
+      for (int blk = 0; blk < 4; ++blk) {
+        __builtin_amdgcn_sched_barrier(0);  // one block at a time: its temporaries die before the next
+        const uint4 raw[4] = {*reinterpret_cast<const uint4*>(qrow + 2 * (128 * blk + 16 * g)),
+                              *reinterpret_cast<const uint4*>(qrow + 2 * (128 * blk + 16 * g) + 16),
+                              *reinterpret_cast<const uint4*>(qrow + 2 * (128 * blk + 64 + 16 * g)),
+                              *reinterpret_cast<const uint4*>(qrow + 2 * (128 * blk + 64 + 16 * g) + 16)};
+        float v[32];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const uint32_t ws[4] = {raw[c].x, raw[c].y, raw[c].z, raw[c].w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            v[8 * c + 2 * e] = ok ? bf16_bits_to_f32(ws[e] & 0xFFFFu) : 0.f;
+            v[8 * c + 2 * e + 1] = ok ? bf16_bits_to_f32(ws[e] >> 16) : 0.f;
+          }
+        }
+        int shi, slo;
+        split_q32(v, qhi[nt][blk], qlo[nt][blk], shi, slo);
+        qs_hi[nt] |= shi << (8 * blk);
+        qs_lo[nt] |= slo << (8 * blk);
+      }
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const uint4 r = *reinterpret_cast<const uint4*>(qrow + 2 * (kDC + 32 * ks + 8 * g));
+        Qrope[hq][nt][ks][lane] = ok ? __builtin_bit_cast(bf16x8, r) : zero_frag<OpBF16>();
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+      wg_barrier();  // the buffers are free for tiles
+    }
+    // ---- score waves: scores of the tile in Kt for this wave's 16 tokens
+    // (rows 16th + r16 on M) and its 32 heads (two N-tiles): S[nt] holds head
+    // 16nt + r16 for tokens 16th + 4g + j.
+    auto score_tile = [&](const uint8_t* __restrict__ Kt, f32x4 (&S)[2]) __attribute__((always_inline)) {
+      f32x4 acc[2][2];
+  #pragma unroll
+      for (int nt = 0; nt < 2; ++nt) acc[nt][0] = acc[nt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int row = th * 16 + r16;
+      const int sw = swz(row);
+      const uint8_t* rp = Kt + row * kRS;
+      static_for<4>([&](auto B) {
+        constexpr int blk = decltype(B)::value;
+        const uint4 k0 = *reinterpret_cast<const uint4*>(rp + 16 * ((8 * blk + g) ^ sw));
+        const uint4 k1 = *reinterpret_cast<const uint4*>(rp + 16 * ((8 * blk + 4 + g) ^ sw));
+        const v8i_t a = {(int)k0.x, (int)k0.y, (int)k0.z, (int)k0.w, (int)k1.x, (int)k1.y, (int)k1.z, (int)k1.w};
+  #pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+          acc[nt][0] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, qhi[nt][blk], acc[nt][0], 0, 0, 0, 127,
+                                                                        blk, qs_hi[nt]);
+          acc[nt][1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, qlo[nt][blk], acc[nt][1], 0, 0, 0, 127,
+                                                                        blk, qs_lo[nt]);
+        }
+      });
+  #pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const uint2 kr = *reinterpret_cast<const uint2*>(rp + 16 * ((32 + 2 * ks + (g >> 1)) ^ sw) + 8 * (g & 1));
+        const bf16x8 kb = widen8(kr.x, kr.y);
+  #pragma unroll
+        for (int nt = 0; nt < 2; ++nt) acc[nt][1] = OpBF16::mma(kb, Qrope[hq][nt][ks][lane], acc[nt][1]);
+      }
+  #pragma unroll
+      for (int nt = 0; nt < 2; ++nt) S[nt] = acc[nt][0] + acc[nt][1];
+    };
+
+    float m_ref[2] = {-INFINITY, -INFINITY};   // reference of head 16nt + r16 (log2 domain)
+    float m_lane[2] = {-INFINITY, -INFINITY};  // this lane's largest logit
+    float l_lane[2] = {0.f, 0.f};              // this lane's sum of weights
+    bool fallback = false;                     // the first tile had no valid token: 0 stood in for m_ref
+    // Softmax weights of a scored tile, written to P as bf16.
+    auto softmax_tile = [&](const f32x4 (&S)[2], int buf, int tb, __bf16* __restrict__ P, bool& over)
+        __attribute__((always_inline)) {
+      const int t0 = th * 16 + 4 * g;
+      const f32x4 ts = *reinterpret_cast<const f32x4*>(&Tsc[buf][t0]);
+      const f32x4 bi = *reinterpret_cast<const f32x4*>(&seg_bias[tb + t0]);
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        float z[4], mx = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          z[j] = __builtin_fmaf(S[nt][j], sm_scale_log2 * ts[j], bi[j]);
+          mx = fmaxf(mx, z[j]);
+        }
+        m_lane[nt] = fmaxf(m_lane[nt], mx);
+        over |= mx > m_ref[nt] + kHeadroom;
+        float pv[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float pp = __builtin_amdgcn_exp2f(z[j] - m_ref[nt]);
+          l_lane[nt] += pp;
+          pv[j] = pp * ts[j];
+        }
+        typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+        const bf16x4_t w4 = {(__bf16)pv[0], (__bf16)pv[1], (__bf16)pv[2], (__bf16)pv[3]};
+        *reinterpret_cast<bf16x4_t*>(P + (hq * 32 + nt * 16 + r16) * kPStride + t0) = w4;
+      }
+    };
+    for (int pass = 0; pass < 2; ++pass) {
+      l_lane[0] = l_lane[1] = 0.f;
+      bool over = false;
+      if (tid == 0) redo_flag = 0;
+      for (int64_t seg = p_begin; seg < p_end; seg += kSeg) {
+        const int64_t seg_end = min(p_end, seg + kSeg);
+        const int T = (int)((seg_end - seg + kTileTok - 1) / kTileTok);
+        const bool need_ref = pass == 0 && seg == p_begin;
+        if (seg != built) {
+          wg_barrier();  // the previous segment is done with the table
+          build_table(seg, seg_end);
+          built = seg;
+          wg_barrier();
+        }
+        wg_barrier();  // tile 0 has landed
+        f32x4 S[2];
+        score_tile(Kbuf[0], S);
+        if (need_ref) {
+          const int t0 = th * 16 + 4 * g;
+          const f32x4 ts = *reinterpret_cast<const f32x4*>(&Tsc[0][t0]);
+          const f32x4 bi = *reinterpret_cast<const f32x4*>(&seg_bias[t0]);
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt) {
+            float mx = -INFINITY;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) mx = fmaxf(mx, __builtin_fmaf(S[nt][j], sm_scale_log2 * ts[j], bi[j]));
+            mx = wave_max_xor16_32(mx);
+            if (g == 0) red[th][hq * 32 + nt * 16 + r16] = mx;
+          }
+          wg_barrier();
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt) {
+            const int hl = hq * 32 + nt * 16 + r16;
+            m_ref[nt] = fmaxf(red[0][hl], red[1][hl]);
+            // No valid token in the first tile (the same for every head): 0
+            // stands in, and the split is recomputed with the true maximum
+            // if any valid token turns up.
+            if (m_ref[nt] == -INFINITY) {
+              m_ref[nt] = 0.f;
+              fallback = true;
+            }
+          }
+        }
+        softmax_tile(S, 0, 0, Pbuf[0], over);
+        wg_barrier();  // tile 1 has landed; P of tile 0 is written
+        int buf = 1;
+        for (int i = 1; i <= T; ++i) {
+          if (i < T) {
+            score_tile(Kbuf[buf], S);
+            softmax_tile(S, buf, i * kTileTok, Pbuf[i & 1], over);
+          }
+          buf = buf == kNB - 1 ? 0 : buf + 1;
+          wg_barrier();
+        }
+      }
+      // Recompute the split once if a logit outgrew its head's reference,
+      // or if the reference was a stand-in and valid tokens were seen.
+      const bool seen = m_lane[0] > -INFINITY || m_lane[1] > -INFINITY;
+      if (__any(over || (fallback && seen)) && lane == 0) atomicOr(&redo_flag, 1);
+      wg_barrier();
+      if (pass == 1 || redo_flag == 0) break;
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const float mt = wave_max_xor16_32(m_lane[nt]);
+        if (g == 0) red[th][hq * 32 + nt * 16 + r16] = mt;
+      }
+      wg_barrier();
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const int hl = hq * 32 + nt * 16 + r16;
+        m_ref[nt] = fmaxf(red[0][hl], red[1][hl]);
+        if (m_ref[nt] == -INFINITY) m_ref[nt] = 0.f;
+      }
+      fallback = false;
+    }
+    // ---- finish: l per head from both token halves, then lse.
+    wg_barrier();  // red is free again
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const float ls = wave_sum_xor16_32(l_lane[nt]);
+      if (g == 0) red[th][hq * 32 + nt * 16 + r16] = ls;
+    }
+    wg_barrier();
+    const bool bad = bad_flag != 0;
+    if (th == 0 && g == 0) {
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const int hl = hq * 32 + nt * 16 + r16;
+        const int h = head_base + hl;
+        if (h < n_heads) {
+          const float l = red[0][hl] + red[1][hl];
+          const float lse = l > 0.f ? (m_ref[nt] + log2f(l)) * 0.69314718055994530942f : -INFINITY;
+          *out_lse(h) = bad ? kNaN : lse;
+        }
+      }
+    }
+  } else {
+    if (any_token) wg_barrier();  // the score waves have the query: the buffers are free for tiles
+    // ---- value waves: the 16-byte piece of each tile this lane loads.  Row
+    // loads 4w'..4w'+3 and (w' < 3) 16 + w' of the tile's 19 (w' = role);
+    // wave 3's fifth load is the tile's scales.  Piece p of a load lands at
+    // slot p of the tile: row p / 38, chunk slot p % 38, which holds chunk
+    // (p % 38) ^ swz(row) of the row (the two spare slots repeat chunk 35).
+    int ld_off[kLoads];
+  #pragma unroll
+    for (int u = 0; u < kLoads; ++u) {
+      const int ld = u < 4 ? 4 * role + u : 16 + role;
+      const int slot = 64 * ld + lane;
+      const int r = min(slot / kRowChunks, kTileTok - 1);
+      const int c = min((slot % kRowChunks) ^ swz(r), kD / 16 - 1);
+      ld_off[u] = (r << 8) | c;
+    }
+    const uint8_t* zero_row = g_zero_row;
+    const float* unit_scale = g_unit_scale;
+    // Send the loads of tile `tile` of the segment (T tiles) into buffer
+    // `buf`; a tile past the segment's end loads the zero row into a buffer
+    // no tile uses, so every call issues exactly kLoads loads.
+    auto issue_tile = [&](int tile, int T, int buf) __attribute__((always_inline)) {
+      const bool real = tile < T;
+      const int32_t* rows = seg_row + min(tile, T - 1) * kTileTok;
+      const uint32_t dst = lds_addr(&Kbuf[0][0]) + buf * kTileBytes;
+  #pragma unroll
+      for (int u = 0; u < kLoads; ++u) {
+        if (u < 4 || role < 3) {
+          const int ld = u < 4 ? 4 * role + u : 16 + role;
+          const int c = ld_off[u] & 255;
+          const int32_t row = real ? rows[ld_off[u] >> 8] : -1;
+          const uint8_t* src = row >= 0 ? kv + ((int64_t)row * (kD / 16) + c) * 16 : zero_row + 16 * c;
+          dma16(src, dst + 1024 * ld);
+        } else {
+          const int32_t row = real ? rows[lane & 31] : -1;
+          const float* src = row >= 0 ? kv_scale + row : unit_scale;
+          dma4(src, lds_addr(&Tsc[0][0]) + buf * 256);
+        }
+      }
+    };
+
+    // ---- value waves: O += P . V for the tile in Vt with the weights in P.
+    // A operand (P): lane l holds head l % 32, tokens 16ks + 8(l / 32) + e.
+    // B operand (V): the transposing read hands lane i of each 16-lane group
+    // G the dim 16(G & 1) + i of the N-tile for tokens 16ks + 8(G >> 1) + e,
+    // e < 8, when lane j of the group points at 8 dims (8(j & 1)..) of token
+    // row 16ks + 8(G >> 1) + j / 2.
+    auto pv_tile = [&](const uint8_t* __restrict__ Vt, const __bf16* __restrict__ P, f32x16 (&acc_o)[8])
+        __attribute__((always_inline)) {
+      const int G = lane >> 4, j = lane & 15;
+  #pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16x8 pa = *reinterpret_cast<const bf16x8*>(P + (hq * 32 + (lane & 31)) * kPStride + 16 * ks +
+                                                           8 * (lane >> 5));
+        const int tr = 16 * ks + 8 * (G >> 1) + (j >> 1);
+        const int sw = swz(tr);
+        const uint8_t* vrow = Vt + tr * kRS + 8 * (j & 1);
+  #pragma unroll
+        for (int nt = 0; nt < 8; ++nt) {
+          const int chunk = 16 * dh + 2 * nt + (G & 1);
+          const v2i_t raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(vrow + 16 * (chunk ^ sw)));
+          acc_o[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, widen8((uint32_t)raw[0], (uint32_t)raw[1]),
+                                                              acc_o[nt], 0, 0, 0);
+        }
+      }
+      // Keep each V fragment's read two MFMAs ahead of its use rather than
+      // all sixteen up front (which needs ~100 registers beside the 128 of
+      // the accumulators).
+      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+      static_for<15>([&](auto) {
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      });
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    };
+    f32x16 acc_o[8];
+    for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) acc_o[nt] = f32x16{};
+      for (int64_t seg = p_begin; seg < p_end; seg += kSeg) {
+        const int64_t seg_end = min(p_end, seg + kSeg);
+        const int T = (int)((seg_end - seg + kTileTok - 1) / kTileTok);
+        const bool need_ref = pass == 0 && seg == p_begin;
+        if (seg != built) {
+          wg_barrier();
+          build_table(seg, seg_end);
+          built = seg;
+          wg_barrier();
+        }
+#pragma unroll
+        for (int i = 0; i < kPF; ++i) issue_tile(i, T, i);
+        vm_wait<kLoads * (kPF - 1)>();  // tile 0 has landed
+        wg_barrier();
+        if (need_ref) wg_barrier();
+        issue_tile(kPF, T, kPF);
+        vm_wait<kLoads * (kPF - 1)>();  // tile 1 has landed
+        wg_barrier();
+        int buf_in = kPF + 1, buf_pv = 0;  // buffers of tiles i + kPF and i - 1
+        for (int i = 1; i <= T; ++i) {
+          issue_tile(i + kPF, T, buf_in);
+          pv_tile(Kbuf[buf_pv], Pbuf[(i - 1) & 1], acc_o);
+          vm_wait<kLoads * (kPF - 1)>();  // tile i + 1 has landed
+          buf_in = buf_in == kNB - 1 ? 0 : buf_in + 1;
+          buf_pv = buf_pv == kNB - 1 ? 0 : buf_pv + 1;
+          wg_barrier();
+        }
+        vm_wait<0>();  // the loads past the segment's end are done with
+      }
+      wg_barrier();
+      if (pass == 1 || redo_flag == 0) break;
+      wg_barrier();
+    }
+    // ---- finish: o = O / l.  D layout of the 32x32 MFMA: element e of
+    // lane l is row (head) 8(e / 4) + 4(l / 32) + e % 4, column (dim) l % 32.
+    wg_barrier();
+    wg_barrier();
+    const bool bad = bad_flag != 0;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int hl = hq * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+      const int h = head_base + hl;
+      const float l = red[0][hl] + red[1][hl];
+      const float inv = bad ? kNaN : (l > 0.f ? 1.f / l : 0.f);
+      if (h < n_heads) {
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) *out_o(h, dh * 256 + nt * 32 + (lane & 31)) = acc_o[nt][e] * inv;
+      }
+    }
+  }
+}
+
+}  // namespace
+
+int launch_decode_f8(const DecodeArgs& a, hipStream_t stream) {
+  int page_shift = 0;
+  while ((1 << page_shift) < a.page_size) ++page_shift;
+  const int n_hg = (a.n_heads + kHeadsWg - 1) / kHeadsWg;
+  const int64_t grid = (int64_t)a.batch * a.num_splits * n_hg;
+  if (grid == 0) return 0;
+  if (grid > 0x7FFFFFFF) return -2;
+  const float sm_log2 = a.sm_scale * 1.44269504088896340736f;
+  hipLaunchKernelGGL(mla_decode_f8ws_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream,
+                     reinterpret_cast<const __bf16*>(a.q), reinterpret_cast<const uint8_t*>(a.kv), a.kv_scale,
+                     a.num_pages, page_shift, a.bt, a.bt_stride, a.lens, a.max_len, a.indices, a.k, a.n_heads,
+                     sm_log2, a.num_splits, n_hg, a.o_part, a.lse_part, a.status);
+  return hipGetLastError() == hipSuccess ? 0 : -3;
+}
+
+}  // namespace spmla
