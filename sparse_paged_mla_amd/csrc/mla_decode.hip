@@ -1,9 +1,9 @@
 // mla_paged_decode kernels: split-KV MLA decode over the selected tokens of
-// the paged latent cache, both contractions on MFMA.  Two kernels share one
-// schedule: mla_decode_kernel (bf16 or fp32 caches, and the small fp32
-// query shapes) widens each tile once into LDS; mla_decode_f8_kernel (FP8
-// cache, bf16 query, 576-dim rows) keeps the tile in LDS as FP8 codes and
-// runs the latent score dims on the scaled FP8 MFMA (further below).
+// the paged latent cache, both contractions on MFMA.  mla_decode_kernel
+// (bf16 or fp32 caches, and the small fp32 query shapes) widens each tile
+// once into LDS; an FP8 cache with a bf16 query and 576-dim rows goes to the
+// role-specialised kernel of mla_decode_f8.hip, which keeps the tile in LDS
+// as FP8 codes.
 //
 // Workgroup = (request b, split s, group of 64 query heads); 8 waves.  A pair
 // of waves shares 16 heads: each wave of the pair contracts half of the row
@@ -447,467 +447,6 @@ __global__ __launch_bounds__(kDecThreads) void mla_decode_kernel(
   }
 }
 
-// ---------------------------------------------------------------------------
-// FP8 cache, bf16 query, 512 latent + 64 rope dims: the same workgroup, wave
-// and tile schedule as above, but the tile stays in LDS as FP8 codes (half
-// the bytes of a widened tile, and no widening pass):
-//  - Scores: the wave's 256 latent dims run on the scaled FP8 MFMA
-//    (16x16x128), against the query written as two scaled e4m3 terms
-//    (split_q32); its 32 rope dims run on the bf16 MFMA with the key codes
-//    widened in registers.
-//  - Values: the bf16 MFMA as above (P in bf16), with V fetched by gfx950's
-//    8-bit transposing LDS read and widened exactly to bf16 in registers.
-// LDS rows are 608 bytes (38 16-byte chunks) and bit 0 of a row's chunk
-// index is flipped on rows r with bit 3 of r differing from bit 4 (swz), so
-// that the score reads, the rope reads, the transposing value reads and the
-// staging writes are all free of bank conflicts on gfx950 (64 banks of 4
-// bytes; 8-byte accesses serve lanes 0-31 then 32-63 per cycle, 16-byte
-// accesses lanes 8p..8p+7 with 8p+16..8p+23).  The score reads take chunks g
-// and 4 + g of a 128-dim block, so lane group g holds dims 16g..16g+15 and
-// 64+16g..64+16g+15 of it: the query operand uses the same order.
-namespace f8dec {
-constexpr int kD = 576, kDC = 512;
-constexpr int kRS = 608;
-constexpr int kTileBytes = kTile * kRS;
-__device__ __forceinline__ int rowbase(int r) { return r * kRS; }
-__device__ __forceinline__ int swz(int r) { return ((r >> 3) ^ (r >> 4)) & 1; }
-}  // namespace f8dec
-
-typedef int v8i_t __attribute__((ext_vector_type(8)));
-typedef int v2i_t __attribute__((ext_vector_type(2)));
-
-// Writes this lane's 32 values v (bf16 values held in fp32) as
-// v = 2^(E-7) * (hi + lo/16), hi and lo e4m3 codes, where E = floor(log2 M)
-// and M is the largest |v| over the four lanes of the row (lanes l, l^16,
-// l^32, l^48: the 128 k-slots of one MFMA row).  One scale per row and term
-// is what makes any assignment of dims to k-slots valid: the hardware
-// applies the E8M0 scale of lane group b to k-slots 32b..32b+31, which
-// lanes 2(b&1) and 2(b&1)+1 hold (low 16 bytes for b < 2, high 16 after).
-// hi is v scaled below 256 and rounded to 4 significant bits; the remainder
-// of an element within 2^14 of M is a multiple of its last bf16 bit below
-// half an e4m3 step, so 16 times it is an e4m3 value and the sum is exact; a
-// smaller element keeps an error below 2^-22 of M.  A non-finite element
-// turns the hi codes of its lane into NaN, so the scores it feeds come out
-// NaN.  Call with the whole wave active.
-__device__ __forceinline__ void split_q32(const float* v, v8i_t& hi, v8i_t& lo, int& shi, int& slo) {
-  float amax = 0.f;
-  bool bad = false;
-#pragma unroll
-  for (int j = 0; j < 32; ++j) {
-    const float a = fabsf(v[j]);
-    bad |= !(a <= 3.402823466e38f);
-    amax = fmaxf(amax, a);
-  }
-  amax = fmaxf(amax, __shfl_xor(amax, 16));
-  amax = fmaxf(amax, __shfl_xor(amax, 32));
-  int E = (int)((__float_as_uint(amax) >> 23) & 0xFF) - 127;
-  E = max(E, -115);
-  const float mul = __uint_as_float((uint32_t)(134 - E) << 23);  // 2^(7 - E)
-  shi = E + 120;
-  slo = E + 116;
-#pragma unroll
-  for (int w = 0; w < 8; ++w) {
-    int h = 0, l = 0;
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      const float x0 = v[4 * w + 2 * p] * mul, x1 = v[4 * w + 2 * p + 1] * mul;
-      const int hp = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
-      const f32x2 d = __builtin_amdgcn_cvt_pk_f32_fp8(hp, false);
-      const int lp = __builtin_amdgcn_cvt_pk_fp8_f32((x0 - d[0]) * 16.f, (x1 - d[1]) * 16.f, 0, false);
-      h |= (hp & 0xFFFF) << (16 * p);
-      l |= (lp & 0xFFFF) << (16 * p);
-    }
-    hi[w] = bad ? 0x7F7F7F7F : h;
-    lo[w] = l;
-  }
-}
-
-// Four FP8 codes (one dword) per pair of halves -> 8 bf16 values, exactly.
-__device__ __forceinline__ bf16x8 widen8(uint32_t w0, uint32_t w1) {
-  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w0, 1.0f, false);
-  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w0, 1.0f, true);
-  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w1, 1.0f, false);
-  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w1, 1.0f, true);
-  const bf16x8 r = {a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
-  return r;
-}
-
-template <int NW>
-__global__ __launch_bounds__(NW * 64) void mla_decode_f8_kernel(
-    const __bf16* __restrict__ q, const uint8_t* __restrict__ kv, const float* __restrict__ kv_scale,
-    int32_t num_pages, int32_t page_shift, const int32_t* __restrict__ bt, int32_t bt_stride,
-    const int32_t* __restrict__ lens, int64_t max_len, const int32_t* __restrict__ indices, int32_t k,
-    int32_t n_heads, float sm_scale_log2, int32_t num_splits, int32_t n_hg, float* __restrict__ o_part,
-    float* __restrict__ lse_part, int32_t* __restrict__ status) {
-  using namespace f8dec;
-  constexpr int NT_H = kDC / 32;  // output 16-dim tiles per half
-  constexpr int NTHR = NW * 64;
-  constexpr int HPW = NW / 2 * kHeadsPerWave;  // heads per workgroup
-  constexpr int SEG = 2 * NTHR;                // segment table entries
-  constexpr int SROWS = kTile * 16 / NTHR;     // staged rows per thread
-
-  __shared__ __attribute__((aligned(16))) uint8_t Kbuf[kBufs][kTileBytes];
-  __shared__ __attribute__((aligned(16))) int32_t seg_row[SEG];
-  __shared__ __attribute__((aligned(16))) float seg_zsc[SEG];
-  __shared__ __attribute__((aligned(16))) float seg_tsc[SEG];
-  __shared__ __attribute__((aligned(16))) float seg_bias[SEG];
-  __shared__ f32x4 sx[2][NW][2][64];
-  __shared__ int redo_flag;
-  __shared__ int bad_flag;
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wv = tid >> 6;
-  const int half = wv & 1;
-  const int g = lane >> 4;
-  const int r16 = lane & 15;
-  const int page_size = 1 << page_shift;
-
-  const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  const int hg = logical % n_hg;
-  const int s = (logical / n_hg) % num_splits;
-  const int b = logical / (n_hg * num_splits);
-  const int head0 = hg * HPW + (wv >> 1) * kHeadsPerWave;
-  const bool wave_active = head0 < n_heads;
-  const float kNaN = __uint_as_float(0x7FC00000u);
-
-  auto out_o = [&](int h, int dim) -> float* {
-    return o_part + ((((int64_t)b * num_splits + s) * n_heads + h) * kDC + dim);
-  };
-  auto out_lse = [&](int h) -> float* { return lse_part + (((int64_t)b * num_splits + s) * n_heads + h); };
-
-  const int32_t L = lens[b];
-  if (L < 0 || (int64_t)L > max_len || (int64_t)L > (int64_t)bt_stride * page_size) {
-    if (tid == 0 && status) atomicOr(status + b, kBadLen);
-    if (wave_active) {
-      for (int i = lane; i < kHeadsPerWave * (kDC / 2); i += 64) {
-        const int h = head0 + i / (kDC / 2);
-        if (h < n_heads) *out_o(h, half * (kDC / 2) + i % (kDC / 2)) = kNaN;
-      }
-      if (half == 0 && lane < kHeadsPerWave && head0 + lane < n_heads) *out_lse(head0 + lane) = kNaN;
-    }
-    return;
-  }
-  const int64_t n = indices ? (int64_t)k : (int64_t)L;
-  const int64_t per = ((n + num_splits - 1) / num_splits + kTile - 1) / kTile * kTile;
-  const int64_t p_begin = (int64_t)s * per;
-  const int64_t p_end = min(n, p_begin + per);
-  v8i_t qhi[2], qlo[2];  // query terms (set below, used by qk_partial)
-  int qs_hi[2], qs_lo[2];
-  bf16x8 qrope;
-
-  const int32_t* btb = bt + (int64_t)b * bt_stride;
-  const int32_t* idxb = indices ? indices + (int64_t)b * k : nullptr;
-  const int srow = tid >> 4;  // staging: tile rows srow + rr * NTHR / 16 of this thread
-  const int sj = tid & 15;    // staging: 16-byte chunks sj and sj + 16, and dword sj of the last 64 bytes
-  struct Staged {  // one tile's rows in flight: codes, row valid, FP8 scale
-    uint32_t raw[SROWS][9];
-    bool ok[SROWS];
-    float sc[SROWS];
-  };
-  Staged st;
-
-  // Issue the global loads of the tile whose first row is seg_row[tb], and
-  // of the rows' FP8 scales: every lane issues three row loads whatever its
-  // row (a masked row reads row 0, the spare third chunk re-reads the row's
-  // last chunk), so the compiler can count them across the tile's math.
-  auto issue = [&](int tb, Staged& x) __attribute__((always_inline)) {
-#pragma unroll
-    for (int rr = 0; rr < SROWS; ++rr) {
-      const int32_t row = seg_row[tb + srow + rr * (NTHR / 16)];
-      x.ok[rr] = row >= 0;
-      const int64_t r = row >= 0 ? row : 0;
-      const uint8_t* src = kv + r * kD;
-      load_raw<16>(src + 16 * sj, x.raw[rr]);
-      load_raw<16>(src + 16 * (sj + 16), x.raw[rr] + 4);
-      x.raw[rr][8] = *reinterpret_cast<const uint32_t*>(src + 512 + 4 * sj);
-      x.sc[rr] = kv_scale[r];
-    }
-  };
-  // Copy the staged codes into an LDS tile (a masked row becomes zeros) and
-  // the rows' score and weight factors into the segment table.
-  auto stage = [&](uint8_t* __restrict__ Kt, int tb, const Staged& x) __attribute__((always_inline)) {
-#pragma unroll
-    for (int rr = 0; rr < SROWS; ++rr) {
-      const int row = srow + rr * (NTHR / 16);
-      if (sj == 0) {
-        const float sc = x.ok[rr] ? x.sc[rr] : 1.f;  // a masked row's scale slot may hold anything
-        seg_zsc[tb + row] = sm_scale_log2 * sc;
-        seg_tsc[tb + row] = sc;
-      }
-      const int sw = swz(row);
-      uint8_t* dst = Kt + rowbase(row) + 16 * (sj ^ sw);
-      const uint32_t* w = x.raw[rr];
-      const bool ok = x.ok[rr];
-      *reinterpret_cast<uint4*>(dst) = ok ? make_uint4(w[0], w[1], w[2], w[3]) : make_uint4(0, 0, 0, 0);
-      *reinterpret_cast<uint4*>(dst + 256) = ok ? make_uint4(w[4], w[5], w[6], w[7]) : make_uint4(0, 0, 0, 0);
-      *reinterpret_cast<uint32_t*>(Kt + rowbase(row) + 16 * ((32 + (sj >> 2)) ^ sw) + 4 * (sj & 3)) = ok ? w[8] : 0u;
-    }
-  };
-
-  // Partial scores S^T[token x head] over this wave's half of the dims.
-  // Key rows r16 and 16 + r16 (A operand); two accumulator chains per row
-  // block (one per query term), summed at the end.
-  auto qk_partial = [&](const uint8_t* __restrict__ Kt, f32x4 (&out)[2]) __attribute__((always_inline)) {
-    f32x4 acc[2][2];
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      acc[m][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-      acc[m][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-#pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        const uint8_t* kp = Kt + rowbase(16 * m + r16) + 256 * half + 128 * blk + 16 * (g ^ swz(16 * m + r16));
-        const uint4 k0 = *reinterpret_cast<const uint4*>(kp);
-        const uint4 k1 = *reinterpret_cast<const uint4*>(kp + 64);
-        const v8i_t a = {(int)k0.x, (int)k0.y, (int)k0.z, (int)k0.w, (int)k1.x, (int)k1.y, (int)k1.z, (int)k1.w};
-        acc[m][0] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, qhi[blk], acc[m][0], 0, 0, 0, 127, 0,
-                                                                      qs_hi[blk]);
-        acc[m][1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, qlo[blk], acc[m][1], 0, 0, 0, 127, 0,
-                                                                      qs_lo[blk]);
-      }
-    }
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      const int row = 16 * m + r16;
-      const uint2 kr = *reinterpret_cast<const uint2*>(Kt + rowbase(row) + kDC + 32 * half +
-                                                       16 * ((g >> 1) ^ swz(row)) + 8 * (g & 1));
-      acc[m][1] = OpBF16::mma(widen8(kr.x, kr.y), qrope, acc[m][1]);
-      out[m] = acc[m][0] + acc[m][1];
-    }
-  };
-
-  // ---- segment table: entry e of the segment starting at position seg is
-  // token idx[seg + e] (or seg + e when dense), resolved to its cache row
-  // through the block table (-1 when masked); two entries per thread, the
-  // index loads of both issued before either page lookup.  The FP8 scales
-  // are fetched with the rows themselves (issue/stage).
-  auto table_idx = [&](int64_t seg, int64_t seg_end, int64_t (&t)[2]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int64_t p = seg + tid + u * NTHR;
-      t[u] = p < seg_end ? (idxb ? (int64_t)idxb[p] : p) : -1;
-    }
-  };
-  auto table_rows = [&](const int64_t (&t)[2]) __attribute__((always_inline)) {
-    int32_t page[2];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) page[u] = (t[u] >= 0 && t[u] < L) ? btb[t[u] >> page_shift] : -1;
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      int32_t row = -1;
-      if (t[u] < -1 || t[u] >= L) {
-        bad_flag = 1;
-        if (status) atomicOr(status + b, kBadIndex);
-      } else if (t[u] >= 0) {
-        if (page[u] < 0 || page[u] >= num_pages) {
-          bad_flag = 1;
-          if (status) atomicOr(status + b, kBadPage);
-        } else {
-          row = (int32_t)(((int64_t)page[u] << page_shift) + (t[u] & (page_size - 1)));
-        }
-      }
-      const int e = tid + u * NTHR;
-      seg_row[e] = row;
-      seg_bias[e] = row >= 0 ? 0.f : -INFINITY;
-    }
-  };
-
-  // Query of head r16 (B operand of S^T = K . Q^T): latent dims
-  // 256*half + 128*blk + 32*g .. +31 as two scaled FP8 terms per block, and
-  // rope dims 512 + 32*half + 8*g .. +7 in bf16.  Its loads and the first
-  // segment's index loads are sent before the split is computed, and the
-  // page lookups after, so the latencies overlap.
-  if (tid == 0) bad_flag = 0;
-  int64_t built = -1;  // segment whose table is in LDS
-  {
-    const int h = head0 + r16;
-    const bool ok = wave_active && h < n_heads;
-    const __bf16* qh = q + ((int64_t)b * n_heads + (ok ? h : 0)) * kD;
-    uint4 qraw[2][4];
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-      // dims 16g..16g+15 and 64+16g..64+16g+15 of the block
-      const uint4* src = reinterpret_cast<const uint4*>(qh + 256 * half + 128 * blk + 16 * g);
-      qraw[blk][0] = src[0];
-      qraw[blk][1] = src[1];
-      qraw[blk][2] = src[8];
-      qraw[blk][3] = src[9];
-    }
-    const uint4 rq = *reinterpret_cast<const uint4*>(qh + kDC + 32 * half + 8 * g);
-    int64_t t0[2];
-    if (p_begin < p_end) table_idx(p_begin, min(p_end, p_begin + SEG), t0);
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-      float v[32];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const uint32_t ws[4] = {qraw[blk][c].x, qraw[blk][c].y, qraw[blk][c].z, qraw[blk][c].w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          v[8 * c + 2 * e] = ok ? bf16_bits_to_f32(ws[e] & 0xFFFFu) : 0.f;
-          v[8 * c + 2 * e + 1] = ok ? bf16_bits_to_f32(ws[e] >> 16) : 0.f;
-        }
-      }
-      split_q32(v, qhi[blk], qlo[blk], qs_hi[blk], qs_lo[blk]);
-    }
-    qrope = ok ? __builtin_bit_cast(bf16x8, rq) : zero_frag<OpBF16>();
-    if (p_begin < p_end) {
-      __syncthreads();  // bad_flag initialised before any table entry sets it
-      table_rows(t0);
-      built = p_begin;
-    }
-  }
-
-  // Value operand source of this lane for the transposing read: lane j of
-  // group g points at 8 dims of token row tau_g(j / 2), where tau_g(s) is
-  // 4g + s for s < 4 and 16 + 4g + s - 4 after, the k-slot order the softmax
-  // weights sit in.  The read hands lane i of the group that dim (i) for all
-  // eight tokens.
-  const int vj = r16 >> 1;
-  const int vrow = vj < 4 ? 4 * g + vj : 16 + 4 * g + vj - 4;
-  // Tile column chunk half*16 + nt lies at chunk half*16 + (nt ^ swz(vrow)).
-  const int vsw = swz(vrow);
-  const int voff_e = rowbase(vrow) + half * (kDC / 2) + 8 * (r16 & 1) + 16 * vsw;  // even nt
-  const int voff_o = rowbase(vrow) + half * (kDC / 2) + 8 * (r16 & 1) - 16 * vsw;  // odd nt
-  typedef __attribute__((address_space(3))) v2i_t lds_v2i;
-
-  f32x4 acc_o[NT_H];
-  float m_ref = -INFINITY;
-  float m_lane = -INFINITY;
-  float l_lane = 0.f;
-  for (int pass = 0; pass < 2; ++pass) {
-#pragma unroll
-    for (int nt = 0; nt < NT_H; ++nt) acc_o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    l_lane = 0.f;
-    if (pass == 1) m_ref = wave_max_xor16_32(m_lane);
-    bool over = false;
-    if (tid == 0) redo_flag = 0;
-
-    for (int64_t seg = p_begin; seg < p_end; seg += SEG) {
-      const int64_t seg_end = min(p_end, seg + SEG);
-      const int ntiles = (int)((seg_end - seg + kTile - 1) / kTile);
-      __syncthreads();
-      if (seg != built) {
-        int64_t t[2];
-        table_idx(seg, seg_end, t);
-        table_rows(t);
-        built = seg;
-      }
-      __syncthreads();
-      // Tiles 0 and 1 are staged and tile 2 is sent; iteration i stages tile
-      // i + 2 and sends tile i + 3.  Tile numbers past the last are clamped
-      // to it, so every iteration issues the same loads with no branch
-      // around them (the compiler can count them), and the surplus copies
-      // land in a buffer that no tile uses any more.
-      const int last = ntiles - 1;
-      auto tclamp = [&](int t) { return min(t, last) * kTile; };
-      issue(0, st);
-      stage(Kbuf[0], 0, st);
-      issue(tclamp(1), st);
-      stage(Kbuf[1], tclamp(1), st);
-      issue(tclamp(2), st);
-      __syncthreads();
-      f32x4 sc_own[2];
-      qk_partial(Kbuf[0], sc_own);
-#pragma unroll
-      for (int m = 0; m < 2; ++m) sx[0][wv][m][lane] = sc_own[m];
-      __syncthreads();
-      int cur = 0;
-      for (int i = 0; i < ntiles; ++i) {
-        const int nxt = cur == 2 ? 0 : cur + 1;
-        const uint8_t* Kt = Kbuf[cur];
-        const int tb = i * kTile;
-        f32x4 sc[2];
-#pragma unroll
-        for (int m = 0; m < 2; ++m) {
-          const f32x4 other = sx[i & 1][wv ^ 1][m][lane];
-          sc[m] = sc_own[m] + other;
-        }
-        qk_partial(Kbuf[nxt], sc_own);
-        f32x4 zsc[2], tsc[2], zb[2];
-#pragma unroll
-        for (int m = 0; m < 2; ++m) {
-          zsc[m] = *reinterpret_cast<const f32x4*>(seg_zsc + tb + m * 16 + g * 4);
-          tsc[m] = *reinterpret_cast<const f32x4*>(seg_tsc + tb + m * 16 + g * 4);
-          zb[m] = *reinterpret_cast<const f32x4*>(seg_bias + tb + m * 16 + g * 4);
-        }
-        float z[2][4];
-        float mx = -INFINITY;
-#pragma unroll
-        for (int m = 0; m < 2; ++m) {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            z[m][j] = __builtin_fmaf(sc[m][j], zsc[m][j], zb[m][j]);
-            mx = fmaxf(mx, z[m][j]);
-          }
-        }
-        m_lane = fmaxf(m_lane, mx);
-        if (__builtin_expect(__any(m_ref == -INFINITY), 0)) {
-          const float full = wave_max_xor16_32(mx);
-          if (m_ref == -INFINITY) m_ref = full;
-        }
-        over |= mx > m_ref + kHeadroom;
-        const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
-        float pv[2][4];
-#pragma unroll
-        for (int m = 0; m < 2; ++m) {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const float pp = __builtin_amdgcn_exp2f(z[m][j] - m_use);
-            l_lane += pp;
-            pv[m][j] = pp * tsc[m][j];
-          }
-        }
-        const bf16x8 pa = {(__bf16)pv[0][0], (__bf16)pv[0][1], (__bf16)pv[0][2], (__bf16)pv[0][3],
-                           (__bf16)pv[1][0], (__bf16)pv[1][1], (__bf16)pv[1][2], (__bf16)pv[1][3]};
-#pragma unroll
-        for (int nt = 0; nt < NT_H; ++nt) {
-          const v2i_t vr =
-              __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(Kt + ((nt & 1) ? voff_o : voff_e) + 16 * nt));
-          acc_o[nt] = OpBF16::mma(pa, widen8((uint32_t)vr[0], (uint32_t)vr[1]), acc_o[nt]);
-        }
-#pragma unroll
-        for (int m = 0; m < 2; ++m) sx[(i + 1) & 1][wv][m][lane] = sc_own[m];
-        stage(Kbuf[nxt == 2 ? 0 : nxt + 1], tclamp(i + 2), st);
-        issue(tclamp(i + 3), st);
-        __syncthreads();
-        cur = nxt;
-      }
-    }
-    if (__any(over) && lane == 0) atomicOr(&redo_flag, 1);
-    __syncthreads();
-    const bool redo = redo_flag != 0;
-    __syncthreads();
-    if (!redo) break;
-  }
-
-  if (!wave_active) return;
-  const bool bad = bad_flag != 0;
-  const float l_run = wave_sum_xor16_32(l_lane);
-  float inv_l[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const float li = __shfl(l_run, g * 4 + j);
-    inv_l[j] = bad ? kNaN : (li > 0.f ? 1.f / li : 0.f);
-  }
-#pragma unroll
-  for (int nt = 0; nt < NT_H; ++nt) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int h = head0 + g * 4 + j;
-      if (h < n_heads) *out_o(h, half * (kDC / 2) + nt * 16 + r16) = acc_o[nt][j] * inv_l[j];
-    }
-  }
-  if (half == 0 && g == 0 && head0 + r16 < n_heads) {
-    float lse = l_run > 0.f ? (m_ref + log2f(l_run)) * 0.69314718055994530942f : -INFINITY;
-    if (bad) lse = kNaN;
-    *out_lse(head0 + r16) = lse;
-  }
-}
-
 template <class Op, int KDT, int KSTEPS, int NT>
 static int launch_one(const DecodeArgs& a, hipStream_t stream) {
   int page_shift = 0;
@@ -921,26 +460,6 @@ static int launch_one(const DecodeArgs& a, hipStream_t stream) {
                      a.q, reinterpret_cast<const uint8_t*>(a.kv), a.kv_scale, a.num_pages, page_shift, a.bt,
                      a.bt_stride, a.lens, a.max_len, a.indices, a.k, a.n_heads, sm_log2, a.num_splits, n_hg,
                      a.o_part, a.lse_part, a.status);
-  return hipGetLastError() == hipSuccess ? 0 : -3;
-}
-
-#ifndef SPMLA_F8_WAVES
-#define SPMLA_F8_WAVES 8
-#endif
-static int launch_f8(const DecodeArgs& a, hipStream_t stream) {
-  constexpr int NW = SPMLA_F8_WAVES;
-  constexpr int HPW = NW / 2 * kHeadsPerWave;
-  int page_shift = 0;
-  while ((1 << page_shift) < a.page_size) ++page_shift;
-  const int n_hg = (a.n_heads + HPW - 1) / HPW;
-  const int64_t grid = (int64_t)a.batch * a.num_splits * n_hg;
-  if (grid == 0) return 0;
-  if (grid > 0x7FFFFFFF) return -2;
-  const float sm_log2 = a.sm_scale * 1.44269504088896340736f;
-  hipLaunchKernelGGL(mla_decode_f8_kernel<NW>, dim3((unsigned)grid), dim3(NW * 64), 0, stream,
-                     reinterpret_cast<const __bf16*>(a.q), reinterpret_cast<const uint8_t*>(a.kv), a.kv_scale,
-                     a.num_pages, page_shift, a.bt, a.bt_stride, a.lens, a.max_len, a.indices, a.k, a.n_heads,
-                     sm_log2, a.num_splits, n_hg, a.o_part, a.lse_part, a.status);
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 

@@ -78,6 +78,7 @@ static_assert(kLoads * (kPF - 1) <= 63, "vmcnt range");
 typedef int v8i_t __attribute__((ext_vector_type(8)));
 typedef int v2i_t __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) v2i_t lds_v2i;
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -124,11 +125,16 @@ __device__ __forceinline__ void wg_barrier() {
 // flight); the waits are the explicit vm_wait calls.  An asm load issued
 // before one of the compiler's own loads only makes the compiler's count
 // for that load conservative, since loads complete in order.
+// (An SALU write of M0 needs one wait state before an instruction that
+// reads it for an LDS address; the compiler inserts no hazard padding inside
+// asm, hence the s_nop.)  No memory clobber: the buffer a load fills is never
+// the one being read in the same phase, and the waits and barriers around
+// the loads carry the clobbers that order them.
 __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds) : "memory", "m0");
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds) : "m0");
 }
 __device__ __forceinline__ void dma4(const void* gptr, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(gptr), "s"(lds) : "memory", "m0");
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(gptr), "s"(lds) : "m0");
 }
 template <class T>
 __device__ __forceinline__ uint32_t lds_addr(T* p) {
@@ -141,47 +147,41 @@ __device__ __forceinline__ int xcd_remap(int bid, int n) {
   return xcd < r ? xcd * (q + 1) + slot : r * (q + 1) + (xcd - r) * q + slot;
 }
 
-// Writes this lane's 32 values v (bf16 values held in fp32) as
-// v = 2^(E-7) * (hi + lo/16), hi and lo e4m3 codes, where E = floor(log2 M)
-// and M is the largest |v| over the four lanes of the row (lanes l, l^16,
-// l^32, l^48: the 128 k-slots of one MFMA row), so one scale per row and
-// term serves the block.  hi is v scaled below 256 and rounded to 4
-// significant bits; the remainder of an element within 2^14 of M is a
+// Writes this lane's 32 bf16 values (w[i] holds values 2i, low half, and
+// 2i + 1) as v = 2^(E-7) * (hi + lo/16), hi and lo e4m3 codes, where
+// E = floor(log2 M) and M is the largest |v| over the four lanes of the row
+// (lanes l, l^16, l^32, l^48: the 128 k-slots of one MFMA row), so one scale
+// per row and term serves the block.  hi is v scaled below 256 and rounded
+// to 4 significant bits; the remainder of an element within 2^14 of M is a
 // multiple of its last bf16 bit below half an e4m3 step, so 16 times it is
 // an e4m3 value and the sum is exact; a smaller element keeps an error below
 // 2^-22 of M.  A non-finite element turns the hi codes of its lane into NaN,
-// so the scores it feeds come out NaN.  Call with the whole wave active.
-__device__ __forceinline__ void split_q32(const float* v, v8i_t& hi, v8i_t& lo, int& shi, int& slo) {
-  float amax = 0.f;
-  bool bad = false;
+// so the scores it feeds come out NaN.  Magnitudes are compared as bf16
+// bits: without the sign, finite values order as integers and Inf and NaN
+// lie above them.  Call with the whole wave active.
+__device__ __forceinline__ void split_q32(const uint32_t (&w)[16], v8i_t& hi, v8i_t& lo, int& shi, int& slo) {
+  u16x2 m = {0, 0};
 #pragma unroll
-  for (int j = 0; j < 32; ++j) {
-    const float a = fabsf(v[j]);
-    bad |= !(a <= 3.402823466e38f);
-    amax = fmaxf(amax, a);
-  }
-  amax = fmaxf(amax, __shfl_xor(amax, 16));
-  amax = fmaxf(amax, __shfl_xor(amax, 32));
-  int E = (int)((__float_as_uint(amax) >> 23) & 0xFF) - 127;
-  E = max(E, -115);
+  for (int i = 0; i < 16; ++i) m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, w[i] & 0x7FFF7FFFu));
+  uint32_t mb = max((uint32_t)m[0], (uint32_t)m[1]);
+  const bool bad = mb >= 0x7F80u;
+  mb = max(mb, (uint32_t)__shfl_xor((int)mb, 16));
+  mb = max(mb, (uint32_t)__shfl_xor((int)mb, 32));
+  const int E = max((int)(mb >> 7) - 127, -115);
   const float mul = __uint_as_float((uint32_t)(134 - E) << 23);  // 2^(7 - E)
   shi = E + 120;
   slo = E + 116;
 #pragma unroll
-  for (int w = 0; w < 8; ++w) {
-    __builtin_amdgcn_sched_barrier(0);  // four elements at a time: few temporaries beside the outputs
-    int h = 0, l = 0;
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      const float x0 = v[4 * w + 2 * p] * mul, x1 = v[4 * w + 2 * p + 1] * mul;
-      const int hp = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
-      const f32x2 d = __builtin_amdgcn_cvt_pk_f32_fp8(hp, false);
-      const int lp = __builtin_amdgcn_cvt_pk_fp8_f32((x0 - d[0]) * 16.f, (x1 - d[1]) * 16.f, 0, false);
-      h |= (hp & 0xFFFF) << (16 * p);
-      l |= (lp & 0xFFFF) << (16 * p);
-    }
-    hi[w] = bad ? 0x7F7F7F7F : h;
-    lo[w] = l;
+  for (int d = 0; d < 8; ++d) {
+    const float x0 = __uint_as_float(w[2 * d] << 16) * mul, x1 = __uint_as_float(w[2 * d] & 0xFFFF0000u) * mul;
+    const float x2 = __uint_as_float(w[2 * d + 1] << 16) * mul, x3 = __uint_as_float(w[2 * d + 1] & 0xFFFF0000u) * mul;
+    int h = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
+    h = __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, h, true);
+    const f32x2 r01 = __builtin_amdgcn_cvt_pk_f32_fp8(h, false), r23 = __builtin_amdgcn_cvt_pk_f32_fp8(h, true);
+    int l = __builtin_amdgcn_cvt_pk_fp8_f32((x0 - r01[0]) * 16.f, (x1 - r01[1]) * 16.f, 0, false);
+    l = __builtin_amdgcn_cvt_pk_fp8_f32((x2 - r23[0]) * 16.f, (x3 - r23[1]) * 16.f, l, true);
+    hi[d] = bad ? 0x7F7F7F7F : h;
+    lo[d] = l;
   }
 }
 
@@ -207,7 +207,8 @@ __global__ __launch_bounds__(kThreads) void mla_decode_f8ws_kernel(
   __shared__ __attribute__((aligned(16))) float seg_bias[kSeg];         // 0, or -inf when masked
   __shared__ __attribute__((aligned(16))) __bf16 Pbuf[2][kHeadsWg * kPStride];
   __shared__ __attribute__((aligned(16))) float red[2][kHeadsWg];       // per token half: head maxima / sums
-  __shared__ __attribute__((aligned(16))) bf16x8 Qrope[2][2][2][64];    // [hq][nt][ks][lane]: rope dims of the query
+  __shared__ __attribute__((aligned(16))) bf16x8 Qrope[4][2][64];       // [head tile of 16][ks][lane]: rope dims
+  __shared__ __attribute__((aligned(16))) uint8_t Qsc[kHeadsWg][2][4];  // E8M0 scale per head, term and block
   __shared__ int redo_flag;
   __shared__ int bad_flag;
 
@@ -235,8 +236,82 @@ __global__ __launch_bounds__(kThreads) void mla_decode_f8ws_kernel(
   };
   auto out_lse = [&](int h) -> float* { return lse_part + (((int64_t)b * num_splits + s) * n_heads + h); };
 
+  // ---- value waves' share of each tile: row loads 4w'..4w'+3 and (w' <
+  // 3) 16 + w' of the tile's 19 (w' = role); wave 3's fifth load is the
+  // tile's scales.  Piece p of a load lands at slot p of the tile: row p /
+  // 38, chunk slot p % 38, which holds chunk (p % 38) ^ swz(row) of the row
+  // (the two spare slots repeat chunk 35).
+  int ld_off[kLoads];
+#pragma unroll
+  for (int u = 0; u < kLoads; ++u) {
+    const int ld = u < 4 ? 4 * role + u : 16 + role;
+    const int slot = 64 * ld + lane;
+    const int r = min(slot / kRowChunks, kTileTok - 1);
+    const int c = min((slot % kRowChunks) ^ swz(r), kD / 16 - 1);
+    ld_off[u] = (r << 8) | c;
+  }
+  // Tile row of this lane's piece of load u (the scale load: row lane % 32).
+  auto piece_row = [&](int u) { return (u < 4 || role < 3) ? ld_off[u] >> 8 : lane & 31; };
+
+  // ---- first loads.  The split positions of a sparse call depend on k
+  // alone, so the index loads for the first segment's table (and for the
+  // value waves' pieces of tiles 0 and 1) go out before anything else.  A
+  // dense call, or one with k = 0, reads the request's length there instead
+  // and does not use it.
+  const int32_t* btb = bt + (int64_t)b * bt_stride;
+  const bool sparse = indices != nullptr;
+  constexpr int kNT = kSeg / kThreads;   // table entries per thread
+  constexpr int kNP = kNT + 2 * kLoads;  // and the value waves' pieces of tiles 0 and 1
+  auto split_len = [&](int64_t n) { return ((n + num_splits - 1) / num_splits + kTileTok - 1) / kTileTok * kTileTok; };
+  auto pos_at = [&](int64_t p0, int i) -> int64_t {
+    if (i < kNT) return p0 + tid + i * kThreads;
+    return p0 + ((i - kNT) / kLoads) * kTileTok + piece_row((i - kNT) % kLoads);
+  };
+  int32_t iv[kNP];
+  {
+    const bool early = sparse && k > 0;
+    const int64_t p0 = (int64_t)s * split_len(k);
+    const int32_t* ib = early ? indices + (int64_t)b * k : lens + b;
+#pragma unroll
+    for (int i = 0; i < kNP; ++i) iv[i] = ib[early ? min(pos_at(p0, i), (int64_t)k - 1) : 0];
+  }
+
+  // ---- the query of the group's 64 heads is staged in LDS next (it
+  // depends on nothing): tile buffers 0..3, free until those buffers are
+  // first requested.  Layout: the latent dims as [half][head][32 chunks of
+  // 16 bytes] (half hv = dims 256hv..256hv+255), then the rope dims as
+  // [head][8 chunks]; chunk c of head h sits at slot c ^ (h % 16) (rope:
+  // c ^ (h % 8)), so that the 16 heads a lane group reads at once fall on
+  // distinct LDS banks.  Wave w stages half w / 4 of heads 16(w % 4)..
+  // 16(w % 4)+15 (8 wave loads; waves 0..3 also their rope dims, 2 more), so
+  // the wave that converts them (below) needs no other wave's loads.  Heads
+  // past the last one stage head 0's query: their results are never stored.
+  constexpr int kQLat = 0, kQRope = 2 * kHeadsWg * 512;
+  constexpr int kQBufs = 4;  // tile t of a segment lives in buffer (t + kQBufs) % kNB
+  static_assert(kQRope + kHeadsWg * 128 <= kQBufs * kTileBytes && kNB - kQBufs >= 2,
+                "the staged query fits below the buffers of tiles 0 and 1");
+  {
+    const int hv = wv >> 2, hw = wv & 3;
+    const uint32_t qs_lds = lds_addr(&Kbuf[0][0]);
+    const __bf16* qb = q + (int64_t)b * n_heads * kD;
+    auto qrow = [&](int hl) { const int h = head_base + hl; return qb + (int64_t)(h < n_heads ? h : 0) * kD; };
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int p = 64 * u + lane, hh = p / 32;
+      dma16(qrow(16 * hw + hh) + 256 * hv + 8 * ((p % 32) ^ hh), qs_lds + kQLat + (hv * kHeadsWg + 16 * hw) * 512 + 1024 * u);
+    }
+    if (hv == 0) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int p = 64 * u + lane, hh = p / 8;
+        dma16(qrow(16 * hw + hh) + kDC + 8 * ((p % 8) ^ (hh & 7)), qs_lds + kQRope + 16 * hw * 128 + 1024 * u);
+      }
+    }
+  }
+
   const int32_t L = lens[b];
   if (L < 0 || (int64_t)L > max_len || (int64_t)L > (int64_t)bt_stride * page_size) {
+    vm_wait<0>();  // the staged query is not needed, but the loads must land before the workgroup ends
     if (tid == 0 && status) atomicOr(status + b, kBadLen);
     for (int i = tid; i < kHeadsWg * kDC; i += kThreads) {
       const int h = head_base + i / kDC;
@@ -245,27 +320,52 @@ __global__ __launch_bounds__(kThreads) void mla_decode_f8ws_kernel(
     if (tid < kHeadsWg && head_base + tid < n_heads) *out_lse(head_base + tid) = kNaN;
     return;
   }
-  const int64_t n = indices ? (int64_t)k : (int64_t)L;
-  const int64_t per = ((n + num_splits - 1) / num_splits + kTileTok - 1) / kTileTok * kTileTok;
+  const int64_t n = sparse ? (int64_t)k : (int64_t)L;
+  const int64_t per = split_len(n);
   const int64_t p_begin = (int64_t)s * per;
   const int64_t p_end = min(n, p_begin + per);
-  const int32_t* btb = bt + (int64_t)b * bt_stride;
-  const int32_t* idxb = indices ? indices + (int64_t)b * k : nullptr;
+  const int32_t* idxb = sparse ? indices + (int64_t)b * k : nullptr;
+  const bool any_token = p_begin < p_end;
+  // Tokens at split positions and the pages of tokens, for the segments
+  // after the first: every load reads a clamped, always valid address, and
+  // its value passes through an empty asm before it is selected, so that
+  // the compiler cannot move the load into the branch of the select (a load
+  // under a branch is waited for inside it, one memory latency per load).
+  // Dense calls have no index array: they read the block table's first
+  // entry and do not use it.
+  const int32_t* idx_src = idxb ? idxb : btb;
+  auto tokens_at = [&](const auto& pos, int64_t seg_end, int64_t* out) {
+    constexpr int N = std::extent<std::remove_reference_t<decltype(pos)>>::value;
+    int32_t v[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] = idx_src[sparse ? min((int64_t)pos[i], n - 1) : 0];
+#pragma unroll
+    for (int i = 0; i < N; ++i) asm volatile("" : "+v"(v[i]));
+#pragma unroll
+    for (int i = 0; i < N; ++i) out[i] = pos[i] < seg_end ? (sparse ? (int64_t)v[i] : (int64_t)pos[i]) : -1;
+  };
+  auto pages_of = [&](const int64_t* t, int32_t* out, auto n_tag) {
+    constexpr int N = decltype(n_tag)::value;
+    int32_t v[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] = btb[(t[i] >= 0 && t[i] < L ? t[i] : 0) >> page_shift];
+#pragma unroll
+    for (int i = 0; i < N; ++i) asm volatile("" : "+v"(v[i]));
+#pragma unroll
+    for (int i = 0; i < N; ++i) out[i] = t[i] >= 0 && t[i] < L ? v[i] : -1;
+  };
   if (tid == 0) bad_flag = 0;
   wg_barrier();  // bad_flag is cleared before any table entry may set it
 
   // Resolve positions [seg, seg_end) of the split (index -> page -> row);
   // entries past seg_end are masked.
   auto build_table = [&](int64_t seg, int64_t seg_end) __attribute__((always_inline)) {
-    int64_t t[kSeg / kThreads];
+    int64_t pos[kSeg / kThreads], t[kSeg / kThreads];
 #pragma unroll
-    for (int u = 0; u < kSeg / kThreads; ++u) {
-      const int64_t p = seg + tid + u * kThreads;
-      t[u] = p < seg_end ? (idxb ? (int64_t)idxb[p] : p) : -1;
-    }
+    for (int u = 0; u < kSeg / kThreads; ++u) pos[u] = seg + tid + u * kThreads;
+    tokens_at(pos, seg_end, t);
     int32_t page[kSeg / kThreads];
-#pragma unroll
-    for (int u = 0; u < kSeg / kThreads; ++u) page[u] = (t[u] >= 0 && t[u] < L) ? btb[t[u] >> page_shift] : -1;
+    pages_of(t, page, std::integral_constant<int, kSeg / kThreads>{});
 #pragma unroll
     for (int u = 0; u < kSeg / kThreads; ++u) {
       int32_t row = -1;
@@ -284,87 +384,164 @@ __global__ __launch_bounds__(kThreads) void mla_decode_f8ws_kernel(
       seg_bias[tid + u * kThreads] = row >= 0 ? 0.f : -INFINITY;
     }
   };
-
-  // ---- the query of the group's 64 heads, staged in LDS (buffer space,
-  // free until the first tile is requested) by direct loads: 64 rows of
-  // 1152 bytes, 72 wave loads of 1 KiB, 9 per wave.  The score waves then
-  // hold heads head_base + 32hq + 16nt + r16 as two scaled FP8 terms per
-  // 128-dim latent block (lane group g holds dims 16g..16g+15 and
-  // 64+16g..64+16g+15 of a block, the k-slot order of the scaled MFMA) plus
-  // the rope dims in bf16 (dims 512 + 32ks + 8g..+7).  The E8M0 scales of
-  // the four blocks share one register per term, one byte each (selected
-  // per MFMA).  The rope part waits in LDS and is read per tile (registers
-  // are the score waves' scarce resource).
-  const bool any_token = p_begin < p_end;
-  if (any_token) {
-    const uint32_t qbase = lds_addr(&Kbuf[0][0]);
+  const uint8_t* zero_row = g_zero_row;
+  const float* unit_scale = g_unit_scale;
+  // Send this lane's loads of a tile whose pieces come from cache rows
+  // row[u] (-1: masked, the zero row) into buffer `buf`.
+  auto dma_rows = [&](const int32_t (&row)[kLoads], int buf) __attribute__((always_inline)) {
+    const uint32_t dst = lds_addr(&Kbuf[0][0]) + buf * kTileBytes;
 #pragma unroll
-    for (int u = 0; u < 9; ++u) {
-      const int ld = 9 * wv + u;
-      const int piece = 64 * ld + lane;
-      const int h = head_base + piece / 72;
-      const __bf16* src = q + ((int64_t)b * n_heads + (h < n_heads ? h : 0)) * kD + 8 * (piece % 72);
-      dma16(src, qbase + 1024 * ld);
+    for (int u = 0; u < kLoads; ++u) {
+      if (u < 4 || role < 3) {
+        const int ld = u < 4 ? 4 * role + u : 16 + role;
+        const int c = ld_off[u] & 255;
+        const uint8_t* src = row[u] >= 0 ? kv + ((int64_t)row[u] * (kD / 16) + c) * 16 : zero_row + 16 * c;
+        dma16(src, dst + 1024 * ld);
+      } else {
+        const float* src = row[u] >= 0 ? kv_scale + row[u] : unit_scale;
+        dma4(src, lds_addr(&Tsc[0][0]) + buf * 256);
+      }
     }
-  }
-  // The first segment's table is resolved while the query is in flight.
-  if (any_token) build_table(p_begin, min(p_end, p_begin + kSeg));
+  };
+
+  // ---- prologue: once the indices are in, the first segment's pages are
+  // requested, and while they load each wave rewrites its staged part of
+  // the query in place as two scaled FP8 terms per 128-dim latent block
+  // (lane (r16, g) converts blocks 2hv and 2hv + 1 of head 16(w % 4) + r16
+  // with the lane layout the score waves use, the 64 bytes it read becoming
+  // its 32 hi and 32 lo codes).  The value waves first resolve their pieces
+  // of tiles 0 and 1 and request those tiles.  The score waves then load the
+  // codes into registers.
+  if (!any_token) vm_wait<0>();  // nothing to score: just let the early loads land
   if (any_token) {
-    vm_wait<0>();
-    wg_barrier();  // the query and the first table are in LDS
+    const int hv = wv >> 2, hw = wv & 3;
+    uint8_t* const qs = &Kbuf[0][0];
+    const int64_t seg_end = min(p_end, p_begin + kSeg);
+    vm_wait<0>();  // the indices are in, this wave's part of the query is staged
+    int32_t t[kNP], pv[kNP];
+#pragma unroll
+    for (int i = 0; i < kNP; ++i) {
+      const int64_t p = pos_at(p_begin, i);
+      t[i] = p < seg_end ? (sparse ? iv[i] : (int32_t)p) : -1;
+      pv[i] = btb[(t[i] >= 0 && t[i] < L ? t[i] : 0) >> page_shift];
+    }
+    auto pages_in = [&]() __attribute__((always_inline)) {
+#pragma unroll
+      for (int i = 0; i < kNP; ++i) asm volatile("" : "+v"(pv[i]));
+    };
+    auto convert = [&]() __attribute__((always_inline)) {
+      const int hl = 16 * hw + r16;
+      // block bb: chunks 16bb + 2g, +1 (dims 128(2hv + bb) + 16g..+15) and
+      // 16bb + 8 + 2g, +1 (64 dims on); both blocks are read before either
+      // is written back
+      uint8_t* row = qs + kQLat + (hv * kHeadsWg + hl) * 512;
+      uint4* q4[2][4];
+      uint4 raw[2][4];
+#pragma unroll
+      for (int bb = 0; bb < 2; ++bb) {
+        const int c0 = 16 * bb + 2 * g;
+        q4[bb][0] = reinterpret_cast<uint4*>(row + 16 * (c0 ^ r16));
+        q4[bb][1] = reinterpret_cast<uint4*>(row + 16 * ((c0 + 1) ^ r16));
+        q4[bb][2] = reinterpret_cast<uint4*>(row + 16 * ((c0 + 8) ^ r16));
+        q4[bb][3] = reinterpret_cast<uint4*>(row + 16 * ((c0 + 9) ^ r16));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) raw[bb][j] = *q4[bb][j];
+      }
+#pragma unroll
+      for (int bb = 0; bb < 2; ++bb) {
+        const uint4* r = raw[bb];
+        const uint32_t w[16] = {r[0].x, r[0].y, r[0].z, r[0].w, r[1].x, r[1].y, r[1].z, r[1].w,
+                                r[2].x, r[2].y, r[2].z, r[2].w, r[3].x, r[3].y, r[3].z, r[3].w};
+        v8i_t hi, lo;
+        int shi, slo;
+        split_q32(w, hi, lo, shi, slo);
+        *q4[bb][0] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+        *q4[bb][1] = make_uint4(hi[4], hi[5], hi[6], hi[7]);
+        *q4[bb][2] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+        *q4[bb][3] = make_uint4(lo[4], lo[5], lo[6], lo[7]);
+        // the four lanes of a row hold the same scales
+        Qsc[hl][0][2 * hv + bb] = (uint8_t)shi;
+        Qsc[hl][1][2 * hv + bb] = (uint8_t)slo;
+      }
+      if (hv == 0) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const uint4 r = *reinterpret_cast<const uint4*>(qs + kQRope + hl * 128 + 16 * ((4 * ks + g) ^ (hl & 7)));
+          Qrope[hw][ks][lane] = __builtin_bit_cast(bf16x8, r);
+        }
+      }
+    };
+    if (score_wave) {
+      convert();
+      pages_in();
+    } else {
+      pages_in();
+      int32_t prow[2][kLoads];
+#pragma unroll
+      for (int tl = 0; tl < 2; ++tl) {
+#pragma unroll
+        for (int u = 0; u < kLoads; ++u) {
+          const int32_t tt = t[kNT + tl * kLoads + u], pp = pv[kNT + tl * kLoads + u];
+          prow[tl][u] = tt >= 0 && tt < L && pp >= 0 && pp < num_pages ? (int32_t)(((int64_t)pp << page_shift) + (tt & (page_size - 1))) : -1;
+        }
+      }
+      dma_rows(prow[0], kQBufs);
+      dma_rows(prow[1], kQBufs + 1);
+      convert();
+    }
+#pragma unroll
+    for (int u = 0; u < kNT; ++u) {
+      int32_t row = -1;
+      if (t[u] < -1 || t[u] >= L) {
+        bad_flag = 1;
+        if (status) atomicOr(status + b, kBadIndex);
+      } else if (t[u] >= 0) {
+        if (pv[u] < 0 || pv[u] >= num_pages) {
+          bad_flag = 1;
+          if (status) atomicOr(status + b, kBadPage);
+        } else {
+          row = (int32_t)(((int64_t)pv[u] << page_shift) + (t[u] & (page_size - 1)));
+        }
+      }
+      seg_row[tid + u * kThreads] = row;
+      seg_bias[tid + u * kThreads] = row >= 0 ? 0.f : -INFINITY;
+    }
+    wg_barrier();  // the query's FP8 terms and the first table are in LDS
   }
 
   int64_t built = any_token ? p_begin : -1;  // segment whose table is in LDS
-  // Both roles run the same sequence of barriers: per segment two around
-  // the table, one when tile 0 has landed, one more when the reference is
-  // set, one when tile 1 has landed, and one per tile; per pass one for the
-  // recompute decision (and one more when it recomputes); two to finish.
+  // Both roles run the same sequence of barriers.
   if (score_wave) {
     v8i_t qhi[2][4], qlo[2][4];
-    int qs_hi[2] = {0, 0}, qs_lo[2] = {0, 0};
+    uint32_t qs_hi[2] = {0, 0}, qs_lo[2] = {0, 0};
     if (any_token) {
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const int hl = hq * 32 + nt * 16 + r16;
-      const bool ok = head_base + hl < n_heads;
-      const uint8_t* qrow = &Kbuf[0][0] + hl * (2 * kD);
+      for (int nt = 0; nt < 2; ++nt) {
+        const int hl = hq * 32 + nt * 16 + r16;
 #pragma unroll
-      for (int blk = 0; blk < 4; ++blk) {
-        __builtin_amdgcn_sched_barrier(0);  // one block at a time: its temporaries die before the next
-        const uint4 raw[4] = {*reinterpret_cast<const uint4*>(qrow + 2 * (128 * blk + 16 * g)),
-                              *reinterpret_cast<const uint4*>(qrow + 2 * (128 * blk + 16 * g) + 16),
-                              *reinterpret_cast<const uint4*>(qrow + 2 * (128 * blk + 64 + 16 * g)),
-                              *reinterpret_cast<const uint4*>(qrow + 2 * (128 * blk + 64 + 16 * g) + 16)};
-        float v[32];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const uint32_t ws[4] = {raw[c].x, raw[c].y, raw[c].z, raw[c].w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            v[8 * c + 2 * e] = ok ? bf16_bits_to_f32(ws[e] & 0xFFFFu) : 0.f;
-            v[8 * c + 2 * e + 1] = ok ? bf16_bits_to_f32(ws[e] >> 16) : 0.f;
-          }
+        for (int blk = 0; blk < 4; ++blk) {
+          const uint8_t* row = &Kbuf[0][0] + kQLat + ((blk >> 1) * kHeadsWg + hl) * 512;
+          const int cb = 16 * (blk & 1) + 2 * g;  // hi codes in chunks cb, cb + 1; lo codes in cb + 8, cb + 9
+          const int hs = hl & 15;
+          const uint4 a0 = *reinterpret_cast<const uint4*>(row + 16 * (cb ^ hs));
+          const uint4 a1 = *reinterpret_cast<const uint4*>(row + 16 * ((cb + 1) ^ hs));
+          const uint4 c0 = *reinterpret_cast<const uint4*>(row + 16 * ((cb + 8) ^ hs));
+          const uint4 c1 = *reinterpret_cast<const uint4*>(row + 16 * ((cb + 9) ^ hs));
+          qhi[nt][blk] = v8i_t{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+          qlo[nt][blk] = v8i_t{(int)c0.x, (int)c0.y, (int)c0.z, (int)c0.w, (int)c1.x, (int)c1.y, (int)c1.z, (int)c1.w};
         }
-        int shi, slo;
-        split_q32(v, qhi[nt][blk], qlo[nt][blk], shi, slo);
-        qs_hi[nt] |= shi << (8 * blk);
-        qs_lo[nt] |= slo << (8 * blk);
+        qs_hi[nt] = *reinterpret_cast<const uint32_t*>(&Qsc[hl][0][0]);
+        qs_lo[nt] = *reinterpret_cast<const uint32_t*>(&Qsc[hl][1][0]);
       }
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const uint4 r = *reinterpret_cast<const uint4*>(qrow + 2 * (kDC + 32 * ks + 8 * g));
-        Qrope[hq][nt][ks][lane] = ok ? __builtin_bit_cast(bf16x8, r) : zero_frag<OpBF16>();
-      }
+      wg_barrier();  // buffers 0..3 are free for tiles
     }
-    __builtin_amdgcn_sched_barrier(0);
-      wg_barrier();  // the buffers are free for tiles
-    }
-    // ---- score waves: scores of the tile in Kt for this wave's 16 tokens
-    // (rows 16th + r16 on M) and its 32 heads (two N-tiles): S[nt] holds head
-    // 16nt + r16 for tokens 16th + 4g + j.
+
+    // Scores of the tile in Kt for this wave's 16 tokens (rows 16th + r16 on
+    // M) and its 32 heads (two N-tiles): S[nt] holds head 16nt + r16 for
+    // tokens 16th + 4g + j.
     auto score_tile = [&](const uint8_t* __restrict__ Kt, f32x4 (&S)[2]) __attribute__((always_inline)) {
       f32x4 acc[2][2];
-  #pragma unroll
+#pragma unroll
       for (int nt = 0; nt < 2; ++nt) acc[nt][0] = acc[nt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
       const int row = th * 16 + r16;
       const int sw = swz(row);
@@ -374,22 +551,22 @@ __global__ __launch_bounds__(kThreads) void mla_decode_f8ws_kernel(
         const uint4 k0 = *reinterpret_cast<const uint4*>(rp + 16 * ((8 * blk + g) ^ sw));
         const uint4 k1 = *reinterpret_cast<const uint4*>(rp + 16 * ((8 * blk + 4 + g) ^ sw));
         const v8i_t a = {(int)k0.x, (int)k0.y, (int)k0.z, (int)k0.w, (int)k1.x, (int)k1.y, (int)k1.z, (int)k1.w};
-  #pragma unroll
+#pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
           acc[nt][0] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, qhi[nt][blk], acc[nt][0], 0, 0, 0, 127,
-                                                                        blk, qs_hi[nt]);
+                                                                        blk, (int)qs_hi[nt]);
           acc[nt][1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, qlo[nt][blk], acc[nt][1], 0, 0, 0, 127,
-                                                                        blk, qs_lo[nt]);
+                                                                        blk, (int)qs_lo[nt]);
         }
       });
-  #pragma unroll
+#pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         const uint2 kr = *reinterpret_cast<const uint2*>(rp + 16 * ((32 + 2 * ks + (g >> 1)) ^ sw) + 8 * (g & 1));
         const bf16x8 kb = widen8(kr.x, kr.y);
-  #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) acc[nt][1] = OpBF16::mma(kb, Qrope[hq][nt][ks][lane], acc[nt][1]);
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) acc[nt][1] = OpBF16::mma(kb, Qrope[2 * hq + nt][ks][lane], acc[nt][1]);
       }
-  #pragma unroll
+#pragma unroll
       for (int nt = 0; nt < 2; ++nt) S[nt] = acc[nt][0] + acc[nt][1];
     };
 
@@ -397,7 +574,8 @@ __global__ __launch_bounds__(kThreads) void mla_decode_f8ws_kernel(
     float m_lane[2] = {-INFINITY, -INFINITY};  // this lane's largest logit
     float l_lane[2] = {0.f, 0.f};              // this lane's sum of weights
     bool fallback = false;                     // the first tile had no valid token: 0 stood in for m_ref
-    // Softmax weights of a scored tile, written to P as bf16.
+    // Softmax weights of a scored tile, written to P as bf16 (times each
+    // token's FP8 scale, which the value contraction needs).
     auto softmax_tile = [&](const f32x4 (&S)[2], int buf, int tb, __bf16* __restrict__ P, bool& over)
         __attribute__((always_inline)) {
       const int t0 = th * 16 + 4 * g;
@@ -425,6 +603,7 @@ __global__ __launch_bounds__(kThreads) void mla_decode_f8ws_kernel(
         *reinterpret_cast<bf16x4_t*>(P + (hq * 32 + nt * 16 + r16) * kPStride + t0) = w4;
       }
     };
+
     for (int pass = 0; pass < 2; ++pass) {
       l_lane[0] = l_lane[1] = 0.f;
       bool over = false;
@@ -441,10 +620,10 @@ __global__ __launch_bounds__(kThreads) void mla_decode_f8ws_kernel(
         }
         wg_barrier();  // tile 0 has landed
         f32x4 S[2];
-        score_tile(Kbuf[0], S);
+        score_tile(Kbuf[kQBufs], S);
         if (need_ref) {
           const int t0 = th * 16 + 4 * g;
-          const f32x4 ts = *reinterpret_cast<const f32x4*>(&Tsc[0][t0]);
+          const f32x4 ts = *reinterpret_cast<const f32x4*>(&Tsc[kQBufs][t0]);
           const f32x4 bi = *reinterpret_cast<const f32x4*>(&seg_bias[t0]);
 #pragma unroll
           for (int nt = 0; nt < 2; ++nt) {
@@ -468,9 +647,9 @@ __global__ __launch_bounds__(kThreads) void mla_decode_f8ws_kernel(
             }
           }
         }
-        softmax_tile(S, 0, 0, Pbuf[0], over);
+        softmax_tile(S, kQBufs, 0, Pbuf[0], over);
         wg_barrier();  // tile 1 has landed; P of tile 0 is written
-        int buf = 1;
+        int buf = kQBufs + 1;  // buffer of tile i
         for (int i = 1; i <= T; ++i) {
           if (i < T) {
             score_tile(Kbuf[buf], S);
@@ -522,82 +701,64 @@ __global__ __launch_bounds__(kThreads) void mla_decode_f8ws_kernel(
       }
     }
   } else {
-    if (any_token) wg_barrier();  // the score waves have the query: the buffers are free for tiles
-    // ---- value waves: the 16-byte piece of each tile this lane loads.  Row
-    // loads 4w'..4w'+3 and (w' < 3) 16 + w' of the tile's 19 (w' = role);
-    // wave 3's fifth load is the tile's scales.  Piece p of a load lands at
-    // slot p of the tile: row p / 38, chunk slot p % 38, which holds chunk
-    // (p % 38) ^ swz(row) of the row (the two spare slots repeat chunk 35).
-    int ld_off[kLoads];
-  #pragma unroll
-    for (int u = 0; u < kLoads; ++u) {
-      const int ld = u < 4 ? 4 * role + u : 16 + role;
-      const int slot = 64 * ld + lane;
-      const int r = min(slot / kRowChunks, kTileTok - 1);
-      const int c = min((slot % kRowChunks) ^ swz(r), kD / 16 - 1);
-      ld_off[u] = (r << 8) | c;
-    }
-    const uint8_t* zero_row = g_zero_row;
-    const float* unit_scale = g_unit_scale;
-    // Send the loads of tile `tile` of the segment (T tiles) into buffer
-    // `buf`; a tile past the segment's end loads the zero row into a buffer
-    // no tile uses, so every call issues exactly kLoads loads.
+    // ---- value waves.  Send the loads of tile `tile` of the segment (T
+    // tiles) into buffer `buf`; a tile past the segment's end loads the zero
+    // row into a buffer no tile uses, so every call issues exactly kLoads
+    // loads.
     auto issue_tile = [&](int tile, int T, int buf) __attribute__((always_inline)) {
       const bool real = tile < T;
       const int32_t* rows = seg_row + min(tile, T - 1) * kTileTok;
-      const uint32_t dst = lds_addr(&Kbuf[0][0]) + buf * kTileBytes;
-  #pragma unroll
-      for (int u = 0; u < kLoads; ++u) {
-        if (u < 4 || role < 3) {
-          const int ld = u < 4 ? 4 * role + u : 16 + role;
-          const int c = ld_off[u] & 255;
-          const int32_t row = real ? rows[ld_off[u] >> 8] : -1;
-          const uint8_t* src = row >= 0 ? kv + ((int64_t)row * (kD / 16) + c) * 16 : zero_row + 16 * c;
-          dma16(src, dst + 1024 * ld);
-        } else {
-          const int32_t row = real ? rows[lane & 31] : -1;
-          const float* src = row >= 0 ? kv_scale + row : unit_scale;
-          dma4(src, lds_addr(&Tsc[0][0]) + buf * 256);
-        }
-      }
+      int32_t row[kLoads];  // all table reads first, so that one LDS wait covers them
+#pragma unroll
+      for (int u = 0; u < kLoads; ++u) row[u] = real ? rows[piece_row(u)] : -1;
+      dma_rows(row, buf);
     };
-
-    // ---- value waves: O += P . V for the tile in Vt with the weights in P.
-    // A operand (P): lane l holds head l % 32, tokens 16ks + 8(l / 32) + e.
-    // B operand (V): the transposing read hands lane i of each 16-lane group
-    // G the dim 16(G & 1) + i of the N-tile for tokens 16ks + 8(G >> 1) + e,
-    // e < 8, when lane j of the group points at 8 dims (8(j & 1)..) of token
-    // row 16ks + 8(G >> 1) + j / 2.
+    // O += P . V for the tile in Vt with the weights in P.  A operand (P):
+    // lane l holds head l % 32, tokens 16ks + 8(l / 32) + e.  B operand (V):
+    // the transposing read hands lane i of each 16-lane group G the dim
+    // 16(G & 1) + i of the N-tile for tokens 16ks + 8(G >> 1) + e, e < 8,
+    // when lane j of the group points at 8 dims (8(j & 1)..) of token row
+    // 16ks + 8(G >> 1) + j / 2.
     auto pv_tile = [&](const uint8_t* __restrict__ Vt, const __bf16* __restrict__ P, f32x16 (&acc_o)[8])
         __attribute__((always_inline)) {
       const int G = lane >> 4, j = lane & 15;
-  #pragma unroll
+      // All LDS reads of the tile are issued before the first MFMA (20
+      // registers of codes), so the MFMAs wait for them once instead of one
+      // read latency each.
+      bf16x8 pa[2];
+      v2i_t raw[2][8];
+#pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const bf16x8 pa = *reinterpret_cast<const bf16x8*>(P + (hq * 32 + (lane & 31)) * kPStride + 16 * ks +
-                                                           8 * (lane >> 5));
+        pa[ks] = *reinterpret_cast<const bf16x8*>(P + (hq * 32 + (lane & 31)) * kPStride + 16 * ks + 8 * (lane >> 5));
         const int tr = 16 * ks + 8 * (G >> 1) + (j >> 1);
         const int sw = swz(tr);
         const uint8_t* vrow = Vt + tr * kRS + 8 * (j & 1);
-  #pragma unroll
+#pragma unroll
         for (int nt = 0; nt < 8; ++nt) {
           const int chunk = 16 * dh + 2 * nt + (G & 1);
-          const v2i_t raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(vrow + 16 * (chunk ^ sw)));
-          acc_o[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, widen8((uint32_t)raw[0], (uint32_t)raw[1]),
-                                                              acc_o[nt], 0, 0, 0);
+          raw[ks][nt] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(vrow + 16 * (chunk ^ sw)));
         }
       }
-      // Keep each V fragment's read two MFMAs ahead of its use rather than
-      // all sixteen up front (which needs ~100 registers beside the 128 of
-      // the accumulators).
-      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
-      static_for<15>([&](auto) {
-        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      });
-      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      // Four groups of four independent MFMAs in this order (left to itself
+      // the scheduler interleaves each read with its MFMA, one LDS latency
+      // per MFMA).
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+        for (int h4 = 0; h4 < 2; ++h4) {
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int nt = 4 * h4; nt < 4 * h4 + 4; ++nt)
+            acc_o[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                pa[ks], widen8((uint32_t)raw[ks][nt][0], (uint32_t)raw[ks][nt][1]), acc_o[nt], 0, 0, 0);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
     };
+
+    // (Tiles 0 and 1 went to buffers 4 and 5 with the query.)
+    if (any_token) wg_barrier();  // the score waves hold the query: buffers 0..3 are free for tiles
+
     f32x16 acc_o[8];
     for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
@@ -612,18 +773,23 @@ __global__ __launch_bounds__(kThreads) void mla_decode_f8ws_kernel(
           built = seg;
           wg_barrier();
         }
+        // Tiles 0 and 1 of the split's first segment were requested with
+        // the query; the others are requested here.
+        const int pre = need_ref ? 2 : 0;
 #pragma unroll
-        for (int i = 0; i < kPF; ++i) issue_tile(i, T, i);
+        for (int i = 0; i < kPF; ++i)
+          if (i >= pre) issue_tile(i, T, (i + kQBufs) % kNB);
         vm_wait<kLoads * (kPF - 1)>();  // tile 0 has landed
         wg_barrier();
         if (need_ref) wg_barrier();
-        issue_tile(kPF, T, kPF);
+        issue_tile(kPF, T, (kPF + kQBufs) % kNB);
         vm_wait<kLoads * (kPF - 1)>();  // tile 1 has landed
         wg_barrier();
-        int buf_in = kPF + 1, buf_pv = 0;  // buffers of tiles i + kPF and i - 1
+        int buf_in = (kPF + 1 + kQBufs) % kNB, buf_pv = kQBufs;  // buffers of tiles i + kPF and i - 1
         for (int i = 1; i <= T; ++i) {
           issue_tile(i + kPF, T, buf_in);
           pv_tile(Kbuf[buf_pv], Pbuf[(i - 1) & 1], acc_o);
+          __builtin_amdgcn_sched_barrier(0);  // the wait stays after this tile's MFMAs
           vm_wait<kLoads * (kPF - 1)>();  // tile i + 1 has landed
           buf_in = buf_in == kNB - 1 ? 0 : buf_in + 1;
           buf_pv = buf_pv == kNB - 1 ? 0 : buf_pv + 1;
