@@ -6,34 +6,38 @@
 // entries under (key desc, index asc), a total order, so the result is unique
 // whatever order atomics land in.
 //
-// Launches per call (all on the caller's stream):
-//  1. tau: one workgroup per request derives its threshold key tau from a
-//     sample of its keys (all of them when the request has at most 4096,
-//     else 16 evenly spread runs of 256):
-//     one histogram of the sample over the 11 bits below the bits its keys
-//     share, and tau the lower edge of the bin holding the sample key of
-//     rank r: k when the sample is the whole request, else e + 4 sqrt(e) + 4
-//     where e = k * 4096 / L is the expected count of sampled keys at or
-//     above the request's k-th largest key, so somewhat more than k keys of
-//     the request reach tau (fewer only if the sample count falls four
-//     deviations short).
-//  2. collect: (request, 4096-key chunk) workgroups.  Each copies its
-//     chunk's keys >= tau, with their indices and in token order, to the
-//     chunk's own slice of the candidate buffer, and writes their count and
-//     smallest and largest key (no atomics, so nothing needs clearing
+// Launches per call (both on the caller's stream):
+//  1. collect: (request, 8192-key chunk) workgroups.  Each requests its
+//     chunk's keys first (a row holds max_len entries, so the loads need not
+//     wait for the request's length), then derives the request's threshold
+//     key tau from a sample of its keys (all of them when the request has at
+//     most 4096, else 16 evenly spread runs of 256): one histogram of the
+//     sample over the 11 bits below the bits its keys share, and tau the
+//     lower edge of the bin holding the sample key of rank r: k when the
+//     sample is the whole request, else e + 4 sqrt(e) + 4 where
+//     e = k * 4096 / L is the expected count of sampled keys at or above the
+//     request's k-th largest key, so somewhat more than k keys of the
+//     request reach tau (fewer only if the sample count falls four
+//     deviations short).  Every chunk of a request draws the same sample, so
+//     all of them find the same tau.  The chunk's keys >= tau go, with their
+//     indices and in token order, to its own slice of the candidate buffer
+//     (at most kTkSlice of them), and their count and smallest and largest
+//     key to its metadata slot (no atomics, so nothing needs clearing
 //     between calls).
-//  3. finish: one workgroup per request gathers the chunks' candidates into
-//     LDS (still in token order) and selects the k_eff best exactly: 11-bit
-//     rounds over the key from the highest bit in which the candidates
-//     differ; once the bin holding the k-th best key has at most 64 keys,
-//     one wave ranks them by (key, index) and the k-th best fixes the
-//     threshold; otherwise the rounds go on and ties are split by rounds
-//     over the index.  The selected indices are written in ascending order
-//     by one block scan over the token-ordered candidates.  Should tau admit
-//     fewer than k keys (the sample fell far short: vanishingly rare for any
-//     spread of scores, but adversarial orders can do it), or more than fit
-//     in LDS (huge tie groups), the same steps run over the whole request
-//     read from the scores, so the result is exact in every case.
+//  2. finish: one workgroup per request gathers the chunks' candidates into
+//     LDS (still in token order; every thread finds the chunk of each of
+//     its list positions by binary search, so all the loads are in flight
+//     at once) and selects the k_eff best exactly: 11-bit rounds over the
+//     key from the highest bit in which the candidates differ; once the bin
+//     holding the k-th best key has at most 64 keys, one wave ranks them by
+//     (key, index) and the k-th best fixes the threshold; otherwise the
+//     rounds go on and ties are split by rounds over the index.  The
+//     selected indices are written in ascending order by one block scan over
+//     the token-ordered candidates.  Should tau admit fewer than k keys (the
+//     sample fell far short: vanishingly rare for any spread of scores, but
+//     adversarial orders can do it), more than a chunk's slice holds or more
+//     than fit in LDS (huge tie groups), the same steps run over the whole
+//     request read from the scores, so the result is exact in every case.
 //
 // Rows of at most 64K keys (max_len), 16-byte aligned, take one launch
 // instead (topk_fused_kernel): one workgroup per request does all three
@@ -44,33 +48,37 @@
 #include "topk_layout.h"
 
 #include <algorithm>
+#include <atomic>
+#include <chrono>
+#include <random>
 
 namespace spmla {
 
 constexpr int kBins = 2048;
 constexpr int kFinThreads = 1024;
-constexpr int kTauThreads = 1024;                // 4 sample keys per thread
 constexpr int kMaxK = 4096;
 constexpr int kSampleRuns = 16, kSampleRun = 256;
 constexpr int kSample = kSampleRuns * kSampleRun;  // keys sampled from a long request
 constexpr int kFinLdsWords = 32768;              // 128 KiB of gathered candidates
 constexpr int kCandLds = kFinLdsWords / 2;       // candidates that fit in LDS (uint2 each)
-static_assert(kSample == kTkChunk, "a collect workgroup holds one sample key per chunk key");
+static_assert(kCandLds % kFinThreads == 0, "the gather gives every thread the same number of list positions");
 
 struct TopkWs {
-  uint32_t* tau;    // [B] threshold key of each request longer than k
-  uint4* meta;      // [B, chunks] (candidate count, smallest key, largest key, 0) of each chunk
-  uint2* cand;      // [B, chunks, kTkChunk] (key, index), chunk c's in its own slice, ascending index
+  unsigned long long* tau_pub;  // [B] (call tag << 32) | threshold key, published by the request's tau block
+  uint4* meta;      // [B, chunks] (candidate count, threshold key used, largest key, 0) of each chunk
+  uint2* cand;      // [B, chunks, kTkSlice] (score bits, index), chunk c's in its own slice, ascending index
   int32_t chunks;
+  uint32_t tag;     // differs from call to call (see launch_topk)
 };
 
-static TopkWs carve(void* ws, int32_t batch, int64_t max_len) {
+static TopkWs carve(void* ws, int32_t batch, int64_t max_len, uint32_t tag) {
   TopkWs w;
   uint8_t* p = reinterpret_cast<uint8_t*>(ws);
   w.chunks = n_chunks(max_len);
+  w.tag = tag;
   const size_t bc = (size_t)batch * (size_t)w.chunks;
-  w.tau = reinterpret_cast<uint32_t*>(p);
-  p += align_up((size_t)batch * 4, 256);
+  w.tau_pub = reinterpret_cast<unsigned long long*>(p);
+  p += align_up((size_t)batch * 8, 256);
   w.meta = reinterpret_cast<uint4*>(p);
   w.cand = reinterpret_cast<uint2*>(p + align_up(bc * 16, 256));
   return w;
@@ -83,6 +91,16 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// The smallest float whose key is at least `key` (key >= 1): every number
+// when key is at most that of -inf, none (NaN) when it exceeds that of +inf.
+// For such a key and every float f, order_key(f) >= key exactly when
+// f >= key_floor(key) (NaN fails both).
+__device__ __forceinline__ float key_floor(uint32_t key) {
+  if (key <= 0x007FFFFFu) return -INFINITY;
+  if (key > 0xFF800000u) return __uint_as_float(0x7FC00000u);
+  return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
+}
+
 __device__ __forceinline__ bool len_ok(int32_t L, int64_t max_len) { return L >= 0 && (int64_t)L <= max_len; }
 
 __device__ __forceinline__ int xcd_remap(int bid, int n) {
@@ -92,23 +110,41 @@ __device__ __forceinline__ int xcd_remap(int bid, int n) {
 }
 
 // Block scan helpers (any block size that is a multiple of 64).
+// Inclusive scan over the wave with DPP moves: shifts right by 1, 2, 4 and 8
+// lanes within each row of 16 (lanes shifted in from outside the row read
+// 0), then the last lane of row 0 added to row 1 and that of row 2 to row 3
+// (row_bcast:15), then the last lane of row 1 added to rows 2 and 3
+// (row_bcast:31).
 __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
-  const int lane = threadIdx.x & 63;
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t t = (uint32_t)__shfl_up((int)v, o);
-    if (lane >= o) v += t;
-  }
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, true);  // row_shr:1
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, true);  // row_shr:2
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, true);  // row_shr:4
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, true);  // row_shr:8
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false);  // row_bcast:15, rows 1 and 3
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false);  // row_bcast:31, rows 2 and 3
   return v;
 }
-// Inclusive block scan; `tmp` holds one word per wave.  Contains barriers.
+// Inclusive block scan; `tmp` holds one word per wave (16-byte aligned, NT /
+// 64 a multiple of 4).  Contains barriers.
 template <int NT>
 __device__ __forceinline__ uint32_t block_incl_scan(uint32_t v, uint32_t* tmp) {
+  constexpr int kW = NT / 64;
+  static_assert(kW % 4 == 0, "the wave totals are read four at a time");
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   v = wave_incl_scan(v);
   if (lane == 63) tmp[wid] = v;
   __syncthreads();
+  uint4 t[kW / 4];
+#pragma unroll
+  for (int i = 0; i < kW / 4; ++i) t[i] = reinterpret_cast<const uint4*>(tmp)[i];
   uint32_t pre = 0;
-  for (int i = 0; i < wid; ++i) pre += tmp[i];
+#pragma unroll
+  for (int i = 0; i < kW / 4; ++i) {
+    pre += 4 * i + 0 < wid ? t[i].x : 0u;
+    pre += 4 * i + 1 < wid ? t[i].y : 0u;
+    pre += 4 * i + 2 < wid ? t[i].z : 0u;
+    pre += 4 * i + 3 < wid ? t[i].w : 0u;
+  }
   __syncthreads();
   return v + pre;
 }
@@ -133,20 +169,6 @@ __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o));
   return v;
-}
-
-// Thread-to-key mapping of a chunk: key j of thread tid is t0 + j*256 + tid
-// (coalesced loads, all issued before any use).
-__device__ __forceinline__ void load_chunk(const float* s, int64_t t0, int64_t t1, uint32_t* key, bool* in) {
-  float v[kTkPer];
-#pragma unroll
-  for (int j = 0; j < kTkPer; ++j) {
-    const int64_t t = t0 + (int64_t)j * kTkThreads + threadIdx.x;
-    in[j] = t < t1;
-    v[j] = s[in[j] ? t : t1 - 1];  // unconditional load (t1 - 1 is in range)
-  }
-#pragma unroll
-  for (int j = 0; j < kTkPer; ++j) key[j] = order_key(v[j]);
 }
 
 // Block-wide search over a histogram in LDS from the top bin down: the bin x
@@ -197,8 +219,51 @@ __device__ void find_bin_asc(const uint32_t* h, uint32_t need, uint32_t* tmp, ui
   __syncthreads();
 }
 
-// Threshold key tau of a request whose length exceeds k (see the top of the
-// file); called by all NT threads, barriers inside.
+// Threshold from this thread's N keys (those with in[j]; `need` in [1, their
+// count over the workgroup]): the lower edge of the bin holding the key of
+// rank `need` from the top, in a histogram over the 11 bits below the bits
+// all the keys share.  Called by all NT threads; barriers inside.
+template <int NT, int N>
+__device__ __forceinline__ uint32_t tau_of(const uint32_t (&key)[N], const bool (&in)[N], uint32_t need, uint32_t* h,
+                                           uint32_t* tmp, uint32_t* res, uint32_t* s_mm) {
+  const int tid = threadIdx.x;
+  uint32_t lo_k = 0xFFFFFFFFu, hi_k = 0u;
+#pragma unroll
+  for (int j = 0; j < N; ++j) {
+    lo_k = min(lo_k, in[j] ? key[j] : 0xFFFFFFFFu);
+    hi_k = max(hi_k, in[j] ? key[j] : 0u);
+  }
+  lo_k = wave_min_u32(lo_k);
+  hi_k = wave_max_u32(hi_k);
+  if (tid == 0) { s_mm[0] = 0xFFFFFFFFu; s_mm[1] = 0u; }
+  for (int i = tid; i < kBins; i += NT) h[i] = 0u;
+  __syncthreads();
+  if ((tid & 63) == 0) { atomicMin(&s_mm[0], lo_k); atomicMax(&s_mm[1], hi_k); }
+  __syncthreads();
+  uint32_t pre, mask;
+  const int hi = first_round_top(s_mm[0], s_mm[1], &pre, &mask);
+  const int lo = hi - 11;
+#pragma unroll
+  for (int j = 0; j < N; ++j)
+    if (in[j]) atomicAdd(&h[(key[j] >> lo) & 2047u], 1u);
+  __syncthreads();
+  find_bin_desc<kBins, NT>(h, need, tmp, res);
+  return pre | (res[0] << lo);
+}
+
+// Rank r of tau's bin in a sample of n_s of a request's L keys:
+// e + 4 sqrt(e) + 4 with e = k * n_s / L, the expected count of sampled keys
+// at or above the request's k-th largest key.
+__device__ __forceinline__ uint32_t sample_need(int32_t k, uint32_t n_s, int32_t L) {
+  const float e = (float)k * (float)n_s / (float)L;
+  const float r = e + 4.f * sqrtf(e) + 4.f;
+  return (uint32_t)min((int64_t)n_s, (int64_t)ceilf(r));
+}
+
+// Threshold key tau of a request whose length exceeds k, from kSample keys:
+// the whole request when it has at most that many, else 16 runs of 256
+// starting evenly over [0, L - 256].  Called by all NT threads; barriers
+// inside.
 template <int NT>
 __device__ __forceinline__ uint32_t request_tau(const float* __restrict__ s, int32_t L, int32_t k, uint32_t* h, uint32_t* tmp,
                                 uint32_t* res, uint32_t* s_mm) {
@@ -225,107 +290,198 @@ __device__ __forceinline__ uint32_t request_tau(const float* __restrict__ s, int
 #pragma unroll
     for (int j = 0; j < PER; ++j) key[j] = order_key(v[j]);
   }
-  uint32_t lo_k = 0xFFFFFFFFu, hi_k = 0u;
+  const uint32_t need = whole ? (uint32_t)k : sample_need(k, kSample, L);
+  return tau_of<NT, PER>(key, in, need, h, tmp, res, s_mm);
+}
+
+// Collect launch: per request one tau block, then its (request, chunk)
+// blocks.  Blocks run in the order tau blocks, chunk 0 of every request,
+// chunk 1, ...: block index (c + 1) * B8 + b for chunk c of request b, where
+// B8 is the batch rounded up to 8, so the tau blocks are dispatched first,
+// the active chunks (low chunk numbers) next and spread evenly over the
+// CUs, and all of a request's blocks run on XCD b % 8 and share its L2.
+//
+// tau block (requests longer than one chunk): derives tau from a sample
+// placed by max_len, so that its loads need not wait for the request's
+// length: 16 runs of 256 starting evenly over [0, max_len - 256], of which
+// the keys below L count.  It publishes (tag << 32) | tau, tag being the
+// call's own value.
+//
+// Chunk block: every key >= tau' = max(tau, 1) goes to the chunk's slice of
+// the candidate buffer in ascending token order (as the score's bits and
+// its index), and the chunk's count, tau' and its largest key to its
+// metadata slot.  A request of at most one chunk has all its keys here and
+// takes the exact threshold (rank k).  A longer one waits for its tau block
+// (the chunk's own loads land meanwhile) and, should the tag not appear
+// within a bounded wait, derives tau itself from the same sample.  Either
+// way the result is exact: the finish checks that the k-th best candidate is
+// at least every chunk's tau', and otherwise selects over the whole request.
+// Key j of thread tid is token t0 + j*256 + tid, so token order is row j
+// first: each wave ballots its selected keys row by row, and one block scan
+// over the 128 (row, wave) counts gives every key its place.  The selection
+// compares scores against the float key_floor(tau'), which admits the same
+// keys; NaN scores are never candidates (should that leave fewer than k, the
+// finish selects over the whole request).
+constexpr int kTauSpin = 4000;  // polls of the published threshold (s_sleep 4 between them)
+
+template <int NT>
+__device__ __forceinline__ uint32_t sample_tau(const float (&sv)[kSampleRuns], int32_t ml, int32_t L, int32_t k, uint32_t* h,
+                                               uint32_t* tmp, uint32_t* res, uint32_t* s_mm) {
+  uint32_t skey[kSampleRuns];
+  bool in[kSampleRuns];
+  uint32_t n_s = 0;
 #pragma unroll
-  for (int j = 0; j < PER; ++j)
-    if (in[j]) { lo_k = min(lo_k, key[j]); hi_k = max(hi_k, key[j]); }
-  lo_k = wave_min_u32(lo_k);
-  hi_k = wave_max_u32(hi_k);
-  if (tid == 0) { s_mm[0] = 0xFFFFFFFFu; s_mm[1] = 0u; }
-  for (int i = tid; i < kBins; i += NT) h[i] = 0u;
-  __syncthreads();
-  if ((tid & 63) == 0) { atomicMin(&s_mm[0], lo_k); atomicMax(&s_mm[1], hi_k); }
-  __syncthreads();
-  uint32_t pre, mask;
-  const int hi = first_round_top(s_mm[0], s_mm[1], &pre, &mask);
-  const int lo = hi - 11;
-  // Rank r of tau's bin in the sample: k for the whole request, else
-  // e + 4 sqrt(e) + 4 with e = k * kSample / L.
-  uint32_t need = (uint32_t)k;
-  if (!whole) {
-    const float e = (float)k * (float)kSample / (float)L;
-    const float r = e + 4.f * sqrtf(e) + 4.f;
-    need = (uint32_t)min((int64_t)kSample, (int64_t)ceilf(r));
+  for (int j = 0; j < kSampleRuns; ++j) {
+    const int32_t r0 = (int32_t)((int64_t)j * (ml - kSampleRun) / (kSampleRuns - 1));
+    n_s += (uint32_t)min(max(L - r0, 0), kSampleRun);
+    skey[j] = order_key(sv[j]);
+    in[j] = r0 + (int)threadIdx.x < L;
   }
-#pragma unroll
-  for (int j = 0; j < PER; ++j)
-    if (in[j]) atomicAdd(&h[(key[j] >> lo) & 2047u], 1u);
-  __syncthreads();
-  find_bin_desc<kBins, NT>(h, need, tmp, res);
-  return pre | (res[0] << lo);
+  return tau_of<NT, kSampleRuns>(skey, in, sample_need(k, n_s, L), h, tmp, res, s_mm);  // barriers inside
 }
 
-// One workgroup per request longer than k: its tau into the workspace.
-__global__ __launch_bounds__(kTauThreads) void topk_tau_kernel(const float* __restrict__ scores, int64_t stride,
-                                                               const int32_t* __restrict__ lens, int64_t max_len,
-                                                               int32_t k, TopkWs ws) {
-  __shared__ uint32_t h[kBins];
-  __shared__ uint32_t tmp[kTauThreads / 64];
-  __shared__ uint32_t res[2];
-  __shared__ uint32_t s_mm[2];
-  const int b = blockIdx.x;
-  const int32_t L = lens[b];
-  if (!len_ok(L, max_len) || L <= k) return;
-  const uint32_t tau = request_tau<kTauThreads>(scores + (int64_t)b * stride, L, k, h, tmp, res, s_mm);
-  if (threadIdx.x == 0) ws.tau[b] = tau;
-}
-
-// (request, chunk) workgroups: every key >= tau goes to the chunk's slice of
-// the candidate buffer in ascending token order, and the chunk's count and
-// smallest and largest candidate keys to its metadata slot.  Key j of
-// thread tid is token t0 + j*256 + tid, so token order is row j first: each
-// wave ballots its selected keys row by row, and one wave scan over the 64
-// (row, wave) counts gives every key its place.
 __global__ __launch_bounds__(kTkThreads) void topk_collect_kernel(const float* __restrict__ scores, int64_t stride,
-                                                                  const int32_t* __restrict__ lens, int64_t max_len,
-                                                                  int32_t k, TopkWs ws) {
+                                                                  const int32_t* __restrict__ lens, int32_t batch,
+                                                                  int64_t max_len, int32_t k, TopkWs ws) {
+  constexpr int kWaves = kTkThreads / 64;
+  constexpr int kRows = kTkPer * kWaves;
+  static_assert(kRows <= kTkThreads && kTkPer <= 64 && kTkPer % 4 == 0, "one block scan covers the (row, wave) counts");
+  static_assert(kSampleRun == kTkThreads && kSample / kTkThreads == kSampleRuns,
+                "thread tid holds key tid of every sample run");
+  __shared__ uint32_t h[kBins];
+  __shared__ __attribute__((aligned(16))) uint32_t tmp[kWaves];
   __shared__ uint32_t res[2];
   __shared__ uint32_t s_mm[2];
-  __shared__ uint32_t rw[kTkPer * (kTkThreads / 64)];  // (row, wave) counts, then their exclusive scan
-  static_assert(kTkPer * (kTkThreads / 64) == 64, "one wave scans the (row, wave) counts");
-  const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  const int b = logical / ws.chunks, chunk = logical % ws.chunks;
+  __shared__ __attribute__((aligned(16))) uint32_t rw[kRows];  // [wave][row] counts, then their offsets
+  __shared__ uint32_t c_max;      // largest key of the chunk
+  if (max_len <= 0) return;       // every length is then 0
+  const int b8 = (batch + 7) & ~7;
+  const int b = (int)blockIdx.x % b8, chunk = (int)blockIdx.x / b8 - 1;
+  if (b >= batch) return;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const float* s = scores + (int64_t)b * stride;
+  const int32_t ml = (int32_t)max_len;  // max_len < 2^31
+  auto load_sample = [&](float (&sv)[kSampleRuns]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < kSampleRuns; ++j)
+      sv[j] = s[(int32_t)((int64_t)j * (ml - kSampleRun) / (kSampleRuns - 1)) + tid];
+  };
+  if (chunk < 0) {
+    // tau block
+    if (ml <= kTkChunk) return;  // every request fits one chunk
+    float sv[kSampleRuns];
+    load_sample(sv);
+    const int32_t L = lens[b];
+    if (!len_ok(L, max_len) || L <= k || L <= kTkChunk) return;
+    const uint32_t tau = sample_tau<kTkThreads>(sv, ml, L, k, h, tmp, res, s_mm);
+    if (tid == 0)
+      __hip_atomic_store(ws.tau_pub + b, ((unsigned long long)ws.tag << 32) | tau, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    return;
+  }
+  const int32_t t0 = chunk * kTkChunk;
+  // (In a block the compiler cannot fold: a plain run of loads whose values
+  // only the active path uses gets moved below the length checks, so the
+  // loads would wait for the length after all.)
+  float v[kTkPer];
+  int32_t always = 1;
+  asm volatile("" : "+s"(always));
+  if (always) {
+#pragma unroll
+    for (int j = 0; j < kTkPer; ++j) v[j] = s[min(t0 + j * kTkThreads + tid, ml - 1)];
+  }
   const int32_t L = lens[b];
   if (!len_ok(L, max_len) || L <= k) return;
-  const int n_act = (int)((L + kTkChunk - 1) / kTkChunk);
+  const int n_act = (L + kTkChunk - 1) / kTkChunk;
   if (chunk >= n_act) return;
-  const float* s = scores + (int64_t)b * stride;
-  const int64_t t0 = (int64_t)chunk * kTkChunk, t1 = min((int64_t)L, t0 + kTkChunk);
-  uint32_t key[kTkPer];
-  bool in[kTkPer];
-  load_chunk(s, t0, t1, key, in);
-  const uint32_t tau = ws.tau[b];
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const uint64_t below = (1ull << lane) - 1ull;
-  uint32_t rank[kTkPer];
-  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+  if (tid == 0) c_max = 0u;
+  if (t0 + kTkChunk > L) {
+#pragma unroll
+    for (int j = 0; j < kTkPer; ++j) v[j] = t0 + j * kTkThreads + tid < L ? v[j] : __uint_as_float(0x7FC00000u);
+  }
+  uint32_t tau;
+  if (L <= kTkChunk) {
+    uint32_t key[kTkPer];
+    bool in[kTkPer];
+#pragma unroll
+    for (int j = 0; j < kTkPer; ++j) {
+      key[j] = order_key(v[j]);
+      in[j] = j * kTkThreads + tid < L;
+    }
+    tau = tau_of<kTkThreads, kTkPer>(key, in, (uint32_t)k, h, tmp, res, s_mm);  // barriers inside
+  } else {
+    if (tid == 0) {
+      // The first poll's load returns after the chunk's loads (loads
+      // complete in order), by when the tau block has usually published.
+      uint32_t got = 0, t = 0;
+      for (int it = 0; it < kTauSpin; ++it) {
+        const unsigned long long w = __hip_atomic_load(ws.tau_pub + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if ((uint32_t)(w >> 32) == ws.tag) {
+          t = (uint32_t)w;
+          got = 1;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(4);
+      }
+      res[0] = t;
+      res[1] = got;
+    }
+    __syncthreads();
+    tau = res[0];
+    if (!res[1]) {
+      __syncthreads();  // res is read before sample_tau rewrites it
+      float sv[kSampleRuns];
+      load_sample(sv);
+      tau = sample_tau<kTkThreads>(sv, ml, L, k, h, tmp, res, s_mm);
+    }
+  }
+  tau = max(tau, 1u);
+  const float ftau = key_floor(tau);
+  // Count pass: lane j ends with the count of row j in this wave.
+  uint32_t row_cnt = 0;
+  float vmax = -INFINITY;
 #pragma unroll
   for (int j = 0; j < kTkPer; ++j) {
-    const bool sel = in[j] && key[j] >= tau;
-    const uint64_t m = __ballot(sel);
-    rank[j] = (uint32_t)__popcll(m & below);
-    if (lane == 0) rw[j * (kTkThreads / 64) + wv] = (uint32_t)__popcll(m);
-    if (sel) { kmin = min(kmin, key[j]); kmax = max(kmax, key[j]); }
+    const uint32_t c = (uint32_t)__popcll(__ballot(v[j] >= ftau));
+    row_cnt = lane == j ? c : row_cnt;
+    vmax = fmaxf(vmax, v[j]);
   }
-  kmin = wave_min_u32(kmin);
-  kmax = wave_max_u32(kmax);
-  if (threadIdx.x == 0) { s_mm[0] = 0xFFFFFFFFu; s_mm[1] = 0u; }
-  __syncthreads();
-  if (lane == 0) { atomicMin(&s_mm[0], kmin); atomicMax(&s_mm[1], kmax); }
-  if (wv == 0) {
-    const uint32_t v = rw[lane];
-    const uint32_t incl = wave_incl_scan(v);
-    rw[lane] = incl - v;
-    if (lane == 63) res[0] = incl;
+  for (int o = 32; o > 0; o >>= 1) vmax = fmaxf(vmax, __shfl_xor(vmax, o));
+  if (lane < kTkPer) rw[wv * kTkPer + lane] = row_cnt;
+  __syncthreads();  // c_max is cleared before any wave raises it
+  if (lane == 0) atomicMax(&c_max, order_key(vmax));
+  {
+    // exclusive scan in token order: entry (row j, wave w) is thread j * kWaves + w
+    const int j = tid / kWaves, w = tid % kWaves;
+    const uint32_t cnt = tid < kRows ? rw[w * kTkPer + j] : 0u;
+    const uint32_t incl = block_incl_scan<kTkThreads>(cnt, tmp);  // barriers inside
+    if (tid < kRows) rw[w * kTkPer + j] = incl - cnt;
+    if (tid == kTkThreads - 1) res[0] = incl;
   }
   __syncthreads();
+  const uint32_t total = res[0];
   const int64_t slot = (int64_t)b * ws.chunks + chunk;
-  if (threadIdx.x == 0) ws.meta[slot] = make_uint4(res[0], s_mm[0], s_mm[1], 0u);
-  uint2* cb = ws.cand + slot * kTkChunk;
+  if (tid == 0) ws.meta[slot] = make_uint4(total, tau, c_max, 0u);
+  if (total > (uint32_t)kTkSlice) return;  // the finish reads the whole request instead
+  uint2* cb = ws.cand + slot * kTkSlice;
+  uint32_t base[kTkPer];
+#pragma unroll
+  for (int q = 0; q < kTkPer / 4; ++q) {
+    const uint4 r = reinterpret_cast<const uint4*>(rw + wv * kTkPer)[q];
+    base[4 * q] = r.x; base[4 * q + 1] = r.y; base[4 * q + 2] = r.z; base[4 * q + 3] = r.w;
+  }
+  // Write pass: the same ballots give each selected key its rank in its row.
+  // (The selection is recomputed from a copy of the threshold the compiler
+  // cannot see through: keeping the count pass's 32 lane masks alive
+  // instead spills scalar registers.)
+  float ftau_w = ftau;
+  asm volatile("" : "+v"(ftau_w));
 #pragma unroll
   for (int j = 0; j < kTkPer; ++j) {
-    const int64_t t = t0 + (int64_t)j * kTkThreads + threadIdx.x;
-    if (in[j] && key[j] >= tau) cb[rw[j * (kTkThreads / 64) + wv] + rank[j]] = make_uint2(key[j], (uint32_t)t);
+    const bool sel = v[j] >= ftau_w;
+    const uint64_t m = __ballot(sel);
+    const uint32_t rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+    if (sel) cb[base[j] + rank] = make_uint2(__float_as_uint(v[j]), (uint32_t)(t0 + j * kTkThreads + tid));
   }
 }
 
@@ -334,9 +490,12 @@ __global__ __launch_bounds__(kTkThreads) void topk_collect_kernel(const float* _
 // the score row `srow` -- with their indices written to `out` in that order.
 // [cmin, cmax] bounds the listed keys.  Called by all kFinThreads threads
 // after a barrier that follows *bin_cnt = 0; barriers inside.
-__device__ __forceinline__ void select_k_best(const uint2* lc, const float* __restrict__ srow, bool whole, uint32_t n_c,
-                              uint32_t cmin, uint32_t cmax, int32_t k, int32_t* __restrict__ out, uint32_t* h,
-                              uint32_t* tmp, uint32_t* res, uint2* bin_list, uint32_t* bin_cnt) {
+// Returns false, writing nothing, when the selection over a list comes out
+// with a k-th best key below tau_max (the largest threshold a chunk
+// collected with: keys between the two may be missing from the list).
+__device__ __forceinline__ bool select_k_best(const uint2* lc, const float* __restrict__ srow, bool whole, uint32_t n_c,
+                              uint32_t cmin, uint32_t cmax, uint32_t tau_max, int32_t k, int32_t* __restrict__ out,
+                              uint32_t* h, uint32_t* tmp, uint32_t* res, uint2* bin_list, uint32_t* bin_cnt) {
   const int tid = threadIdx.x;
   auto cand = [&](uint32_t j) -> uint2 { return whole ? make_uint2(order_key(srow[j]), j) : lc[j]; };
   uint32_t need = (uint32_t)k;
@@ -376,17 +535,20 @@ __device__ __forceinline__ void select_k_best(const uint2* lc, const float* __re
         if ((e.x & kmask) == kpre) bin_list[atomicAdd(bin_cnt, 1u)] = e;
       }
       __syncthreads();
-      if (tid < (int)in_bin) {
-        // Rank of this lane's key among the bin's keys (larger key first,
-        // then smaller index); the entry of rank need - 1 is the last one
-        // selected.  Every lane reads the same LDS word at a time.
-        const uint2 e = bin_list[tid];
+      if (tid < 64) {
+        // Wave 0 holds the bin's keys, one per lane; each lane ranks its own
+        // among them (larger key first, then smaller index) from the other
+        // lanes' registers; the entry of rank need - 1 is the last one
+        // selected.
+        const bool mine = tid < (int)in_bin;
+        const uint2 e = mine ? bin_list[tid] : make_uint2(0u, 0u);
         uint32_t rank = 0;
         for (uint32_t m = 0; m < in_bin; ++m) {
-          const uint2 o = bin_list[m];
-          rank += (o.x > e.x || (o.x == e.x && o.y < e.y)) ? 1u : 0u;
+          const uint32_t ox = (uint32_t)__builtin_amdgcn_readlane((int)e.x, (int)m);
+          const uint32_t oy = (uint32_t)__builtin_amdgcn_readlane((int)e.y, (int)m);
+          rank += (ox > e.x || (ox == e.x && oy < e.y)) ? 1u : 0u;
         }
-        if (rank == need - 1) { res[0] = e.x; res[1] = e.y; }
+        if (mine && rank == need - 1) { res[0] = e.x; res[1] = e.y; }
       }
       __syncthreads();
       T = res[0];
@@ -427,6 +589,7 @@ __device__ __forceinline__ void select_k_best(const uint2* lc, const float* __re
       I = ipre;
     }
   }
+  if (!whole && T < tau_max) return false;  // uniform: T is the same in every thread
   // The candidates are in ascending token order, so the selected ones are
   // written in order by one block scan: thread tid takes a contiguous run.
   const uint32_t per = (n_c + kFinThreads - 1) / kFinThreads;
@@ -439,6 +602,7 @@ __device__ __forceinline__ void select_k_best(const uint2* lc, const float* __re
     const uint2 e = cand(j);
     if (picked(e)) out[pos++] = (int32_t)e.y;
   }
+  return true;
 }
 
 __global__ __launch_bounds__(kFinThreads) void topk_finish_kernel(const float* __restrict__ scores, int64_t stride,
@@ -447,16 +611,21 @@ __global__ __launch_bounds__(kFinThreads) void topk_finish_kernel(const float* _
                                                                   int32_t* __restrict__ status) {
   __shared__ uint32_t big[kFinLdsWords];   // gathered candidates (uint2)
   __shared__ uint32_t h[kBins];
-  __shared__ uint32_t tmp[kFinThreads / 64];
+  __shared__ __attribute__((aligned(16))) uint32_t tmp[kFinThreads / 64];
   __shared__ uint32_t res[2];
   __shared__ uint32_t coff[kFinThreads];  // chunk offsets in the gathered candidate list
-  __shared__ uint32_t ccnt[kFinThreads];  // chunk candidate counts
   __shared__ uint32_t s_mm[2];
+  __shared__ uint32_t ovf;                 // some chunk had more candidates than its slice
+  __shared__ uint32_t s_tmax;              // largest threshold a chunk collected with
   __shared__ uint2 bin_list[64];           // members of the boundary bin, when few
   __shared__ uint32_t bin_cnt;
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
+  // The request's chunk metadata is requested before its length is known
+  // (slots past its last chunk hold stale values and are not used).
+  const int64_t slot0 = (int64_t)b * ws.chunks;
+  const uint4 meta_raw = tid < ws.chunks ? ws.meta[slot0 + tid] : make_uint4(0u, 0xFFFFFFFFu, 0u, 0u);
   const int32_t L = lens[b];
   int32_t* out = out_idx + (int64_t)b * k;
   if (!len_ok(L, max_len)) {
@@ -469,39 +638,61 @@ __global__ __launch_bounds__(kFinThreads) void topk_finish_kernel(const float* _
     return;
   }
   // Candidates: the chunks' keys >= tau gathered into LDS in token order, or,
-  // should fewer than k or more than LDS holds have reached tau (or the
-  // request have more chunks than this workgroup has threads), every key of
-  // the request read from the scores.
+  // should fewer than k have reached tau, more than a slice or LDS holds (or
+  // the request have more chunks than this workgroup has threads), every key
+  // of the request read from the scores.
   const int n_act = (int)((L + kTkChunk - 1) / kTkChunk);
-  const int64_t slot0 = (int64_t)b * ws.chunks;
-  const uint4 meta = (tid < n_act) ? ws.meta[slot0 + tid] : make_uint4(0u, 0xFFFFFFFFu, 0u, 0u);
-  if (tid == 0) { s_mm[0] = 0xFFFFFFFFu; s_mm[1] = 0u; }
-  const uint32_t c_incl = block_incl_scan<kFinThreads>(meta.x, tmp);
-  if (tid < n_act) { coff[tid] = c_incl - meta.x; ccnt[tid] = meta.x; }
+  const uint4 meta = tid < n_act ? meta_raw : make_uint4(0u, 0xFFFFFFFFu, 0u, 0u);
+  if (tid == 0) { s_mm[0] = 0xFFFFFFFFu; s_mm[1] = 0u; ovf = 0u; s_tmax = 0u; }
+  const uint32_t c_incl = block_incl_scan<kFinThreads>(meta.x, tmp);  // barriers inside
+  if (tid < n_act) coff[tid] = c_incl - meta.x;
   if (tid == kFinThreads - 1) res[0] = c_incl;
   {
     const uint32_t wmin = wave_min_u32(meta.y), wmax = wave_max_u32(meta.z);
-    if (lane == 0) { atomicMin(&s_mm[0], wmin); atomicMax(&s_mm[1], wmax); }
+    const uint32_t tmax = wave_max_u32(tid < n_act ? meta.y : 0u);
+    if (lane == 0) { atomicMin(&s_mm[0], wmin); atomicMax(&s_mm[1], wmax); atomicMax(&s_tmax, tmax); }
+    if (meta.x > (uint32_t)kTkSlice) ovf = 1u;
   }
   __syncthreads();
   const uint32_t n_cand = res[0];
-  const bool whole = n_cand < (uint32_t)k || n_cand > (uint32_t)kCandLds || n_act > kFinThreads;
+  const bool whole = ovf != 0u || n_cand < (uint32_t)k || n_cand > (uint32_t)kCandLds || n_act > kFinThreads;
   const uint32_t n_c = whole ? (uint32_t)L : n_cand;
   const float* srow = scores + (int64_t)b * stride;
   uint2* lc = reinterpret_cast<uint2*>(big);
   if (!whole) {
-    // Wave w copies chunks w, w + 16, ...: each chunk's slice goes to its
-    // offset in the gathered list.
-    for (int c = tid >> 6; c < n_act; c += kFinThreads / 64) {
-      const uint32_t n = ccnt[c], off = coff[c];
-      const uint2* src = ws.cand + (slot0 + c) * kTkChunk;
-      for (uint32_t i = lane; i < n; i += 64) lc[off + i] = src[i];
+    // List position j = tid + m * kFinThreads comes from the last chunk c
+    // with coff[c] <= j (chunks without candidates share their offset with
+    // the next chunk, so the last such c is the one that holds j).
+    constexpr int kG = kCandLds / kFinThreads;
+    uint2 e[kG];
+#pragma unroll
+    for (int m = 0; m < kG; ++m) {
+      const uint32_t j = (uint32_t)(tid + m * kFinThreads);
+      if (j < n_cand) {
+        int lo = 0, hi = n_act - 1;
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (coff[mid] <= j) lo = mid; else hi = mid - 1;
+        }
+        e[m] = ws.cand[(slot0 + lo) * kTkSlice + (j - coff[lo])];
+        e[m].x = order_key(__uint_as_float(e[m].x));
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < kG; ++m) {
+      const uint32_t j = (uint32_t)(tid + m * kFinThreads);
+      if (j < n_cand) lc[j] = e[m];
     }
   }
-  const uint32_t cmin = s_mm[0], cmax = s_mm[1];
+  const uint32_t cmin = s_mm[0], cmax = s_mm[1], tau_max = s_tmax;
   if (tid == 0) bin_cnt = 0u;
   __syncthreads();
-  select_k_best(lc, srow, whole, n_c, cmin, cmax, k, out, h, tmp, res, bin_list, &bin_cnt);
+  if (!select_k_best(lc, srow, whole, n_c, cmin, cmax, tau_max, k, out, h, tmp, res, bin_list, &bin_cnt)) {
+    __syncthreads();
+    if (tid == 0) bin_cnt = 0u;
+    __syncthreads();
+    select_k_best(lc, srow, true, (uint32_t)L, 0u, 0u, 0u, k, out, h, tmp, res, bin_list, &bin_cnt);
+  }
 }
 
 // Single-launch form for rows of up to kFusedMaxLen keys: one workgroup per
@@ -527,7 +718,7 @@ __global__ __launch_bounds__(kFinThreads) void topk_fused_kernel(const float* __
                                                                  int32_t* __restrict__ status) {
   __shared__ uint32_t big[kFinLdsWords];   // wave regions, then the packed candidate list (uint2)
   __shared__ uint32_t h[kBins];
-  __shared__ uint32_t tmp[kFinThreads / 64];
+  __shared__ __attribute__((aligned(16))) uint32_t tmp[kFinThreads / 64];
   __shared__ uint32_t res[2];
   __shared__ uint32_t s_mm[2];
   __shared__ uint32_t c_mm[2];             // smallest and largest candidate key
@@ -628,8 +819,21 @@ __global__ __launch_bounds__(kFinThreads) void topk_fused_kernel(const float* __
     }
     __syncthreads();
   }
-  select_k_best(lc, srow, whole, whole ? (uint32_t)L : n_cand, c_mm[0], c_mm[1], k, out, h, tmp, res, bin_list,
+  select_k_best(lc, srow, whole, whole ? (uint32_t)L : n_cand, c_mm[0], c_mm[1], tau, k, out, h, tmp, res, bin_list,
                 &bin_cnt);
+}
+
+// Tags for the published thresholds: a process-wide counter started at a
+// random value, so a stale word in a reused workspace (a previous call, or
+// memory a previous process left behind) is unlikely to carry the current
+// call's tag; when one does, the stale threshold can only cost speed (see
+// the collect launch).
+static uint32_t next_tag() {
+  static std::atomic<uint32_t> counter{[] {
+    std::random_device rd;
+    return rd() ^ (uint32_t)std::chrono::steady_clock::now().time_since_epoch().count();
+  }()};
+  return counter.fetch_add(1, std::memory_order_relaxed) + 1u;
 }
 
 int launch_topk(const TopkArgs& a, hipStream_t s) {
@@ -640,13 +844,11 @@ int launch_topk(const TopkArgs& a, hipStream_t s) {
                        a.score_stride, a.lens, a.max_len, a.k, a.out_idx, a.status);
     return hipGetLastError() == hipSuccess ? 0 : -3;
   }
-  TopkWs ws = carve(a.workspace, a.batch, a.max_len);
-  const int64_t grid = (int64_t)a.batch * ws.chunks;
-  if (grid > 0x7FFFFFFF) return -2;
-  hipLaunchKernelGGL(topk_tau_kernel, dim3((unsigned)a.batch), dim3(kTauThreads), 0, s, a.scores, a.score_stride,
-                     a.lens, a.max_len, a.k, ws);
-  hipLaunchKernelGGL(topk_collect_kernel, dim3((unsigned)grid), dim3(kTkThreads), 0, s, a.scores, a.score_stride,
-                     a.lens, a.max_len, a.k, ws);
+  TopkWs ws = carve(a.workspace, a.batch, a.max_len, next_tag());
+  const int64_t grid8 = (int64_t)((a.batch + 7) & ~7) * (ws.chunks + 1);
+  if (grid8 > 0x7FFFFFFF) return -2;
+  hipLaunchKernelGGL(topk_collect_kernel, dim3((unsigned)grid8), dim3(kTkThreads), 0, s, a.scores, a.score_stride,
+                     a.lens, a.batch, a.max_len, a.k, ws);
   hipLaunchKernelGGL(topk_finish_kernel, dim3((unsigned)a.batch), dim3(kFinThreads), 0, s, a.scores, a.score_stride,
                      a.lens, a.max_len, a.k, ws, a.out_idx, a.status);
   return hipGetLastError() == hipSuccess ? 0 : -3;
