@@ -28,8 +28,9 @@
  * Conventions shared by every entry point
  *  - Pointers: every array pointer is DEVICE memory unless stated otherwise.
  *    The caller owns all memory; the library never allocates, frees or keeps a
- *    pointer beyond the work it enqueues.  Buffers must stay alive until that
- *    work completes on `stream`.
+ *    pointer beyond the work it enqueues (topk_select_noalloc's static
+ *    workspace aside).  Buffers must stay alive until that work completes on
+ *    `stream`.
  *  - Streams: `stream` is a hipStream_t (NULL = the null stream).  Every entry
  *    point only enqueues work; none synchronises the host.
  *  - Layouts: row-major, last dimension contiguous.  Pools and row arrays must
@@ -47,7 +48,8 @@
  *    The caller decides what to do with a flagged request, in the spirit of
  *    aborting a request rather than returning wrong data [WA section 3].
  *  - Reentrancy: stateless and thread-safe; calls on different streams may
- *    overlap.
+ *    overlap (except topk_select_noalloc calls on one GPU, which share its
+ *    static workspace).
  */
 #ifndef SPARSE_MLA_H
 #define SPARSE_MLA_H
@@ -163,6 +165,26 @@ int topk_select(const float* scores, int64_t score_stride,
                 const int32_t* context_lens, int32_t batch, int64_t max_len, int32_t k,
                 int32_t* out_idx, void* workspace, size_t workspace_bytes,
                 int32_t* req_status, void* stream);
+
+/*
+ * topk_select_noalloc -- topk_select for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): same arguments, result, errors and launches, without the
+ * workspace.  Its workspace is a static device array of
+ * SPMLA_TOPK_SCRATCH_BYTES that the library holds on every GPU it runs on
+ * until the process ends; the call itself allocates nothing.  Sizes for which
+ * topk_workspace_bytes(batch, max_len, k) exceeds that array are rejected with
+ * SPMLA_EWORKSPACE and nothing is enqueued.  The first call on a device
+ * resolves the array's address there (call with that device current).  Every
+ * call on one GPU shares the array, which keeps the last call's contents
+ * (nothing in it needs clearing between calls): calls that overlap on one GPU
+ * (other streams, other host threads) race and must be serialised by the
+ * caller.
+ */
+#define SPMLA_TOPK_SCRATCH_BYTES ((size_t)32 << 20)
+int topk_select_noalloc(const float* scores, int64_t score_stride,
+                        const int32_t* context_lens, int32_t batch, int64_t max_len, int32_t k,
+                        int32_t* out_idx, int32_t* req_status, void* stream);
 
 /*
  * mla_paged_decode -- split-KV attention of every query head over a token set

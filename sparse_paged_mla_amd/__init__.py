@@ -55,6 +55,8 @@ def declare(lib):
     lib.topk_workspace_bytes.argtypes = [i32, i64, i32]
     lib.topk_select.restype = ctypes.c_int
     lib.topk_select.argtypes = [vp, i64, vp, i32, i64, i32, vp, vp, ctypes.c_size_t, vp, vp]
+    lib.topk_select_noalloc.restype = ctypes.c_int
+    lib.topk_select_noalloc.argtypes = [vp, i64, vp, i32, i64, i32, vp, vp, vp]
     lib.mla_paged_decode.restype = ctypes.c_int
     lib.mla_paged_decode.argtypes = [vp, i32, vp, vp, i32, i32, i32, vp, i32, vp, i32, i64, vp, i32, i32, i32, i32,
                                      f32, i32, vp, vp, vp, vp]
@@ -139,6 +141,14 @@ def topk_select(scores, context_lens, max_len, k, out_idx, workspace, req_status
     _check(lib.topk_select(_ptr(scores), scores.stride(0), _ptr(context_lens), B, int(max_len), int(k),
                            _ptr(out_idx), _ptr(workspace), workspace.numel() * workspace.element_size(),
                            _ptr(req_status), _stream(stream)))
+
+
+def topk_select_noalloc(scores, context_lens, max_len, k, out_idx, req_status=None, stream=None):
+    """topk_select with the library's static device workspace instead of a caller buffer."""
+    lib = load_library()
+    B = context_lens.shape[0]
+    _check(lib.topk_select_noalloc(_ptr(scores), scores.stride(0), _ptr(context_lens), B, int(max_len), int(k),
+                                   _ptr(out_idx), _ptr(req_status), _stream(stream)))
 
 
 def mla_paged_decode(q, kv_pool, kv_scale, block_table, context_lens, max_len, indices, d_latent, sm_scale,

@@ -134,6 +134,28 @@ int topk_select(const float* scores, int64_t score_stride, const int32_t* contex
   return map_launch(spmla::launch_topk(a, reinterpret_cast<hipStream_t>(stream)), w);
 }
 
+int topk_select_noalloc(const float* scores, int64_t score_stride, const int32_t* context_lens, int32_t batch,
+                        int64_t max_len, int32_t k, int32_t* out_idx, int32_t* req_status, void* stream) {
+  const char* w = "topk_select_noalloc";
+  static_assert(SPMLA_TOPK_SCRATCH_BYTES == spmla::kTopkScratchBytes, "header and library agree on the scratch size");
+  if (batch < 0) return fail(SPMLA_EINVAL, "%s: batch < 0", w);
+  if (k < 1 || k > 4096) return fail(SPMLA_EUNSUPPORTED, "%s: k must be in [1, 4096]", w);
+  if (max_len < 0 || max_len >= (int64_t)1 << 31) return fail(SPMLA_EINVAL, "%s: max_len out of [0, 2^31)", w);
+  if (score_stride < max_len) return fail(SPMLA_EINVAL, "%s: score_stride < max_len", w);
+  if (batch == 0) return ok();
+  if (!scores || !context_lens || !out_idx) return fail(SPMLA_EINVAL, "%s: null pointer", w);
+  const size_t need = spmla::topk_workspace_size(batch, max_len, k);
+  if (need > spmla::kTopkScratchBytes)
+    return fail(SPMLA_EWORKSPACE, "%s: batch %d, max_len %lld need %zu bytes of workspace; the static scratch holds %zu",
+                w, batch, (long long)max_len, need, spmla::kTopkScratchBytes);
+  void* ws = nullptr;
+  if (spmla::topk_scratch(&ws) != 0)
+    return fail(SPMLA_ELAUNCH, "%s: the static scratch has no address on the current device (%s)", w,
+                hipGetErrorString(hipGetLastError()));
+  spmla::TopkArgs a{scores, score_stride, context_lens, batch, max_len, k, out_idx, ws, req_status};
+  return map_launch(spmla::launch_topk(a, reinterpret_cast<hipStream_t>(stream)), w);
+}
+
 int mla_paged_decode(const void* q, int32_t q_dtype, const void* kv_pool, const float* kv_scale, int32_t kv_dtype,
                      int32_t num_pages, int32_t page_size, const int32_t* block_table, int32_t bt_stride,
                      const int32_t* context_lens, int32_t batch, int64_t max_len, const int32_t* indices, int32_t k,

@@ -24,6 +24,9 @@ struct TopkArgs {
   int32_t k; int32_t* out_idx; void* workspace; int32_t* status;
 };
 int launch_topk(const TopkArgs& a, hipStream_t stream);
+// Device address of the static top-k workspace on the current device
+// (resolved on the first call per device); 0, or -2 / -3 on failure.
+int topk_scratch(void** ptr);
 
 struct DecodeArgs {
   const void* q; int q_dtype; const void* kv; const float* kv_scale; int kv_dtype;

@@ -50,6 +50,7 @@
 #include <algorithm>
 #include <atomic>
 #include <chrono>
+#include <mutex>
 #include <random>
 
 namespace spmla {
@@ -821,6 +822,29 @@ __global__ __launch_bounds__(kFinThreads) void topk_fused_kernel(const float* __
   }
   select_k_best(lc, srow, whole, whole ? (uint32_t)L : n_cand, c_mm[0], c_mm[1], tau, k, out, h, tmp, res, bin_list,
                 &bin_cnt);
+}
+
+// ---- allocation-free form (topk_select_noalloc): the workspace is this
+// file-scope device array, which every GPU the library runs on holds until
+// the process ends.  Host code never passes the array's name to a kernel
+// (on the host it only stands for the symbol); the device address is
+// resolved once per device with hipGetSymbolAddress and kept.
+static __device__ __align__(256) uint8_t scratch[kTopkScratchBytes];
+
+int topk_scratch(void** ptr) {
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return -3;
+  if (dev < 0 || dev >= kMaxDevices) return -2;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return -3;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return 0;
 }
 
 // Tags for the published thresholds: a process-wide counter started at a

@@ -13,6 +13,8 @@ constexpr int kTkThreads = 256;
 constexpr int kTkPer = 32;                       // keys per thread per chunk
 constexpr int kTkChunk = kTkThreads * kTkPer;    // 8192 keys per collect workgroup
 constexpr int kTkSlice = 2048;                   // candidate slots per chunk
+constexpr size_t kTopkScratchBytes = (size_t)32 << 20;  // static workspace of topk_select_noalloc
+constexpr int kMaxDevices = 64;
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 inline int32_t n_chunks(int64_t max_len) {
