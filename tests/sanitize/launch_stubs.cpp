@@ -6,6 +6,7 @@
 
 namespace {
 int g_launches = 0;
+alignas(256) unsigned char g_fake_scratch[256];  // stands in for the static device workspace; never touched
 }
 
 namespace spmla {
@@ -16,6 +17,7 @@ int launch_merge(const MergeArgs&, hipStream_t) { return ++g_launches, 0; }
 int launch_cache_append(const AppendArgs&, hipStream_t) { return ++g_launches, 0; }
 int launch_page_check(const PageCheckArgs&, hipStream_t) { return ++g_launches, 0; }
 int launch_mq_expand(const MqExpandArgs&, hipStream_t) { return ++g_launches, 0; }
+int topk_scratch(void** ptr) { return *ptr = g_fake_scratch, 0; }
 }  // namespace spmla
 
 extern "C" int spmla_stub_launches(void) { return g_launches; }

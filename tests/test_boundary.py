@@ -123,6 +123,22 @@ def test_topk_rejects(lib):
     assert f(None, 1000, None, 0, 1000, 2048, None, None, 0, None, None) == OK
 
 
+def test_topk_noalloc_rejects(lib):
+    """The static-workspace form checks the same arguments, and sizes whose
+    workspace exceeds its 32 MiB array, before any HIP call."""
+    f = lib.topk_select_noalloc
+    assert f(FAKE, 1000, FAKE, 4, 1000, 0, FAKE, None, None) == EUNSUPPORTED
+    assert f(FAKE, 1000, FAKE, 4, 1000, 4097, FAKE, None, None) == EUNSUPPORTED
+    assert f(FAKE, 999, FAKE, 4, 1000, 2048, FAKE, None, None) == EINVAL
+    assert f(None, 1000, FAKE, 4, 1000, 2048, FAKE, None, None) == EINVAL
+    assert f(FAKE, 1000, FAKE, -1, 1000, 2048, FAKE, None, None) == EINVAL
+    assert f(None, 1000, None, 0, 1000, 2048, None, None, None) == OK
+    big = 1 << 20
+    assert lib.topk_workspace_bytes(1024, big, 2048) > 32 << 20
+    assert f(FAKE, big, FAKE, 1024, big, 2048, FAKE, None, None) == EWORKSPACE
+    assert b"static scratch" in lib.spmla_last_error()
+
+
 def test_decode_rejects(lib):
     lib.mla_paged_decode.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
                                      ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
@@ -247,10 +263,12 @@ def test_valid_calls_reach_the_launcher_and_rejected_ones_do_not(lib):
     need = lib.topk_workspace_bytes(4, 100000, 2048)
     assert lib.topk_select(FAKE, 100000, FAKE, 4, 100000, 2048, FAKE, ctypes.c_void_p(0x100000), need, None,
                            None) == OK
+    assert lib.topk_select_noalloc(FAKE, 100000, FAKE, 4, 100000, 2048, FAKE, None, None) == OK
     assert lib.spmla_last_error() == b""
-    assert _launches(lib) == n0 + 7
+    assert _launches(lib) == n0 + 8
     assert _idx(lib, d=96) == EUNSUPPORTED
     assert _dec(lib, splits=0) == EUNSUPPORTED
     assert lib.topk_select(FAKE, 100000, FAKE, 4, 100000, 2048, FAKE, ctypes.c_void_p(0x100000), need - 1, None,
                            None) == EWORKSPACE
-    assert _launches(lib) == n0 + 7
+    assert lib.topk_select_noalloc(FAKE, 1 << 20, FAKE, 1024, 1 << 20, 2048, FAKE, None, None) == EWORKSPACE
+    assert _launches(lib) == n0 + 8
