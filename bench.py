@@ -43,7 +43,60 @@ def parse():
                     help="requests in the CPU-oracle sample (-1: auto, 0: skip)")
     ap.add_argument("--profile-only", action="store_true",
                     help="no CPU baseline; adds one plain 256 MiB device copy (counter calibration) for rocprofv3")
+    ap.add_argument("--counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU work: turn the counter_collection.csv files of a FETCH_SIZE and a WRITE_SIZE "
+                         "rocprofv3 run of --profile-only into profiles/counters.json entries for --config, "
+                         "and print them as a markdown table")
     return ap.parse_args()
+
+
+# Kernel-name fragment -> source file whose HBM traffic it measures.
+COUNTER_SOURCES = [("indexer_kernel", "indexer.hip"), ("topk_", "topk.hip"), ("mla_decode_f8ws", "mla_decode_f8.hip"),
+                   ("mla_decode_kernel", "mla_decode.hip"), ("lse_merge", "lse_merge.hip"),
+                   ("cache_append", "cache_append.hip")]
+CALIB_BYTES = 256 << 20  # the plain device copy --profile-only adds
+
+
+def summarize_counters(fetch_csv, write_csv, workload):
+    """HBM bytes per launch of each kernel source from two rocprofv3 counter
+    runs of `bench.py --profile-only` (FETCH_SIZE, then WRITE_SIZE, in KiB per
+    dispatch), scaled by what the same counters read for the plain 256 MiB
+    device copy; a source with several kernels per call (top-k) sums them."""
+    import csv
+    per = {}
+    for path, counter in ((fetch_csv, "FETCH_SIZE"), (write_csv, "WRITE_SIZE")):
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] == counter:
+                per.setdefault(r["Kernel_Name"], {}).setdefault(counter, []).append(float(r["Counter_Value"]))
+    copies = per.get("__amd_rocclr_copyBuffer", {})
+    rf = CALIB_BYTES / (max(copies["FETCH_SIZE"]) * 1024)
+    wf = CALIB_BYTES / (max(copies["WRITE_SIZE"]) * 1024)
+    recs = {}
+    for name, c in per.items():
+        src = next((f for frag, f in COUNTER_SOURCES if frag in name), None)
+        if src is None or "FETCH_SIZE" not in c or "WRITE_SIZE" not in c:
+            continue
+        fk, wk = statistics.fmean(c["FETCH_SIZE"]), statistics.fmean(c["WRITE_SIZE"])
+        r = recs.setdefault(src, dict(fetch_kib=0.0, write_kib=0.0, kernels=[]))
+        r["fetch_kib"] += fk
+        r["write_kib"] += wk
+        r["kernels"].append((name, fk, wk))
+    p = os.path.join(ROOT, "profiles", "counters.json")
+    allrec = json.load(open(p)) if os.path.exists(p) else {}
+    w = allrec.setdefault(workload, {})
+    print("| Kernel | FETCH_SIZE (KiB) | WRITE_SIZE (KiB) | Calibrated HBM MB/launch |")
+    print("|---|---|---|---|")
+    print(f"| `__amd_rocclr_copyBuffer` (256 MiB calibration copy) | {max(copies['FETCH_SIZE']):.0f} | "
+          f"{max(copies['WRITE_SIZE']):.0f} | {2 * CALIB_BYTES / 1e6:.1f} |")
+    for src, r in sorted(recs.items()):
+        for name, fk, wk in r["kernels"]:
+            print(f"| `{name.split('(')[0]}` | {fk:.0f} | {wk:.0f} | {(fk * 1024 * rf + wk * 1024 * wf) / 1e6:.1f} |")
+        w[src] = dict(source_sha=kernel_source_sha(src),
+                      hbm_bytes_per_launch=int(r["fetch_kib"] * 1024 * rf + r["write_kib"] * 1024 * wf),
+                      fetch_kib=r["fetch_kib"], write_kib=r["write_kib"], read_factor=rf, write_factor=wf,
+                      summary=f"profiles/{workload}_step_hbm_traffic.md")
+    print(f"\nread factor {rf:.3f}, write factor {wf:.3f}")
+    json.dump(allrec, open(p, "w"), indent=1)
 
 
 def algorithmic(cfg, lens):
@@ -369,6 +422,9 @@ def cpu_baseline(inp, n_single, n_multi, gpu_pass, step):
 
 def main():
     args = parse()
+    if args.counters:
+        summarize_counters(*args.counters, args.config)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
               file=sys.stderr)
@@ -481,7 +537,9 @@ def main():
     dk = alg[dom]
     t_dom = kernel_ms[dom] * 1e-3
     hbm_bound = dk["bytes"] / (HBM_PEAK_GBS * 1e9) >= dk["flops"] / (BF16_PEAK_TFLOPS * 1e12)
-    src = {"indexer": "indexer.hip", "topk": "topk.hip", "decode": "mla_decode.hip", "merge": "lse_merge.hip"}[dom]
+    src = {"indexer": "indexer.hip", "topk": "topk.hip",
+           "decode": "mla_decode_f8.hip" if cfg.cache_dtype == 2 and cfg.q_dtype == 1 else "mla_decode.hip",
+           "merge": "lse_merge.hip"}[dom]
     traffic = measured_traffic(src, cfg.name)
     if hbm_bound:
         achieved = dk["bytes"] / t_dom / 1e9
