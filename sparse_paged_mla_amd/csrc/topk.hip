@@ -48,6 +48,7 @@
 #include "topk_layout.h"
 
 #include <algorithm>
+#include <type_traits>
 #include <atomic>
 #include <chrono>
 #include <mutex>
@@ -606,11 +607,109 @@ __device__ __forceinline__ bool select_k_best(const uint2* lc, const float* __re
   return true;
 }
 
+// select_k_best over a list held in registers: thread tid holds list
+// entries [j0, j0 + n_mine) in e[0 .. n_mine) (j0 = tid * per, per the same
+// in every thread, so thread order is list order), each as (key, index).
+// Same rounds, bin ranking, tie rounds, tau_max check and ordered output as
+// select_k_best, without reading the list again from memory.  Called by all
+// kFinThreads threads; barriers inside.
+constexpr int kRegCand = kCandLds / kFinThreads;  // list entries a thread can hold
+template <int P>
+__device__ __forceinline__ bool select_regs(const uint2 (&e)[P], uint32_t n_mine, uint32_t cmin, uint32_t cmax,
+                                            uint32_t tau_max, int32_t k, int32_t* __restrict__ out, uint32_t* h,
+                                            uint32_t* tmp, uint32_t* res, uint2* bin_list, uint32_t* bin_cnt) {
+  const int tid = threadIdx.x;
+  uint32_t need = (uint32_t)k;
+  uint32_t kpre = 0, kmask = 0;
+  const int hi0 = first_round_top(cmin, cmax, &kpre, &kmask);
+  uint32_t T = 0, I = 0xFFFFFFFFu;
+  bool done = false;
+  if (tid == 0) *bin_cnt = 0u;
+  for (int hi = hi0; hi > 0 && !done; hi -= 11) {
+    const int lo = max(hi - 11, 0);
+    const uint32_t wmask = (1u << (hi - lo)) - 1u;
+    for (int i = tid; i < kBins; i += kFinThreads) h[i] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < P; ++i)
+      if (i < (int)n_mine && (e[i].x & kmask) == kpre) atomicAdd(&h[(e[i].x >> lo) & wmask], 1u);
+    __syncthreads();
+    find_bin_desc<kBins, kFinThreads>(h, need, tmp, res);
+    const uint32_t bin = res[0];
+    kpre |= bin << lo;
+    kmask |= wmask << lo;
+    need -= res[1];
+    const uint32_t in_bin = h[bin];
+    __syncthreads();  // h and res are read before the next round rewrites them
+    if (in_bin <= 64u) {
+#pragma unroll
+      for (int i = 0; i < P; ++i)
+        if (i < (int)n_mine && (e[i].x & kmask) == kpre) bin_list[atomicAdd(bin_cnt, 1u)] = e[i];
+      __syncthreads();
+      if (tid < 64) {
+        const bool mine = tid < (int)in_bin;
+        const uint2 b = mine ? bin_list[tid] : make_uint2(0u, 0u);
+        uint32_t rank = 0;
+        for (uint32_t m = 0; m < in_bin; ++m) {
+          const uint32_t ox = (uint32_t)__builtin_amdgcn_readlane((int)b.x, (int)m);
+          const uint32_t oy = (uint32_t)__builtin_amdgcn_readlane((int)b.y, (int)m);
+          rank += (ox > b.x || (ox == b.x && oy < b.y)) ? 1u : 0u;
+        }
+        if (mine && rank == need - 1) { res[0] = b.x; res[1] = b.y; }
+      }
+      __syncthreads();
+      T = res[0];
+      I = res[1];
+      done = true;
+    }
+  }
+  if (!done) {
+    // T = kpre; among keys equal to T the `need` lowest indices are taken.
+    T = kpre;
+    uint32_t n_eq_local = 0;
+#pragma unroll
+    for (int i = 0; i < P; ++i) n_eq_local += (i < (int)n_mine && e[i].x == T) ? 1u : 0u;
+    const uint32_t n_eq = block_incl_scan<kFinThreads>(n_eq_local, tmp);
+    if (tid == kFinThreads - 1) res[0] = n_eq;
+    __syncthreads();
+    const uint32_t total_eq = res[0];
+    __syncthreads();
+    if (total_eq > need) {
+      uint32_t ipre = 0, imask = 0;
+      for (int hi = 31; hi > 0; hi -= 11) {
+        const int lo = max(hi - 11, 0);
+        const uint32_t wmask = (1u << (hi - lo)) - 1u;
+        for (int i = tid; i < kBins; i += kFinThreads) h[i] = 0u;
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < P; ++i)
+          if (i < (int)n_mine && e[i].x == T && (e[i].y & imask) == ipre) atomicAdd(&h[(e[i].y >> lo) & wmask], 1u);
+        __syncthreads();
+        find_bin_asc<kBins, kFinThreads>(h, need, tmp, res);
+        ipre |= res[0] << lo;
+        imask |= wmask << lo;
+        need -= res[1];
+      }
+      I = ipre;
+    }
+  }
+  if (T < tau_max) return false;  // uniform: T is the same in every thread
+  auto picked = [&](const uint2 x) { return x.x > T || (x.x == T && x.y <= I); };
+  uint32_t mine = 0;
+#pragma unroll
+  for (int i = 0; i < P; ++i) mine += (i < (int)n_mine && picked(e[i])) ? 1u : 0u;
+  uint32_t pos = block_incl_scan<kFinThreads>(mine, tmp) - mine;
+#pragma unroll
+  for (int i = 0; i < P; ++i) {
+    if (i < (int)n_mine && picked(e[i]) && pos < (uint32_t)k) out[pos++] = (int32_t)e[i].y;
+  }
+  return true;
+}
+
 __global__ __launch_bounds__(kFinThreads) void topk_finish_kernel(const float* __restrict__ scores, int64_t stride,
                                                                   const int32_t* __restrict__ lens, int64_t max_len,
                                                                   int32_t k, TopkWs ws, int32_t* __restrict__ out_idx,
                                                                   int32_t* __restrict__ status) {
-  __shared__ uint32_t big[kFinLdsWords];   // gathered candidates (uint2)
   __shared__ uint32_t h[kBins];
   __shared__ __attribute__((aligned(16))) uint32_t tmp[kFinThreads / 64];
   __shared__ uint32_t res[2];
@@ -657,43 +756,59 @@ __global__ __launch_bounds__(kFinThreads) void topk_finish_kernel(const float* _
   __syncthreads();
   const uint32_t n_cand = res[0];
   const bool whole = ovf != 0u || n_cand < (uint32_t)k || n_cand > (uint32_t)kCandLds || n_act > kFinThreads;
-  const uint32_t n_c = whole ? (uint32_t)L : n_cand;
   const float* srow = scores + (int64_t)b * stride;
-  uint2* lc = reinterpret_cast<uint2*>(big);
   if (!whole) {
-    // List position j = tid + m * kFinThreads comes from the last chunk c
-    // with coff[c] <= j (chunks without candidates share their offset with
-    // the next chunk, so the last such c is the one that holds j).
-    constexpr int kG = kCandLds / kFinThreads;
-    uint2 e[kG];
-#pragma unroll
-    for (int m = 0; m < kG; ++m) {
-      const uint32_t j = (uint32_t)(tid + m * kFinThreads);
-      if (j < n_cand) {
+    // Thread tid takes list positions [j0, j0 + per) straight into
+    // registers: the chunk of j0 by binary search over the chunk offsets
+    // (chunks without candidates share their offset with the next chunk, so
+    // the last chunk c with coff[c] <= j is the one that holds j), then on
+    // through the following chunks.
+    // The register arrays are sized to the run (4, 8 or 16 entries): each
+    // pass of the selection runs every entry slot in every lane, and a
+    // workgroup of 16 waves runs four of them on each SIMD.
+    const uint32_t per = (n_cand + kFinThreads - 1) / kFinThreads;  // <= kRegCand
+    const uint32_t j0 = min(n_cand, tid * per), n_mine = min(n_cand, j0 + per) - j0;
+    const uint32_t cmin = s_mm[0], cmax = s_mm[1], tau_max = s_tmax;
+    auto gather_select = [&](auto p_tag) __attribute__((always_inline)) -> bool {
+      constexpr int P = decltype(p_tag)::value;
+      uint2 e[P];
+      int c = 0;
+      {
         int lo = 0, hi = n_act - 1;
         while (lo < hi) {
           const int mid = (lo + hi + 1) >> 1;
-          if (coff[mid] <= j) lo = mid; else hi = mid - 1;
+          if (coff[mid] <= j0) lo = mid; else hi = mid - 1;
         }
-        e[m] = ws.cand[(slot0 + lo) * kTkSlice + (j - coff[lo])];
-        e[m].x = order_key(__uint_as_float(e[m].x));
+        c = lo;
       }
-    }
+      uint32_t next = c + 1 < n_act ? coff[c + 1] : n_cand;
 #pragma unroll
-    for (int m = 0; m < kG; ++m) {
-      const uint32_t j = (uint32_t)(tid + m * kFinThreads);
-      if (j < n_cand) lc[j] = e[m];
-    }
+      for (int i = 0; i < P; ++i) {
+        if (i < (int)n_mine) {
+          const uint32_t j = j0 + i;
+          while (j >= next) {
+            ++c;
+            next = c + 1 < n_act ? coff[c + 1] : n_cand;
+          }
+          e[i] = ws.cand[(slot0 + c) * kTkSlice + (j - coff[c])];
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < P; ++i)
+        if (i < (int)n_mine) e[i].x = order_key(__uint_as_float(e[i].x));
+      return select_regs<P>(e, n_mine, cmin, cmax, tau_max, k, out, h, tmp, res, bin_list, &bin_cnt);
+    };
+    const bool done = per <= 4   ? gather_select(std::integral_constant<int, 4>{})
+                      : per <= 8 ? gather_select(std::integral_constant<int, 8>{})
+                                 : gather_select(std::integral_constant<int, kRegCand>{});
+    if (done) return;
+    __syncthreads();
   }
-  const uint32_t cmin = s_mm[0], cmax = s_mm[1], tau_max = s_tmax;
+  // The whole request, read from the scores.
   if (tid == 0) bin_cnt = 0u;
   __syncthreads();
-  if (!select_k_best(lc, srow, whole, n_c, cmin, cmax, tau_max, k, out, h, tmp, res, bin_list, &bin_cnt)) {
-    __syncthreads();
-    if (tid == 0) bin_cnt = 0u;
-    __syncthreads();
-    select_k_best(lc, srow, true, (uint32_t)L, 0u, 0u, 0u, k, out, h, tmp, res, bin_list, &bin_cnt);
-  }
+  select_k_best(nullptr, srow, true, (uint32_t)L, 0u, 0u, 0u, k, out, h, tmp, res, bin_list, &bin_cnt);
+
 }
 
 // Single-launch form for rows of up to kFusedMaxLen keys: one workgroup per
@@ -820,8 +935,27 @@ __global__ __launch_bounds__(kFinThreads) void topk_fused_kernel(const float* __
     }
     __syncthreads();
   }
-  select_k_best(lc, srow, whole, whole ? (uint32_t)L : n_cand, c_mm[0], c_mm[1], tau, k, out, h, tmp, res, bin_list,
-                &bin_cnt);
+  if (!whole) {
+    // Each thread takes its run of the packed list into registers.
+    const uint32_t per = (n_cand + kFinThreads - 1) / kFinThreads;  // <= kRegCand
+    const uint32_t j0 = min(n_cand, tid * per), n_mine = min(n_cand, j0 + per) - j0;
+    auto load_select = [&](auto p_tag) __attribute__((always_inline)) -> bool {
+      constexpr int P = decltype(p_tag)::value;  // sized to the run, as in the finish
+      uint2 e[P];
+#pragma unroll
+      for (int i = 0; i < P; ++i)
+        if (i < (int)n_mine) e[i] = lc[j0 + i];
+      return select_regs<P>(e, n_mine, c_mm[0], c_mm[1], tau, k, out, h, tmp, res, bin_list, &bin_cnt);
+    };
+    const bool done = per <= 4   ? load_select(std::integral_constant<int, 4>{})
+                      : per <= 8 ? load_select(std::integral_constant<int, 8>{})
+                                 : load_select(std::integral_constant<int, kRegCand>{});
+    if (done) return;
+    __syncthreads();
+    if (tid == 0) bin_cnt = 0u;
+    __syncthreads();
+  }
+  select_k_best(lc, srow, true, (uint32_t)L, 0u, 0u, 0u, k, out, h, tmp, res, bin_list, &bin_cnt);
 }
 
 // ---- allocation-free form (topk_select_noalloc): the workspace is this
