@@ -2,7 +2,9 @@
 // the result over the union of the splits (exact online-softmax algebra).
 // One wave per (request, head) row: every lane reads the row's num_splits
 // lse values, forms the weights exp(lse_s - lse), and streams float4 slices of
-// the d-dim partials.  HBM-bound; the partial traffic is the whole cost.
+// the d-dim partials.  HBM-bound; the partial traffic is the whole cost, so
+// the partials (read once) and the result (written once) go through
+// non-temporal loads and stores.
 #include "common.h"
 #include "launch.h"
 
@@ -30,13 +32,14 @@ __global__ __launch_bounds__(kMergeThreads) void lse_merge_kernel(const float* _
     d = 512;
   }
   // Partial slices of this lane (SP > 0): dims 4*lane + 256*i of split sp.
-  float4 pv[SP > 0 ? SP : 1][2];
+  f32x4 pv[SP > 0 ? SP : 1][2];
   if constexpr (SP > 0) {
 #pragma unroll
     for (int sp = 0; sp < SP; ++sp)
 #pragma unroll
       for (int i = 0; i < 2; ++i)
-        pv[sp][i] = *reinterpret_cast<const float4*>(o_part + ((b * SP + sp) * n_heads + h) * 512 + lane * 4 + 256 * i);
+        pv[sp][i] = __builtin_nontemporal_load(
+            reinterpret_cast<const f32x4*>(o_part + ((b * SP + sp) * n_heads + h) * 512 + lane * 4 + 256 * i));
   }
   // Lane s < splits holds lse of split s.
   float my = -INFINITY;
@@ -65,15 +68,14 @@ __global__ __launch_bounds__(kMergeThreads) void lse_merge_kernel(const float* _
   if constexpr (SP > 0) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int sp = 0; sp < SP; ++sp) {
         const float ws = wsh[wid][sp];
         if (ws == 0.f) continue;  // an empty split: its partial (perhaps never written) is not used
-        const float4 v = pv[sp][i];
-        acc.x += ws * v.x; acc.y += ws * v.y; acc.z += ws * v.z; acc.w += ws * v.w;
+        acc += ws * pv[sp][i];
       }
-      *reinterpret_cast<float4*>(orow + lane * 4 + 256 * i) = acc;
+      __builtin_nontemporal_store(acc, reinterpret_cast<f32x4*>(orow + lane * 4 + 256 * i));
     }
   } else {
     for (int i = lane * 4; i < d; i += 256) {

@@ -66,7 +66,8 @@ constexpr int kTileBytes = kTileTok * kRS;        // 19456
 constexpr int kRowLoads = kTileBytes / 1024;      // 19 wave loads of 1 KiB per tile
 constexpr int kLoads = 5;                         // per value wave per tile: 19 row loads + 1 scale load
 constexpr int kNB = 6;                            // tile buffers
-constexpr int kPF = 4;                            // tiles requested ahead of the scored one
+constexpr int kPF = 2;                            // tiles requested ahead of the scored one (2 measured
+                                                  // faster than 3 or 4: the loads still land in time)
 constexpr int kSeg = 1024;                        // positions resolved at once
 constexpr int kHeadsWg = 64;
 constexpr int kPStride = 40;                      // bf16 per weight row (32 tokens + 8 pad)
