@@ -38,6 +38,8 @@ struct DecodeArgs {
 int launch_decode(const DecodeArgs& a, hipStream_t stream);
 // FP8 cache, bf16 query, 512 + 64 dims (mla_decode_f8.hip).
 int launch_decode_f8(const DecodeArgs& a, hipStream_t stream);
+// bf16 cache, bf16 query, 512 + 64 dims (mla_decode_bf16.hip).
+int launch_decode_bf16(const DecodeArgs& a, hipStream_t stream);
 
 struct MergeArgs {
   const float* o_part; const float* lse_part; int32_t batch, num_splits, n_heads, d; float* o; float* lse;

@@ -1,9 +1,9 @@
 // mla_paged_decode kernels: split-KV MLA decode over the selected tokens of
 // the paged latent cache, both contractions on MFMA.  mla_decode_kernel
-// (bf16 or fp32 caches, and the small fp32 query shapes) widens each tile
-// once into LDS; an FP8 cache with a bf16 query and 576-dim rows goes to the
-// role-specialised kernel of mla_decode_f8.hip, which keeps the tile in LDS
-// as FP8 codes.
+// (the fp32 query with 64 + 16 dims, over fp32, bf16 or FP8 caches) widens
+// each tile once into LDS; a bf16 query with 576-dim rows goes to the
+// role-specialised kernels of mla_decode_f8.hip (FP8 cache, the tile kept in
+// LDS as codes) and mla_decode_bf16.hip (bf16 cache).
 //
 // Workgroup = (request b, split s, group of 64 query heads); 8 waves.  A pair
 // of waves shares 16 heads: each wave of the pair contracts half of the row
@@ -466,7 +466,7 @@ static int launch_one(const DecodeArgs& a, hipStream_t stream) {
 int launch_decode(const DecodeArgs& a, hipStream_t s) {
   const int D = a.d_latent + a.d_rope;
   if (a.q_dtype == kBF16 && D == 576 && a.d_latent == 512) {
-    if (a.kv_dtype == kBF16) return launch_one<OpBF16, kBF16, 18, 32>(a, s);
+    if (a.kv_dtype == kBF16) return launch_decode_bf16(a, s);
     if (a.kv_dtype == kFP8) return launch_decode_f8(a, s);
     return -2;
   }

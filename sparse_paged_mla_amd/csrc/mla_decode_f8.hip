@@ -49,13 +49,13 @@
 // quantity as the running-max form, and the accumulators are never rescaled.
 #include "common.h"
 #include "launch.h"
+#include "decode_ws.h"
 
 #include <utility>
 
-#pragma clang diagnostic ignored "-Winline-asm"  // m0 is clobbered on purpose: the direct loads set it
-
 namespace spmla {
 namespace {
+using namespace ws;
 
 constexpr int kThreads = 512;
 constexpr int kTileTok = 32;
@@ -88,65 +88,7 @@ typedef __attribute__((address_space(3))) void lds_void;
 __device__ __attribute__((aligned(16))) uint8_t g_zero_row[kD];
 __device__ __attribute__((aligned(16))) float g_unit_scale[4] = {1.f, 1.f, 1.f, 1.f};
 
-template <class F, int... I>
-__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
-  (f(std::integral_constant<int, I>{}), ...);
-}
-template <int N, class F>
-__device__ __forceinline__ void static_for(F&& f) {
-  static_for_impl(f, std::make_integer_sequence<int, N>{});
-}
-
 __device__ __forceinline__ int swz(int r) { return ((r >> 3) ^ (r >> 4)) & 1; }
-
-// Wait until at most N vector-memory operations of this wave are in flight
-// (gfx9 s_waitcnt: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt left at
-// their maxima).  The empty asm statements keep memory operations from being
-// moved across the wait.
-template <int N>
-__device__ __forceinline__ void vm_wait() {
-  static_assert(N >= 0 && N <= 63, "vmcnt");
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-  asm volatile("" ::: "memory");
-}
-
-// Workgroup barrier: this wave's LDS reads and writes complete, then
-// s_barrier.  No fence: direct loads in flight are left alone.
-__device__ __forceinline__ void wg_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-// Direct loads into LDS: each lane's 16 (or 4) bytes at gptr land at LDS
-// byte address lds + 16 * lane (4 * lane) of the issuing wave; lds must be
-// the same in every lane.  Written as asm so that the compiler does not
-// treat later LDS reads as waiting on them (it would wait for every load in
-// flight); the waits are the explicit vm_wait calls.  An asm load issued
-// before one of the compiler's own loads only makes the compiler's count
-// for that load conservative, since loads complete in order.
-// (An SALU write of M0 needs one wait state before an instruction that
-// reads it for an LDS address; the compiler inserts no hazard padding inside
-// asm, hence the s_nop.)  No memory clobber: the buffer a load fills is never
-// the one being read in the same phase, and the waits and barriers around
-// the loads carry the clobbers that order them.
-__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds) : "m0");
-}
-__device__ __forceinline__ void dma4(const void* gptr, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(gptr), "s"(lds) : "m0");
-}
-template <class T>
-__device__ __forceinline__ uint32_t lds_addr(T* p) {
-  return (uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) T*)p);
-}
-
-__device__ __forceinline__ int xcd_remap(int bid, int n) {
-  const int q = n >> 3, r = n & 7;
-  const int xcd = bid & 7, slot = bid >> 3;
-  return xcd < r ? xcd * (q + 1) + slot : r * (q + 1) + (xcd - r) * q + slot;
-}
 
 // Writes this lane's 32 bf16 values (w[i] holds values 2i, low half, and
 // 2i + 1) as v = 2^(E-7) * (hi + lo/16), hi and lo e4m3 codes, where
