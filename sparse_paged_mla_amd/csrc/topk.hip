@@ -181,19 +181,26 @@ __device__ void find_bin_desc(const uint32_t* h, uint32_t need, uint32_t* tmp, u
   constexpr int PER = NB / NT;
   const int tid = threadIdx.x;
   const int hi = NB - tid * PER;  // thread 0 owns the top PER bins
-  uint32_t mine = 0;
+  uint32_t c[PER], mine = 0;      // the counts stay in registers for the search below
 #pragma unroll
-  for (int j = 1; j <= PER; ++j) mine += h[hi - j];
+  for (int j = 0; j < PER; ++j) {
+    c[j] = h[hi - 1 - j];
+    mine += c[j];
+  }
   if (tid == 0) { out[0] = 0u; out[1] = 0u; }
   const uint32_t incl = block_incl_scan<NT>(mine, tmp);
   const uint32_t excl = incl - mine;
   if (excl < need && need <= incl) {
-    uint32_t run = excl;
-    for (int j = 1; j <= PER; ++j) {
-      const uint32_t c = h[hi - j];
-      if (run + c >= need) { out[0] = (uint32_t)(hi - j); out[1] = run; break; }
-      run += c;
+    // the first j (from the top) whose running sum reaches need
+    uint32_t run = excl, bin = 0, above = 0;
+    bool found = false;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      if (!found && run + c[j] >= need) { bin = (uint32_t)(hi - 1 - j); above = run; found = true; }
+      run += c[j];
     }
+    out[0] = bin;
+    out[1] = above;
   }
   __syncthreads();
 }
@@ -204,19 +211,25 @@ __device__ void find_bin_asc(const uint32_t* h, uint32_t need, uint32_t* tmp, ui
   constexpr int PER = NB / NT;
   const int tid = threadIdx.x;
   const int lo = tid * PER;
-  uint32_t mine = 0;
+  uint32_t c[PER], mine = 0;
 #pragma unroll
-  for (int j = 0; j < PER; ++j) mine += h[lo + j];
+  for (int j = 0; j < PER; ++j) {
+    c[j] = h[lo + j];
+    mine += c[j];
+  }
   if (tid == 0) { out[0] = 0u; out[1] = 0u; }
   const uint32_t incl = block_incl_scan<NT>(mine, tmp);
   const uint32_t excl = incl - mine;
   if (excl < need && need <= incl) {
-    uint32_t run = excl;
+    uint32_t run = excl, bin = 0, below = 0;
+    bool found = false;
+#pragma unroll
     for (int j = 0; j < PER; ++j) {
-      const uint32_t c = h[lo + j];
-      if (run + c >= need) { out[0] = (uint32_t)(lo + j); out[1] = run; break; }
-      run += c;
+      if (!found && run + c[j] >= need) { bin = (uint32_t)(lo + j); below = run; found = true; }
+      run += c[j];
     }
+    out[0] = bin;
+    out[1] = below;
   }
   __syncthreads();
 }
@@ -224,8 +237,10 @@ __device__ void find_bin_asc(const uint32_t* h, uint32_t need, uint32_t* tmp, ui
 // Threshold from this thread's N keys (those with in[j]; `need` in [1, their
 // count over the workgroup]): the lower edge of the bin holding the key of
 // rank `need` from the top, in a histogram over the 11 bits below the bits
-// all the keys share.  Called by all NT threads; barriers inside.
-template <int NT, int N>
+// all the keys share.  Called by all NT threads; barriers inside.  With
+// kCleared the caller has already zeroed h and set s_mm to (~0, 0), with a
+// barrier after.
+template <int NT, int N, bool kCleared = false>
 __device__ __forceinline__ uint32_t tau_of(const uint32_t (&key)[N], const bool (&in)[N], uint32_t need, uint32_t* h,
                                            uint32_t* tmp, uint32_t* res, uint32_t* s_mm) {
   const int tid = threadIdx.x;
@@ -237,9 +252,11 @@ __device__ __forceinline__ uint32_t tau_of(const uint32_t (&key)[N], const bool 
   }
   lo_k = wave_min_u32(lo_k);
   hi_k = wave_max_u32(hi_k);
-  if (tid == 0) { s_mm[0] = 0xFFFFFFFFu; s_mm[1] = 0u; }
-  for (int i = tid; i < kBins; i += NT) h[i] = 0u;
-  __syncthreads();
+  if constexpr (!kCleared) {
+    if (tid == 0) { s_mm[0] = 0xFFFFFFFFu; s_mm[1] = 0u; }
+    for (int i = tid; i < kBins; i += NT) h[i] = 0u;
+    __syncthreads();
+  }
   if ((tid & 63) == 0) { atomicMin(&s_mm[0], lo_k); atomicMax(&s_mm[1], hi_k); }
   __syncthreads();
   uint32_t pre, mask;
@@ -324,9 +341,9 @@ __device__ __forceinline__ uint32_t request_tau(const float* __restrict__ s, int
 // compares scores against the float key_floor(tau'), which admits the same
 // keys; NaN scores are never candidates (should that leave fewer than k, the
 // finish selects over the whole request).
-constexpr int kTauSpin = 4000;  // polls of the published threshold (s_sleep 4 between them)
+constexpr int kTauSpin = 8000;  // polls of the published threshold (s_sleep 1 between them, four in flight)
 
-template <int NT>
+template <int NT, bool kCleared = false>
 __device__ __forceinline__ uint32_t sample_tau(const float (&sv)[kSampleRuns], int32_t ml, int32_t L, int32_t k, uint32_t* h,
                                                uint32_t* tmp, uint32_t* res, uint32_t* s_mm) {
   uint32_t skey[kSampleRuns];
@@ -339,7 +356,7 @@ __device__ __forceinline__ uint32_t sample_tau(const float (&sv)[kSampleRuns], i
     skey[j] = order_key(sv[j]);
     in[j] = r0 + (int)threadIdx.x < L;
   }
-  return tau_of<NT, kSampleRuns>(skey, in, sample_need(k, n_s, L), h, tmp, res, s_mm);  // barriers inside
+  return tau_of<NT, kSampleRuns, kCleared>(skey, in, sample_need(k, n_s, L), h, tmp, res, s_mm);  // barriers inside
 }
 
 __global__ __launch_bounds__(kTkThreads) void topk_collect_kernel(const float* __restrict__ scores, int64_t stride,
@@ -373,9 +390,16 @@ __global__ __launch_bounds__(kTkThreads) void topk_collect_kernel(const float* _
     if (ml <= kTkChunk) return;  // every request fits one chunk
     float sv[kSampleRuns];
     load_sample(sv);
+    // While the sample loads: clear the histogram (a barrier that waits
+    // for LDS only, not for the loads in flight).
+    for (int i = tid; i < kBins; i += kTkThreads) h[i] = 0u;
+    if (tid == 0) { s_mm[0] = 0xFFFFFFFFu; s_mm[1] = 0u; }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
     const int32_t L = lens[b];
     if (!len_ok(L, max_len) || L <= k || L <= kTkChunk) return;
-    const uint32_t tau = sample_tau<kTkThreads>(sv, ml, L, k, h, tmp, res, s_mm);
+    const uint32_t tau = sample_tau<kTkThreads, true>(sv, ml, L, k, h, tmp, res, s_mm);
     if (tid == 0)
       __hip_atomic_store(ws.tau_pub + b, ((unsigned long long)ws.tag << 32) | tau, __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
@@ -413,17 +437,37 @@ __global__ __launch_bounds__(kTkThreads) void topk_collect_kernel(const float* _
     tau = tau_of<kTkThreads, kTkPer>(key, in, (uint32_t)k, h, tmp, res, s_mm);  // barriers inside
   } else {
     if (tid == 0) {
-      // The first poll's load returns after the chunk's loads (loads
+      // The first polls' loads return after the chunk's loads (loads
       // complete in order), by when the tau block has usually published.
+      // Four polls are kept in flight: each check waits for the oldest
+      // only, and its slot is refilled at once, so a published word is seen
+      // about one load latency after it lands instead of up to two.
+      auto poll = [&]() { return __hip_atomic_load(ws.tau_pub + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
       uint32_t got = 0, t = 0;
-      for (int it = 0; it < kTauSpin; ++it) {
-        const unsigned long long w = __hip_atomic_load(ws.tau_pub + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if ((uint32_t)(w >> 32) == ws.tag) {
+      auto check = [&](unsigned long long w) {
+        if (!got && (uint32_t)(w >> 32) == ws.tag) {
           t = (uint32_t)w;
           got = 1;
-          break;
         }
-        __builtin_amdgcn_s_sleep(4);
+      };
+      // Two sets of four slots take turns (one is checked while the other
+      // is refilled), so no loaded value has to move between registers.
+      unsigned long long wa[4], wb[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) wa[q] = poll();
+      for (int it = 0; it < kTauSpin / 8 && !got; ++it) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          __builtin_amdgcn_s_sleep(1);
+          wb[q] = poll();
+          check(wa[q]);
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          __builtin_amdgcn_s_sleep(1);
+          wa[q] = poll();
+          check(wb[q]);
+        }
       }
       res[0] = t;
       res[1] = got;
