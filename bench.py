@@ -52,7 +52,8 @@ def parse():
 
 # Kernel-name fragment -> source file whose HBM traffic it measures.
 COUNTER_SOURCES = [("indexer_kernel", "indexer.hip"), ("topk_", "topk.hip"), ("mla_decode_f8ws", "mla_decode_f8.hip"),
-                   ("mla_decode_kernel", "mla_decode.hip"), ("lse_merge", "lse_merge.hip"),
+                   ("mla_decode_bf16ws", "mla_decode_bf16.hip"), ("mla_decode_kernel", "mla_decode.hip"),
+                   ("lse_merge", "lse_merge.hip"),
                    ("cache_append", "cache_append.hip")]
 CALIB_BYTES = 256 << 20  # the plain device copy --profile-only adds
 
@@ -538,7 +539,8 @@ def main():
     t_dom = kernel_ms[dom] * 1e-3
     hbm_bound = dk["bytes"] / (HBM_PEAK_GBS * 1e9) >= dk["flops"] / (BF16_PEAK_TFLOPS * 1e12)
     src = {"indexer": "indexer.hip", "topk": "topk.hip",
-           "decode": "mla_decode_f8.hip" if cfg.cache_dtype == 2 and cfg.q_dtype == 1 else "mla_decode.hip",
+           "decode": ("mla_decode.hip" if cfg.q_dtype != 1 else
+                      "mla_decode_f8.hip" if cfg.cache_dtype == 2 else "mla_decode_bf16.hip"),
            "merge": "lse_merge.hip"}[dom]
     traffic = measured_traffic(src, cfg.name)
     if hbm_bound:
