@@ -277,35 +277,43 @@ def test_fp8_growing_logits_recompute():
         _check_full(inp, splits, "growing logits fp8")
 
 
+# The two role-specialised decode kernels: FP8 cache (c3f) and bf16 cache (c3).
+SPARSE_CACHES = [pytest.param("c3f", id="fp8"), pytest.param("c3", id="bf16")]
+
+
+@pytest.mark.parametrize("name", SPARSE_CACHES)
 @pytest.mark.parametrize("n_heads", [8, 40, 72])
-def test_fp8_partial_head_groups(n_heads):
+def test_partial_head_groups(name, n_heads):
     """Head counts that leave waves, and lanes within a wave, without a head."""
     _lib()
-    cfg = gen.CONFIGS["c3f"].with_(batch=3, n_heads=n_heads)
-    _check_full(gen.make_inputs(cfg, lens=[70, 2500, 5000]), 3, f"fp8 {n_heads} heads")
+    cfg = gen.CONFIGS[name].with_(batch=3, n_heads=n_heads)
+    _check_full(gen.make_inputs(cfg, lens=[70, 2500, 5000]), 3, f"{name} {n_heads} heads")
 
 
+@pytest.mark.parametrize("cache", [pytest.param(gen.FP8, id="fp8"), pytest.param(gen.BF16, id="bf16")])
 @pytest.mark.parametrize("splits", [1, 2, 5])
-def test_fp8_dense_multi_segment(splits):
-    """Dense attention on an FP8 cache: splits longer than one segment table
-    (1024 positions) and a ragged last tile."""
+def test_dense_multi_segment(cache, splits):
+    """Dense attention: splits longer than one segment table (1024
+    positions) and a ragged last tile."""
     _lib()
-    cfg = gen.CONFIGS["c2"].with_(batch=2, cache_dtype=gen.FP8)
-    _check_full(gen.make_inputs(cfg, lens=[2500, 4133]), splits, "dense fp8")
+    cfg = gen.CONFIGS["c2"].with_(batch=2, cache_dtype=cache)
+    _check_full(gen.make_inputs(cfg, lens=[2500, 4133]), splits, f"dense cache {cache}")
 
 
-def test_fp8_empty_splits():
+@pytest.mark.parametrize("name", SPARSE_CACHES)
+def test_empty_splits(name):
     """A small top-k spread over many splits leaves whole splits empty."""
     _lib()
-    cfg = gen.CONFIGS["c3f"].with_(batch=2, topk=32)
-    _check_full(gen.make_inputs(cfg, lens=[40, 3000]), 4, "fp8 empty splits")
+    cfg = gen.CONFIGS[name].with_(batch=2, topk=32)
+    _check_full(gen.make_inputs(cfg, lens=[40, 3000]), 4, f"{name} empty splits")
 
 
 # ------------------------------------------------------------ fault handling
 
-def test_device_faults_flag_only_the_offending_request():
+@pytest.mark.parametrize("name", SPARSE_CACHES)
+def test_device_faults_flag_only_the_offending_request(name):
     spm = _lib()
-    cfg = gen.CONFIGS["c3f"].with_(batch=4)
+    cfg = gen.CONFIGS[name].with_(batch=4)
     inp = gen.make_inputs(cfg, lens=[500, 600, 700, 800])
     bt = inp.block_table.copy()
     bt[1, 2] = inp.num_pages + 5      # request 1: page id out of range
