@@ -4,19 +4,23 @@
 // specialised by role so that vector work on one wave of a SIMD overlaps
 // matrix work on the other.
 //
-// Workgroup = (request b, split s, group of 64 query heads); 8 waves.
+// Workgroup = (request b, split s, group of HW query heads); 8 waves.  HW is
+// 64, or 32 when a call has so few (request, split) pairs that 64-head
+// groups would leave more than half of the CUs without a workgroup (twice
+// the workgroups then share the same tiles, each with half the matrix work).
 //  - Waves 0-3, score waves: wave (hq, th) holds the query of heads
-//    32hq..32hq+31 of the group and computes, for every 32-token tile, the
-//    scores of those heads against the tile's tokens 16th..16th+15 over all
-//    576 dims, then their softmax weights.  Latent dims: the scaled FP8 MFMA
-//    (16x16x128, tokens on M, heads on N) against the query written as two
-//    scaled e4m3 terms per 128-dim block (the cache codes are used as they
-//    are); rope dims: the bf16 MFMA with the codes widened exactly in
-//    registers.  The weights go to LDS as bf16, already multiplied by each
-//    token's FP8 scale.
-//  - Waves 4-7, value waves: wave (hq, dh) accumulates O[32 heads x 256 dims]
-//    (heads 32hq.., dims 256dh..) += P[32 heads x 32 tokens] . V[32 tokens x
-//    256 dims] on the 32x32x16 bf16 MFMA, one tile behind the score waves.
+//    hq*HW/2.. (HW/2 heads) of the group and computes, for every 32-token
+//    tile, the scores of those heads against the tile's tokens
+//    16th..16th+15 over all 576 dims, then their softmax weights.  Latent
+//    dims: the scaled FP8 MFMA (16x16x128, tokens on M, heads on N) against
+//    the query written as two scaled e4m3 terms per 128-dim block (the cache
+//    codes are used as they are); rope dims: the bf16 MFMA with the codes
+//    widened exactly in registers.  The weights go to LDS as bf16, already
+//    multiplied by each token's FP8 scale.
+//  - Waves 4-7, value waves: each accumulates O[32 heads x 512 * 32 / HW
+//    dims] += P[32 heads x 32 tokens] . V[32 tokens x those dims] on the
+//    32x32x16 bf16 MFMA, one tile behind the score waves (64 heads: two head
+//    tiles x two dim halves; 32 heads: one head tile x four dim quarters).
 //    V comes from the same LDS tile through gfx950's 8-bit transposing LDS
 //    read and is widened exactly to bf16 in registers.  These waves also
 //    fetch the tiles: every lane's 16-byte piece of a tile goes straight from
@@ -51,6 +55,7 @@
 #include "launch.h"
 #include "decode_ws.h"
 
+#include <atomic>
 #include <utility>
 
 namespace spmla {
@@ -65,15 +70,13 @@ constexpr int kRowChunks = kRS / 16;              // 38 chunk slots per row
 constexpr int kTileBytes = kTileTok * kRS;        // 19456
 constexpr int kRowLoads = kTileBytes / 1024;      // 19 wave loads of 1 KiB per tile
 constexpr int kLoads = 5;                         // per value wave per tile: 19 row loads + 1 scale load
-constexpr int kNB = 6;                            // tile buffers
 constexpr int kPF = 2;                            // tiles requested ahead of the scored one (2 measured
                                                   // faster than 3 or 4: the loads still land in time)
 constexpr int kSeg = 1024;                        // positions resolved at once
-constexpr int kHeadsWg = 64;
+constexpr int kMaxDev = 64;                       // devices whose CU count is cached
 constexpr int kPStride = 40;                      // bf16 per weight row (32 tokens + 8 pad)
 constexpr float kHeadroom = 16.f;
 static_assert(kTileBytes % 1024 == 0 && kRowLoads + 1 == 4 * kLoads, "tile loads split evenly");
-static_assert(kNB >= kPF + 2, "a tile buffer is refilled only after both roles are done with it");
 static_assert(kLoads * (kPF - 1) <= 63, "vmcnt range");
 
 typedef int v8i_t __attribute__((ext_vector_type(8)));
@@ -138,19 +141,33 @@ __device__ __forceinline__ bf16x8 widen8(uint32_t w0, uint32_t w1) {
   return r;
 }
 
+template <int HW>
 __global__ __launch_bounds__(kThreads) void mla_decode_f8ws_kernel(
     const __bf16* __restrict__ q, const uint8_t* __restrict__ kv, const float* __restrict__ kv_scale,
     int32_t num_pages, int32_t page_shift, const int32_t* __restrict__ bt, int32_t bt_stride,
     const int32_t* __restrict__ lens, int64_t max_len, const int32_t* __restrict__ indices, int32_t k,
     int32_t n_heads, float sm_scale_log2, int32_t num_splits, int32_t n_hg, float* __restrict__ o_part,
     float* __restrict__ lse_part, int32_t* __restrict__ status) {
+  // HW heads per workgroup: 64, or 32 when a call has too few (request,
+  // split) pairs to fill the GPU with 64-head groups.
+  constexpr int kHeadsWg = HW;
+  constexpr int NT = HW / 32;              // 16-head N-tiles of a score wave (it holds HW / 2 heads)
+  constexpr int kDimParts = 128 / HW;      // value waves per 32-head tile: 2, or 4
+  constexpr int kVDims = kDC / kDimParts;  // output dims of a value wave: 256, or 128
+  constexpr int NTV = kVDims / 32;         // its 32-dim N-tiles
+  constexpr int kHG16 = HW / 16;           // 16-head groups of the staged query
+  constexpr int kQBufs = HW == 64 ? 4 : 2; // buffers holding the staged query; tile t of a segment
+                                           // lives in buffer (t + kQBufs) % kNB
+  constexpr int kNB = kQBufs + 2;          // tile buffers
+  static_assert(HW == 64 || HW == 32, "head groups of 64 or 32");
+  static_assert(kNB >= kPF + 2, "a tile buffer is refilled only after both roles are done with it");
   __shared__ __attribute__((aligned(16))) uint8_t Kbuf[kNB][kTileBytes];
   __shared__ __attribute__((aligned(16))) float Tsc[kNB][64];          // FP8 scales of a tile's rows (32 used)
   __shared__ __attribute__((aligned(16))) int32_t seg_row[kSeg];        // cache row, or -1 when masked
   __shared__ __attribute__((aligned(16))) float seg_bias[kSeg];         // 0, or -inf when masked
   __shared__ __attribute__((aligned(16))) __bf16 Pbuf[2][kHeadsWg * kPStride];
   __shared__ __attribute__((aligned(16))) float red[2][kHeadsWg];       // per token half: head maxima / sums
-  __shared__ __attribute__((aligned(16))) bf16x8 Qrope[4][2][64];       // [head tile of 16][ks][lane]: rope dims
+  __shared__ __attribute__((aligned(16))) bf16x8 Qrope[kHG16][2][64];   // [head tile of 16][ks][lane]: rope dims
   __shared__ __attribute__((aligned(16))) uint8_t Qsc[kHeadsWg][2][4];  // E8M0 scale per head, term and block
   __shared__ int redo_flag;
   __shared__ int bad_flag;
@@ -160,9 +177,10 @@ __global__ __launch_bounds__(kThreads) void mla_decode_f8ws_kernel(
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const bool score_wave = wv < 4;
   const int role = wv & 3;
-  const int hq = role >> 1;            // head tile: heads 32hq..32hq+31 of the group
+  const int hq = role >> 1;            // score waves: heads hq * HW / 2.. of the group
   const int th = role & 1;             // score waves: token half of each tile
-  const int dh = role & 1;             // value waves: dim half
+  const int vht = role / kDimParts;    // value waves: heads 32vht..32vht+31 of the group
+  const int dpart = role % kDimParts;  // value waves: output dims kVDims * dpart..
   const int g = lane >> 4;
   const int r16 = lane & 15;
   const int page_size = 1 << page_shift;
@@ -219,22 +237,24 @@ __global__ __launch_bounds__(kThreads) void mla_decode_f8ws_kernel(
     for (int i = 0; i < kNP; ++i) iv[i] = ib[early ? min(pos_at(p0, i), (int64_t)k - 1) : 0];
   }
 
-  // ---- the query of the group's 64 heads is staged in LDS next (it
-  // depends on nothing): tile buffers 0..3, free until those buffers are
+  // ---- the query of the group's heads is staged in LDS next (it depends
+  // on nothing): tile buffers 0..kQBufs-1, free until those buffers are
   // first requested.  Layout: the latent dims as [half][head][32 chunks of
   // 16 bytes] (half hv = dims 256hv..256hv+255), then the rope dims as
   // [head][8 chunks]; chunk c of head h sits at slot c ^ (h % 16) (rope:
   // c ^ (h % 8)), so that the 16 heads a lane group reads at once fall on
-  // distinct LDS banks.  Wave w stages half w / 4 of heads 16(w % 4)..
-  // 16(w % 4)+15 (8 wave loads; waves 0..3 also their rope dims, 2 more), so
-  // the wave that converts them (below) needs no other wave's loads.  Heads
-  // past the last one stage head 0's query: their results are never stored.
+  // distinct LDS banks.  A query wave stages half hv of 16 heads 16hw.. (8
+  // wave loads; those with hv = 0 also their rope dims, 2 more), so the wave
+  // that converts them (below) needs no other wave's loads.  Heads past the
+  // last one stage head 0's query: their results are never stored.
   constexpr int kQLat = 0, kQRope = 2 * kHeadsWg * 512;
-  constexpr int kQBufs = 4;  // tile t of a segment lives in buffer (t + kQBufs) % kNB
   static_assert(kQRope + kHeadsWg * 128 <= kQBufs * kTileBytes && kNB - kQBufs >= 2,
                 "the staged query fits below the buffers of tiles 0 and 1");
-  {
-    const int hv = wv >> 2, hw = wv & 3;
+  // Query waves: all 8 for 64 heads (wave w: half w / 4 of heads
+  // 16(w % 4)..), waves 0-3 for 32 heads (half w / 2 of heads 16(w % 2)..).
+  const bool q_wave = wv < 2 * kHG16;
+  const int hv = wv / kHG16, hw = wv % kHG16;
+  if (q_wave) {
     const uint32_t qs_lds = lds_addr(&Kbuf[0][0]);
     const __bf16* qb = q + (int64_t)b * n_heads * kD;
     auto qrow = [&](int hl) { const int h = head_base + hl; return qb + (int64_t)(h < n_heads ? h : 0) * kD; };
@@ -357,7 +377,6 @@ __global__ __launch_bounds__(kThreads) void mla_decode_f8ws_kernel(
   // codes into registers.
   if (!any_token) vm_wait<0>();  // nothing to score: just let the early loads land
   if (any_token) {
-    const int hv = wv >> 2, hw = wv & 3;
     uint8_t* const qs = &Kbuf[0][0];
     const int64_t seg_end = min(p_end, p_begin + kSeg);
     vm_wait<0>();  // the indices are in, this wave's part of the query is staged
@@ -415,7 +434,7 @@ __global__ __launch_bounds__(kThreads) void mla_decode_f8ws_kernel(
       }
     };
     if (score_wave) {
-      convert();
+      convert();  // score waves are query waves for either head count
       pages_in();
     } else {
       pages_in();
@@ -430,7 +449,7 @@ __global__ __launch_bounds__(kThreads) void mla_decode_f8ws_kernel(
       }
       dma_rows(prow[0], kQBufs);
       dma_rows(prow[1], kQBufs + 1);
-      convert();
+      if (q_wave) convert();
     }
 #pragma unroll
     for (int u = 0; u < kNT; ++u) {
@@ -455,12 +474,16 @@ __global__ __launch_bounds__(kThreads) void mla_decode_f8ws_kernel(
   int64_t built = any_token ? p_begin : -1;  // segment whose table is in LDS
   // Both roles run the same sequence of barriers.
   if (score_wave) {
-    v8i_t qhi[2][4], qlo[2][4];
-    uint32_t qs_hi[2] = {0, 0}, qs_lo[2] = {0, 0};
+    v8i_t qhi[NT][4], qlo[NT][4];
+    uint32_t qs_hi[NT], qs_lo[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) qs_hi[nt] = qs_lo[nt] = 0;
+    // Head of N-tile nt of this score wave (its lane r16), within the group.
+    auto shead = [&](int nt) { return hq * (kHeadsWg / 2) + nt * 16 + r16; };
     if (any_token) {
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        const int hl = hq * 32 + nt * 16 + r16;
+      for (int nt = 0; nt < NT; ++nt) {
+        const int hl = shead(nt);
 #pragma unroll
         for (int blk = 0; blk < 4; ++blk) {
           const uint8_t* row = &Kbuf[0][0] + kQLat + ((blk >> 1) * kHeadsWg + hl) * 512;
@@ -476,16 +499,16 @@ __global__ __launch_bounds__(kThreads) void mla_decode_f8ws_kernel(
         qs_hi[nt] = *reinterpret_cast<const uint32_t*>(&Qsc[hl][0][0]);
         qs_lo[nt] = *reinterpret_cast<const uint32_t*>(&Qsc[hl][1][0]);
       }
-      wg_barrier();  // buffers 0..3 are free for tiles
+      wg_barrier();  // the query's buffers are free for tiles
     }
 
     // Scores of the tile in Kt for this wave's 16 tokens (rows 16th + r16 on
     // M) and its 32 heads (two N-tiles): S[nt] holds head 16nt + r16 for
     // tokens 16th + 4g + j.
-    auto score_tile = [&](const uint8_t* __restrict__ Kt, f32x4 (&S)[2]) __attribute__((always_inline)) {
-      f32x4 acc[2][2];
+    auto score_tile = [&](const uint8_t* __restrict__ Kt, f32x4 (&S)[NT]) __attribute__((always_inline)) {
+      f32x4 acc[NT][2];
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) acc[nt][0] = acc[nt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int nt = 0; nt < NT; ++nt) acc[nt][0] = acc[nt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
       const int row = th * 16 + r16;
       const int sw = swz(row);
       const uint8_t* rp = Kt + row * kRS;
@@ -495,7 +518,7 @@ __global__ __launch_bounds__(kThreads) void mla_decode_f8ws_kernel(
         const uint4 k1 = *reinterpret_cast<const uint4*>(rp + 16 * ((8 * blk + 4 + g) ^ sw));
         const v8i_t a = {(int)k0.x, (int)k0.y, (int)k0.z, (int)k0.w, (int)k1.x, (int)k1.y, (int)k1.z, (int)k1.w};
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
+        for (int nt = 0; nt < NT; ++nt) {
           acc[nt][0] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, qhi[nt][blk], acc[nt][0], 0, 0, 0, 127,
                                                                         blk, (int)qs_hi[nt]);
           acc[nt][1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, qlo[nt][blk], acc[nt][1], 0, 0, 0, 127,
@@ -507,25 +530,25 @@ __global__ __launch_bounds__(kThreads) void mla_decode_f8ws_kernel(
         const uint2 kr = *reinterpret_cast<const uint2*>(rp + 16 * ((32 + 2 * ks + (g >> 1)) ^ sw) + 8 * (g & 1));
         const bf16x8 kb = widen8(kr.x, kr.y);
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) acc[nt][1] = OpBF16::mma(kb, Qrope[2 * hq + nt][ks][lane], acc[nt][1]);
+        for (int nt = 0; nt < NT; ++nt) acc[nt][1] = OpBF16::mma(kb, Qrope[NT * hq + nt][ks][lane], acc[nt][1]);
       }
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) S[nt] = acc[nt][0] + acc[nt][1];
+      for (int nt = 0; nt < NT; ++nt) S[nt] = acc[nt][0] + acc[nt][1];
     };
 
-    float m_ref[2] = {-INFINITY, -INFINITY};   // reference of head 16nt + r16 (log2 domain)
-    float m_lane[2] = {-INFINITY, -INFINITY};  // this lane's largest logit
-    float l_lane[2] = {0.f, 0.f};              // this lane's sum of weights
+    float m_ref[NT], m_lane[NT], l_lane[NT];   // per N-tile: reference (log2 domain), this lane's
+#pragma unroll                                 // largest logit, this lane's sum of weights
+    for (int nt = 0; nt < NT; ++nt) m_ref[nt] = m_lane[nt] = -INFINITY;
     bool fallback = false;                     // the first tile had no valid token: 0 stood in for m_ref
     // Softmax weights of a scored tile, written to P as bf16 (times each
     // token's FP8 scale, which the value contraction needs).
-    auto softmax_tile = [&](const f32x4 (&S)[2], int buf, int tb, __bf16* __restrict__ P, bool& over)
+    auto softmax_tile = [&](const f32x4 (&S)[NT], int buf, int tb, __bf16* __restrict__ P, bool& over)
         __attribute__((always_inline)) {
       const int t0 = th * 16 + 4 * g;
       const f32x4 ts = *reinterpret_cast<const f32x4*>(&Tsc[buf][t0]);
       const f32x4 bi = *reinterpret_cast<const f32x4*>(&seg_bias[tb + t0]);
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
+      for (int nt = 0; nt < NT; ++nt) {
         float z[4], mx = -INFINITY;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -543,12 +566,13 @@ __global__ __launch_bounds__(kThreads) void mla_decode_f8ws_kernel(
         }
         typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
         const bf16x4_t w4 = {(__bf16)pv[0], (__bf16)pv[1], (__bf16)pv[2], (__bf16)pv[3]};
-        *reinterpret_cast<bf16x4_t*>(P + (hq * 32 + nt * 16 + r16) * kPStride + t0) = w4;
+        *reinterpret_cast<bf16x4_t*>(P + shead(nt) * kPStride + t0) = w4;
       }
     };
 
     for (int pass = 0; pass < 2; ++pass) {
-      l_lane[0] = l_lane[1] = 0.f;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) l_lane[nt] = 0.f;
       bool over = false;
       if (tid == 0) redo_flag = 0;
       for (int64_t seg = p_begin; seg < p_end; seg += kSeg) {
@@ -562,24 +586,24 @@ __global__ __launch_bounds__(kThreads) void mla_decode_f8ws_kernel(
           wg_barrier();
         }
         wg_barrier();  // tile 0 has landed
-        f32x4 S[2];
+        f32x4 S[NT];
         score_tile(Kbuf[kQBufs], S);
         if (need_ref) {
           const int t0 = th * 16 + 4 * g;
           const f32x4 ts = *reinterpret_cast<const f32x4*>(&Tsc[kQBufs][t0]);
           const f32x4 bi = *reinterpret_cast<const f32x4*>(&seg_bias[t0]);
 #pragma unroll
-          for (int nt = 0; nt < 2; ++nt) {
+          for (int nt = 0; nt < NT; ++nt) {
             float mx = -INFINITY;
 #pragma unroll
             for (int j = 0; j < 4; ++j) mx = fmaxf(mx, __builtin_fmaf(S[nt][j], sm_scale_log2 * ts[j], bi[j]));
             mx = wave_max_xor16_32(mx);
-            if (g == 0) red[th][hq * 32 + nt * 16 + r16] = mx;
+            if (g == 0) red[th][shead(nt)] = mx;
           }
           wg_barrier();
 #pragma unroll
-          for (int nt = 0; nt < 2; ++nt) {
-            const int hl = hq * 32 + nt * 16 + r16;
+          for (int nt = 0; nt < NT; ++nt) {
+            const int hl = shead(nt);
             m_ref[nt] = fmaxf(red[0][hl], red[1][hl]);
             // No valid token in the first tile (the same for every head): 0
             // stands in, and the split is recomputed with the true maximum
@@ -604,19 +628,21 @@ __global__ __launch_bounds__(kThreads) void mla_decode_f8ws_kernel(
       }
       // Recompute the split once if a logit outgrew its head's reference,
       // or if the reference was a stand-in and valid tokens were seen.
-      const bool seen = m_lane[0] > -INFINITY || m_lane[1] > -INFINITY;
+      bool seen = false;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) seen |= m_lane[nt] > -INFINITY;
       if (__any(over || (fallback && seen)) && lane == 0) atomicOr(&redo_flag, 1);
       wg_barrier();
       if (pass == 1 || redo_flag == 0) break;
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
+      for (int nt = 0; nt < NT; ++nt) {
         const float mt = wave_max_xor16_32(m_lane[nt]);
-        if (g == 0) red[th][hq * 32 + nt * 16 + r16] = mt;
+        if (g == 0) red[th][shead(nt)] = mt;
       }
       wg_barrier();
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        const int hl = hq * 32 + nt * 16 + r16;
+      for (int nt = 0; nt < NT; ++nt) {
+        const int hl = shead(nt);
         m_ref[nt] = fmaxf(red[0][hl], red[1][hl]);
         if (m_ref[nt] == -INFINITY) m_ref[nt] = 0.f;
       }
@@ -625,16 +651,16 @@ __global__ __launch_bounds__(kThreads) void mla_decode_f8ws_kernel(
     // ---- finish: l per head from both token halves, then lse.
     wg_barrier();  // red is free again
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
+    for (int nt = 0; nt < NT; ++nt) {
       const float ls = wave_sum_xor16_32(l_lane[nt]);
-      if (g == 0) red[th][hq * 32 + nt * 16 + r16] = ls;
+      if (g == 0) red[th][shead(nt)] = ls;
     }
     wg_barrier();
     const bool bad = bad_flag != 0;
     if (th == 0 && g == 0) {
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        const int hl = hq * 32 + nt * 16 + r16;
+      for (int nt = 0; nt < NT; ++nt) {
+        const int hl = shead(nt);
         const int h = head_base + hl;
         if (h < n_heads) {
           const float l = red[0][hl] + red[1][hl];
@@ -662,23 +688,23 @@ __global__ __launch_bounds__(kThreads) void mla_decode_f8ws_kernel(
     // 16(G & 1) + i of the N-tile for tokens 16ks + 8(G >> 1) + e, e < 8,
     // when lane j of the group points at 8 dims (8(j & 1)..) of token row
     // 16ks + 8(G >> 1) + j / 2.
-    auto pv_tile = [&](const uint8_t* __restrict__ Vt, const __bf16* __restrict__ P, f32x16 (&acc_o)[8])
+    auto pv_tile = [&](const uint8_t* __restrict__ Vt, const __bf16* __restrict__ P, f32x16 (&acc_o)[NTV])
         __attribute__((always_inline)) {
       const int G = lane >> 4, j = lane & 15;
       // All LDS reads of the tile are issued before the first MFMA (20
       // registers of codes), so the MFMAs wait for them once instead of one
       // read latency each.
       bf16x8 pa[2];
-      v2i_t raw[2][8];
+      v2i_t raw[2][NTV];
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        pa[ks] = *reinterpret_cast<const bf16x8*>(P + (hq * 32 + (lane & 31)) * kPStride + 16 * ks + 8 * (lane >> 5));
+        pa[ks] = *reinterpret_cast<const bf16x8*>(P + (vht * 32 + (lane & 31)) * kPStride + 16 * ks + 8 * (lane >> 5));
         const int tr = 16 * ks + 8 * (G >> 1) + (j >> 1);
         const int sw = swz(tr);
         const uint8_t* vrow = Vt + tr * kRS + 8 * (j & 1);
 #pragma unroll
-        for (int nt = 0; nt < 8; ++nt) {
-          const int chunk = 16 * dh + 2 * nt + (G & 1);
+        for (int nt = 0; nt < NTV; ++nt) {
+          const int chunk = (kVDims / 16) * dpart + 2 * nt + (G & 1);
           raw[ks][nt] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(vrow + 16 * (chunk ^ sw)));
         }
       }
@@ -688,7 +714,7 @@ __global__ __launch_bounds__(kThreads) void mla_decode_f8ws_kernel(
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
-        for (int h4 = 0; h4 < 2; ++h4) {
+        for (int h4 = 0; h4 < NTV / 4; ++h4) {
           __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
           for (int nt = 4 * h4; nt < 4 * h4 + 4; ++nt)
@@ -700,12 +726,12 @@ __global__ __launch_bounds__(kThreads) void mla_decode_f8ws_kernel(
     };
 
     // (Tiles 0 and 1 went to buffers 4 and 5 with the query.)
-    if (any_token) wg_barrier();  // the score waves hold the query: buffers 0..3 are free for tiles
+    if (any_token) wg_barrier();  // the score waves hold the query: its buffers are free for tiles
 
-    f32x16 acc_o[8];
+    f32x16 acc_o[NTV];
     for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
-      for (int nt = 0; nt < 8; ++nt) acc_o[nt] = f32x16{};
+      for (int nt = 0; nt < NTV; ++nt) acc_o[nt] = f32x16{};
       for (int64_t seg = p_begin; seg < p_end; seg += kSeg) {
         const int64_t seg_end = min(p_end, seg + kSeg);
         const int T = (int)((seg_end - seg + kTileTok - 1) / kTileTok);
@@ -751,13 +777,13 @@ __global__ __launch_bounds__(kThreads) void mla_decode_f8ws_kernel(
     const bool bad = bad_flag != 0;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      const int hl = hq * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+      const int hl = vht * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
       const int h = head_base + hl;
       const float l = red[0][hl] + red[1][hl];
       const float inv = bad ? kNaN : (l > 0.f ? 1.f / l : 0.f);
       if (h < n_heads) {
 #pragma unroll
-        for (int nt = 0; nt < 8; ++nt) *out_o(h, dh * 256 + nt * 32 + (lane & 31)) = acc_o[nt][e] * inv;
+        for (int nt = 0; nt < NTV; ++nt) *out_o(h, dpart * kVDims + nt * 32 + (lane & 31)) = acc_o[nt][e] * inv;
       }
     }
   }
@@ -768,15 +794,34 @@ __global__ __launch_bounds__(kThreads) void mla_decode_f8ws_kernel(
 int launch_decode_f8(const DecodeArgs& a, hipStream_t stream) {
   int page_shift = 0;
   while ((1 << page_shift) < a.page_size) ++page_shift;
-  const int n_hg = (a.n_heads + kHeadsWg - 1) / kHeadsWg;
-  const int64_t grid = (int64_t)a.batch * a.num_splits * n_hg;
+  // 32-head groups when 64-head ones would leave more than half of the CUs
+  // without a workgroup: twice the workgroups, each with half the matrix
+  // work per tile over the same tiles.
+  const int64_t pairs = (int64_t)a.batch * a.num_splits;
+  if (pairs == 0) return 0;
+  static std::atomic<int> n_cu[kMaxDev];  // CU count per device, 0 until first asked
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return -3;
+  int cus = n_cu[dev].load(std::memory_order_relaxed);
+  if (cus == 0) {
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) return -3;
+    n_cu[dev].store(cus, std::memory_order_relaxed);
+  }
+  const bool narrow = 2 * pairs * ((a.n_heads + 63) / 64) <= cus;
+  const int hw = narrow ? 32 : 64;
+  const int n_hg = (a.n_heads + hw - 1) / hw;
+  const int64_t grid = pairs * n_hg;
   if (grid == 0) return 0;
   if (grid > 0x7FFFFFFF) return -2;
   const float sm_log2 = a.sm_scale * 1.44269504088896340736f;
-  hipLaunchKernelGGL(mla_decode_f8ws_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream,
-                     reinterpret_cast<const __bf16*>(a.q), reinterpret_cast<const uint8_t*>(a.kv), a.kv_scale,
-                     a.num_pages, page_shift, a.bt, a.bt_stride, a.lens, a.max_len, a.indices, a.k, a.n_heads,
-                     sm_log2, a.num_splits, n_hg, a.o_part, a.lse_part, a.status);
+  auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, reinterpret_cast<const __bf16*>(a.q),
+                       reinterpret_cast<const uint8_t*>(a.kv), a.kv_scale, a.num_pages, page_shift, a.bt, a.bt_stride,
+                       a.lens, a.max_len, a.indices, a.k, a.n_heads, sm_log2, a.num_splits, n_hg, a.o_part, a.lse_part,
+                       a.status);
+  };
+  if (narrow) go(mla_decode_f8ws_kernel<32>);
+  else go(mla_decode_f8ws_kernel<64>);
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 

@@ -290,6 +290,18 @@ def test_partial_head_groups(name, n_heads):
     _check_full(gen.make_inputs(cfg, lens=[70, 2500, 5000]), 3, f"{name} {n_heads} heads")
 
 
+@pytest.mark.parametrize("n_heads", [72, 128])
+def test_fp8_many_pairs_64_head_groups(n_heads):
+    """The FP8 kernel's 64-head workgroups at a size the oracle checks whole:
+    66 requests x 2 splits are enough (request, split) pairs to fill a
+    256-CU GPU with 64-head groups, so the 32-head form is not taken (the
+    smaller cases above take it)."""
+    _lib()
+    cfg = gen.CONFIGS["c3f"].with_(batch=66, n_heads=n_heads, topk=256)
+    lens = 40 + (np.arange(66) * 97) % 560
+    _check_full(gen.make_inputs(cfg, lens=lens), 2, f"fp8 64-head groups, {n_heads} heads")
+
+
 @pytest.mark.parametrize("cache", [pytest.param(gen.FP8, id="fp8"), pytest.param(gen.BF16, id="bf16")])
 @pytest.mark.parametrize("splits", [1, 2, 5])
 def test_dense_multi_segment(cache, splits):
