@@ -209,9 +209,12 @@ int topk_select_noalloc(const float* scores, int64_t score_stride,
  *               kv_scale [num_pages, page_size] fp32 iff FP8.
  *  o_part       [batch, num_splits, n_heads, d_latent] fp32.
  *  lse_part     [batch, num_splits, n_heads] fp32, natural log.
- * Supported: q BF16 with d_latent + d_rope = 576 and d_latent = 512, or q F32
- * with d_latent + d_rope = 80 and d_latent = 64; n_heads <= 256;
- * 1 <= num_splits <= 64; page_size in {16, 32, 64, 128}; 0 <= k <= 65536.
+ * Supported: d_latent >= 8 and d_rope >= 0 multiples of 8 with
+ * d_latent + d_rope <= 1024; q F32 over any cache, q BF16 over a bf16 or FP8
+ * cache; n_heads <= 256; 1 <= num_splits <= 64; page_size in
+ * {16, 32, 64, 128}; 0 <= k <= 65536.  Tuned kernels serve q BF16 with
+ * 512 + 64 (bf16 or FP8 cache) and q F32 with 64 + 16; other shapes run a
+ * plain fp32 kernel with the same results (to rounding) and status bits.
  */
 int mla_paged_decode(const void* q, int32_t q_dtype,
                      const void* kv_pool, const float* kv_scale, int32_t kv_dtype,

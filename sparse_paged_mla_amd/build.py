@@ -13,7 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libsparse_mla.so")
-SOURCES = ["api.cpp", "indexer.hip", "topk.hip", "mla_decode.hip", "mla_decode_f8.hip", "mla_decode_bf16.hip", "lse_merge.hip", "cache_append.hip", "page_check.hip", "mq_expand.hip"]
+SOURCES = ["api.cpp", "indexer.hip", "topk.hip", "mla_decode.hip", "mla_decode_f8.hip", "mla_decode_bf16.hip", "mla_decode_generic.hip", "lse_merge.hip", "cache_append.hip", "page_check.hip", "mq_expand.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -167,10 +167,10 @@ int mla_paged_decode(const void* q, int32_t q_dtype, const void* kv_pool, const 
   if (kv_dtype < SPMLA_F32 || kv_dtype > SPMLA_FP8_E4M3) return fail(SPMLA_EINVAL, "%s: bad kv_dtype", w);
   if (n_heads < 1 || n_heads > 256) return fail(SPMLA_EUNSUPPORTED, "%s: n_heads must be in [1, 256]", w);
   if (d_latent < 1 || d_rope < 0) return fail(SPMLA_EINVAL, "%s: bad d_latent / d_rope", w);
-  const bool shape_bf16 = q_dtype == SPMLA_BF16 && d_latent == 512 && d_rope == 64 && kv_dtype != SPMLA_F32;
-  const bool shape_f32 = q_dtype == SPMLA_F32 && d_latent == 64 && d_rope == 16;
-  if (!shape_bf16 && !shape_f32)
-    return fail(SPMLA_EUNSUPPORTED, "%s: supported shapes are bf16 q with 512+64 (bf16/FP8 cache) or fp32 q with 64+16", w);
+  if (!spmla::decode_generic_shape(q_dtype, kv_dtype, d_latent, d_rope))
+    return fail(SPMLA_EUNSUPPORTED,
+                "%s: d_latent (>= 8) and d_rope must be multiples of 8 with d_latent + d_rope <= %d; bf16 queries "
+                "need a bf16 or FP8 cache", w, spmla::kDecodeGenericMaxDim);
   if (num_splits < 1 || num_splits > 64) return fail(SPMLA_EUNSUPPORTED, "%s: num_splits must be in [1, 64]", w);
   if (indices && (k < 0 || k > 65536)) return fail(SPMLA_EUNSUPPORTED, "%s: k must be in [0, 65536]", w);
   if (!(sm_scale > 0.f) || sm_scale > 1e30f) return fail(SPMLA_EINVAL, "%s: sm_scale must be positive and finite", w);

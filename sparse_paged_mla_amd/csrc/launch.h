@@ -40,6 +40,19 @@ int launch_decode(const DecodeArgs& a, hipStream_t stream);
 int launch_decode_f8(const DecodeArgs& a, hipStream_t stream);
 // bf16 cache, bf16 query, 512 + 64 dims (mla_decode_bf16.hip).
 int launch_decode_bf16(const DecodeArgs& a, hipStream_t stream);
+// Other shapes (mla_decode_generic.hip): latent and rope widths multiples of
+// 8, latent >= 8, latent + rope <= kDecodeGenericMaxDim; fp32 or bf16
+// queries; fp32, bf16 or FP8 caches, except bf16 queries over fp32 caches.
+constexpr int kDecodeGenericMaxDim = 1024;
+inline bool decode_generic_shape(int q_dtype, int kv_dtype, int d_latent, int d_rope) {
+  constexpr int f32 = 0, bf16 = 1, fp8 = 2;  // the C ABI's dtype codes
+  if (d_latent < 8 || d_latent % 8 != 0 || d_rope < 0 || d_rope % 8 != 0) return false;
+  if (d_latent + d_rope > kDecodeGenericMaxDim) return false;
+  if (q_dtype != f32 && q_dtype != bf16) return false;
+  if (kv_dtype != f32 && kv_dtype != bf16 && kv_dtype != fp8) return false;
+  return !(q_dtype == bf16 && kv_dtype == f32);
+}
+int launch_decode_generic(const DecodeArgs& a, hipStream_t stream);
 
 struct MergeArgs {
   const float* o_part; const float* lse_part; int32_t batch, num_splits, n_heads, d; float* o; float* lse;

@@ -476,7 +476,7 @@ int launch_decode(const DecodeArgs& a, hipStream_t s) {
     if (a.kv_dtype == kFP8) return launch_one<OpF32, kFP8, 20, 4>(a, s);
     return -2;
   }
-  return -2;
+  return launch_decode_generic(a, s);  // any other shape the interface takes
 }
 
 }  // namespace spmla

@@ -146,7 +146,10 @@ def test_decode_rejects(lib):
                                      ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                      ctypes.c_int32, ctypes.c_float, ctypes.c_int32, ctypes.c_void_p,
                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
-    assert _dec(lib, d_latent=256) == EUNSUPPORTED
+    assert _dec(lib, d_latent=260) == EUNSUPPORTED          # widths must be multiples of 8
+    assert _dec(lib, d_rope=12) == EUNSUPPORTED
+    assert _dec(lib, d_latent=0) == EINVAL
+    assert _dec(lib, d_latent=1024, d_rope=8) == EUNSUPPORTED  # latent + rope <= 1024
     assert _dec(lib, q_dtype=FP8) == EUNSUPPORTED
     assert _dec(lib, kv_dtype=F32) == EUNSUPPORTED          # bf16 queries need a bf16/FP8 cache
     assert _dec(lib, splits=0) == EUNSUPPORTED

@@ -290,6 +290,34 @@ def test_partial_head_groups(name, n_heads):
     _check_full(gen.make_inputs(cfg, lens=[70, 2500, 5000]), 3, f"{name} {n_heads} heads")
 
 
+GENERIC_SHAPES = [
+    pytest.param(dict(d_latent=40, d_rope=24, q_dtype=gen.BF16, cache_dtype=gen.FP8), id="40+24-bf16q-fp8"),
+    pytest.param(dict(d_latent=96, d_rope=0, q_dtype=gen.F32, cache_dtype=gen.BF16), id="96+0-f32q-bf16"),
+    pytest.param(dict(d_latent=256, d_rope=32, q_dtype=gen.BF16, cache_dtype=gen.BF16), id="256+32-bf16"),
+    pytest.param(dict(d_latent=512, d_rope=64, q_dtype=gen.F32, cache_dtype=gen.FP8), id="512+64-f32q-fp8"),
+    pytest.param(dict(d_latent=8, d_rope=8, q_dtype=gen.F32, cache_dtype=gen.F32), id="8+8-f32"),
+    pytest.param(dict(d_latent=1000, d_rope=24, q_dtype=gen.BF16, cache_dtype=gen.BF16), id="1000+24-bf16"),
+]
+
+
+@pytest.mark.parametrize("shape", GENERIC_SHAPES)
+@pytest.mark.parametrize("splits", [1, 3])
+def test_generic_shapes_dense(shape, splits):
+    """Latent and rope widths outside the two tuned shapes (any multiples of
+    8): dense attention over pages of 16, 24 heads (a partial group of 16)."""
+    _lib()
+    cfg = gen.CONFIGS["c2"].with_(batch=3, n_heads=24, page_size=16, **shape)
+    _check_full(gen.make_inputs(cfg, lens=[5, 300, 777]), splits, f"generic dense {shape}")
+
+
+@pytest.mark.parametrize("shape", GENERIC_SHAPES[:3])
+def test_generic_shapes_sparse(shape):
+    """The same shapes behind an indexer and top-k (k below and above L)."""
+    _lib()
+    cfg = gen.CONFIGS["c3"].with_(batch=2, n_heads=24, topk=64, idx_heads=8, idx_dim=32, **shape)
+    _check_full(gen.make_inputs(cfg, lens=[40, 900]), 2, f"generic sparse {shape}")
+
+
 @pytest.mark.parametrize("n_heads", [72, 128])
 def test_fp8_many_pairs_64_head_groups(n_heads):
     """The FP8 kernel's 64-head workgroups at a size the oracle checks whole:
