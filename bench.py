@@ -434,7 +434,7 @@ def main():
     import torch
     import spmla_gen as gen
     from spmla_gen.torch_io import device_batch
-    from sparse_paged_mla_amd.step import DEFAULT_SPLITS, DecodeStep
+    from sparse_paged_mla_amd.step import DecodeStep, default_splits
     import sparse_paged_mla_amd as spm
 
     spm.load_library()
@@ -445,8 +445,8 @@ def main():
     torch.cuda.synchronize()
     print(f"[bench] {cfg.name}: inputs ready in {time.perf_counter() - t_gen:.1f} s "
           f"(sum L = {int(inp.lens.sum())}, pool {inp.num_pages} pages)", file=sys.stderr, flush=True)
-    splits = args.splits or DEFAULT_SPLITS.get(cfg.name, 1)
-    step = DecodeStep(db, num_splits=splits)
+    splits, split_tokens = default_splits(cfg.name, inp.lens, cfg.n_heads, args.splits)
+    step = DecodeStep(db, num_splits=splits, split_tokens=split_tokens)
     stages = ["indexer", "select", "attend", "merge"] if step.sparse else ["attend", "merge"]
     if splits == 1:
         stages.remove("merge")
@@ -592,6 +592,7 @@ def main():
                            f"indexer {cfg.idx_heads}x{cfg.idx_dim} {gen.DTYPE_NAMES[cfg.idx_dtype]}, top-k {cfg.topk}")
                         + f", cache {gen.DTYPE_NAMES[cfg.cache_dtype]}, page {cfg.page_size}",
             "global_batch": cfg.batch, "seq_len": int(inp.max_len), "num_splits": splits,
+            "split_tokens": split_tokens,
             "parallelism": "single GPU", "cache_flush_between_steps": flush},
         "roofline": roof,
         "cpu_baseline": cpu,

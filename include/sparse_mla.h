@@ -197,11 +197,19 @@ int topk_select_noalloc(const float* scores, int64_t score_stride,
  * over the split's tokens; every head reads the same shared latent row
  * [KW 5.1.2], and the value of a token is its first d_latent dims.  The token
  * set is indices[b, 0 .. k) (entries -1 are skipped) or, with indices == NULL,
- * every t < context_lens[b].  Split s takes list positions [s*c, (s+1)*c) with
- * c = ceil(n / num_splits) rounded up to a multiple of 32 (n = k, or
- * context_lens[b] when dense).  A split with no tokens gives o_part = 0 and
- * lse_part = -inf.  With num_splits == 1 the partials are the final result;
- * otherwise combine them with lse_merge.
+ * every t < context_lens[b].  Split s takes list positions [s*c, (s+1)*c)
+ * (n = k, or context_lens[b] when dense), with
+ *   split_tokens == 0: c = ceil(n / num_splits) rounded up to a multiple of
+ *     32, the same number of splits for every request; a split with no
+ *     tokens gives o_part = 0 and lse_part = -inf;
+ *   split_tokens > 0 (a multiple of 32): c = split_tokens for every request,
+ *     the last split (s = num_splits - 1) taking all positions from s*c to n:
+ *     a long request spreads over more splits than a short one, so that a
+ *     ragged batch gives every split about the same work.  Splits that start
+ *     at or past n write lse_part = -inf and leave o_part unwritten
+ *     (lse_merge gives them weight 0 and never reads their o_part).
+ * With num_splits == 1 the partials are the final result; otherwise combine
+ * them with lse_merge.
  *
  *  q            [batch, n_heads, d_latent + d_rope], q_dtype F32 or BF16 (the
  *               arithmetic follows it, as for dsa_indexer_scores).
@@ -209,6 +217,7 @@ int topk_select_noalloc(const float* scores, int64_t score_stride,
  *               kv_scale [num_pages, page_size] fp32 iff FP8.
  *  o_part       [batch, num_splits, n_heads, d_latent] fp32.
  *  lse_part     [batch, num_splits, n_heads] fp32, natural log.
+ *  split_tokens 0, or a positive multiple of 32 (else SPMLA_EINVAL): see above.
  * Supported: d_latent >= 8 and d_rope >= 0 multiples of 8 with
  * d_latent + d_rope <= 1024; q F32 over any cache, q BF16 over a bf16 or FP8
  * cache; n_heads <= 256; 1 <= num_splits <= 64; page_size in
@@ -223,7 +232,8 @@ int mla_paged_decode(const void* q, int32_t q_dtype,
                      const int32_t* context_lens, int32_t batch, int64_t max_len,
                      const int32_t* indices, int32_t k,
                      int32_t n_heads, int32_t d_latent, int32_t d_rope, float sm_scale,
-                     int32_t num_splits, float* o_part, float* lse_part,
+                     int32_t num_splits, int32_t split_tokens,
+                     float* o_part, float* lse_part,
                      int32_t* req_status, void* stream);
 
 /*

@@ -59,7 +59,7 @@ def declare(lib):
     lib.topk_select_noalloc.argtypes = [vp, i64, vp, i32, i64, i32, vp, vp, vp]
     lib.mla_paged_decode.restype = ctypes.c_int
     lib.mla_paged_decode.argtypes = [vp, i32, vp, vp, i32, i32, i32, vp, i32, vp, i32, i64, vp, i32, i32, i32, i32,
-                                     f32, i32, vp, vp, vp, vp]
+                                     f32, i32, i32, vp, vp, vp, vp]
     lib.kv_cache_append.restype = ctypes.c_int
     lib.kv_cache_append.argtypes = [vp, i32, i32, i32, vp, vp, i32, i32, i32, vp, i32, vp, vp, vp]
     lib.kv_cache_append_pair.restype = ctypes.c_int
@@ -152,10 +152,11 @@ def topk_select_noalloc(scores, context_lens, max_len, k, out_idx, req_status=No
 
 
 def mla_paged_decode(q, kv_pool, kv_scale, block_table, context_lens, max_len, indices, d_latent, sm_scale,
-                     o_part, lse_part, req_status=None, stream=None):
+                     o_part, lse_part, req_status=None, stream=None, split_tokens=0):
     """Split-KV attention over indices[b] (or every token when indices is None).
 
-    o_part [B, S, H, d_latent] and lse_part [B, S, H] fix the number of splits S."""
+    o_part [B, S, H, d_latent] and lse_part [B, S, H] fix the number of splits S;
+    split_tokens > 0 fixes the split length instead of dividing each request by S."""
     lib = load_library()
     B, H, D = q.shape
     num_pages, page_size = kv_pool.shape[0], kv_pool.shape[1]
@@ -164,7 +165,8 @@ def mla_paged_decode(q, kv_pool, kv_scale, block_table, context_lens, max_len, i
     _check(lib.mla_paged_decode(_ptr(q), _dtype_code(q), _ptr(kv_pool), _ptr(kv_scale), _dtype_code(kv_pool),
                                 num_pages, page_size, _ptr(block_table), block_table.shape[1], _ptr(context_lens), B,
                                 int(max_len), _ptr(indices), k, H, int(d_latent), D - int(d_latent),
-                                float(sm_scale), S, _ptr(o_part), _ptr(lse_part), _ptr(req_status), _stream(stream)))
+                                float(sm_scale), S, int(split_tokens), _ptr(o_part), _ptr(lse_part), _ptr(req_status),
+                                _stream(stream)))
 
 
 def lse_merge(o_part, lse_part, o, lse, stream=None):

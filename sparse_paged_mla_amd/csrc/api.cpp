@@ -160,7 +160,7 @@ int mla_paged_decode(const void* q, int32_t q_dtype, const void* kv_pool, const 
                      int32_t num_pages, int32_t page_size, const int32_t* block_table, int32_t bt_stride,
                      const int32_t* context_lens, int32_t batch, int64_t max_len, const int32_t* indices, int32_t k,
                      int32_t n_heads, int32_t d_latent, int32_t d_rope, float sm_scale, int32_t num_splits,
-                     float* o_part, float* lse_part, int32_t* req_status, void* stream) {
+                     int32_t split_tokens, float* o_part, float* lse_part, int32_t* req_status, void* stream) {
   const char* w = "mla_paged_decode";
   if (int rc = check_paging(w, num_pages, page_size, block_table, bt_stride, context_lens, batch, max_len)) return rc;
   if (q_dtype != SPMLA_F32 && q_dtype != SPMLA_BF16) return fail(SPMLA_EUNSUPPORTED, "%s: q_dtype must be F32 or BF16", w);
@@ -172,6 +172,8 @@ int mla_paged_decode(const void* q, int32_t q_dtype, const void* kv_pool, const 
                 "%s: d_latent (>= 8) and d_rope must be multiples of 8 with d_latent + d_rope <= %d; bf16 queries "
                 "need a bf16 or FP8 cache", w, spmla::kDecodeGenericMaxDim);
   if (num_splits < 1 || num_splits > 64) return fail(SPMLA_EUNSUPPORTED, "%s: num_splits must be in [1, 64]", w);
+  if (split_tokens < 0 || split_tokens % 32 != 0)
+    return fail(SPMLA_EINVAL, "%s: split_tokens must be 0 or a positive multiple of 32", w);
   if (indices && (k < 0 || k > 65536)) return fail(SPMLA_EUNSUPPORTED, "%s: k must be in [0, 65536]", w);
   if (!(sm_scale > 0.f) || sm_scale > 1e30f) return fail(SPMLA_EINVAL, "%s: sm_scale must be positive and finite", w);
   if (batch > 0) {
@@ -182,7 +184,7 @@ int mla_paged_decode(const void* q, int32_t q_dtype, const void* kv_pool, const 
   }
   spmla::DecodeArgs a{q, q_dtype, kv_pool, kv_scale, kv_dtype, num_pages, page_size, block_table, bt_stride,
                       context_lens, batch, max_len, indices, indices ? k : 0, n_heads, d_latent, d_rope, sm_scale,
-                      num_splits, o_part, lse_part, req_status};
+                      num_splits, split_tokens, o_part, lse_part, req_status};
   return map_launch(spmla::launch_decode(a, reinterpret_cast<hipStream_t>(stream)), w);
 }
 

@@ -72,5 +72,35 @@ __device__ __forceinline__ int xcd_remap(int bid, int n) {
   return xcd < r ? xcd * (q + 1) + slot : r * (q + 1) + (xcd - r) * q + slot;
 }
 
+// Workgroup -> (request b, split s, head group hg) over a grid of
+// batch * num_splits * n_hg workgroups.  Equal split counts: b-major over
+// xcd_remap's logical order (a request's workgroups share an L2).  A fixed
+// split length (spread): the (request, split) pairs go in split-major order,
+// so that a ragged batch's empty tail splits are dispatched last, with the
+// requests of split s rotated by s (pair p is split s = p / batch of request
+// (p - s) mod batch), and are dealt to the XCDs round-robin, so that a
+// request's splits land on consecutive XCDs and every XCD gets about an equal
+// share of the pairs with work; the n_hg workgroups of a pair (they read the
+// same rows) share an XCD: in each full round of 8 * n_hg ids, id i takes
+// pair round * 8 + i % 8 and head group (i % (8 * n_hg)) / 8; the last,
+// partial round takes its pairs in order.
+struct WgCoord {
+  int b, s, hg;
+};
+__device__ __forceinline__ WgCoord wg_coord(int bid, int n, int num_splits, int n_hg, bool spread) {
+  if (!spread) {
+    const int logical = xcd_remap(bid, n);
+    return {logical / (n_hg * num_splits), (logical / n_hg) % num_splits, logical % n_hg};
+  }
+  const int batch = n / (num_splits * n_hg);
+  const int full = batch * num_splits / 8;  // full rounds
+  const int round_ids = 8 * n_hg;
+  const int r = bid / round_ids, w = bid % round_ids;
+  const int p = r < full ? r * 8 + (w & 7) : full * 8 + w / n_hg;
+  const int hg = r < full ? w >> 3 : w % n_hg;
+  const int s = p / batch;
+  return {(p - s % batch + batch) % batch, s, hg};
+}
+
 }  // namespace ws
 }  // namespace spmla

@@ -33,6 +33,7 @@ struct DecodeArgs {
   int32_t num_pages, page_size; const int32_t* bt; int32_t bt_stride;
   const int32_t* lens; int32_t batch; int64_t max_len; const int32_t* indices; int32_t k;
   int32_t n_heads, d_latent, d_rope; float sm_scale; int32_t num_splits;
+  int32_t split_tokens;  // 0: ceil(n / num_splits) rounded up to 32; else the fixed split length
   float* o_part; float* lse_part; int32_t* status;
 };
 int launch_decode(const DecodeArgs& a, hipStream_t stream);

@@ -55,7 +55,8 @@ __global__ __launch_bounds__(kDecThreads) void mla_decode_kernel(
     const void* __restrict__ q, const uint8_t* __restrict__ kv, const float* __restrict__ kv_scale,
     int32_t num_pages, int32_t page_shift, const int32_t* __restrict__ bt, int32_t bt_stride,
     const int32_t* __restrict__ lens, int64_t max_len, const int32_t* __restrict__ indices, int32_t k,
-    int32_t n_heads, float sm_scale_log2, int32_t num_splits, int32_t n_hg, float* __restrict__ o_part,
+    int32_t n_heads, float sm_scale_log2, int32_t num_splits, int32_t split_tok, int32_t n_hg,
+    float* __restrict__ o_part,
     float* __restrict__ lse_part, int32_t* __restrict__ status) {
   typedef typename Op::elem E;
   constexpr int KPL = Op::KPL;
@@ -123,9 +124,13 @@ __global__ __launch_bounds__(kDecThreads) void mla_decode_kernel(
     return;
   }
   const int64_t n = indices ? (int64_t)k : (int64_t)L;
-  const int64_t per = ((n + num_splits - 1) / num_splits + kTile - 1) / kTile * kTile;
+  const int64_t per = split_tok > 0 ? (int64_t)split_tok : ((n + num_splits - 1) / num_splits + kTile - 1) / kTile * kTile;
   const int64_t p_begin = (int64_t)s * per;
-  const int64_t p_end = min(n, p_begin + per);
+  const int64_t p_end = split_tok > 0 && s == num_splits - 1 ? n : min(n, p_begin + per);
+  if (split_tok > 0 && p_begin >= p_end) {  // past the request's last token: only lse -inf
+    if (wave_active && half == 0 && lane < kHeadsPerWave && head0 + lane < n_heads) *out_lse(head0 + lane) = -INFINITY;
+    return;
+  }
 
   // Query fragments for this wave's half of the dims: B operand of S^T = K . Q^T
   // (column = head r16).
@@ -458,7 +463,7 @@ static int launch_one(const DecodeArgs& a, hipStream_t stream) {
   const float sm_log2 = a.sm_scale * 1.44269504088896340736f;
   hipLaunchKernelGGL((mla_decode_kernel<Op, KDT, KSTEPS, NT>), dim3((unsigned)grid), dim3(kDecThreads), 0, stream,
                      a.q, reinterpret_cast<const uint8_t*>(a.kv), a.kv_scale, a.num_pages, page_shift, a.bt,
-                     a.bt_stride, a.lens, a.max_len, a.indices, a.k, a.n_heads, sm_log2, a.num_splits, n_hg,
+                     a.bt_stride, a.lens, a.max_len, a.indices, a.k, a.n_heads, sm_log2, a.num_splits, a.split_tokens, n_hg,
                      a.o_part, a.lse_part, a.status);
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }

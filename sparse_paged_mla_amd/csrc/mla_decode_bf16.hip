@@ -87,7 +87,7 @@ __global__ __launch_bounds__(kThreads) void mla_decode_bf16ws_kernel(
     const __bf16* __restrict__ q, const uint8_t* __restrict__ kv, int32_t num_pages, int32_t page_shift,
     const int32_t* __restrict__ bt, int32_t bt_stride, const int32_t* __restrict__ lens, int64_t max_len,
     const int32_t* __restrict__ indices, int32_t k, int32_t n_heads, float sm_scale_log2, int32_t num_splits,
-    int32_t n_hg, float* __restrict__ o_part, float* __restrict__ lse_part, int32_t* __restrict__ status) {
+    int32_t split_tok, int32_t n_hg, float* __restrict__ o_part, float* __restrict__ lse_part, int32_t* __restrict__ status) {
   __shared__ __attribute__((aligned(16))) uint8_t Kbuf[kNB][kTileBytes];
   __shared__ __attribute__((aligned(16))) int32_t seg_row[kSeg];       // cache row, or -1 when masked
   __shared__ __attribute__((aligned(16))) __bf16 Pbuf[2][kHeadsWg * kPStride];
@@ -108,10 +108,8 @@ __global__ __launch_bounds__(kThreads) void mla_decode_bf16ws_kernel(
   const int page_size = 1 << page_shift;
   const float kNaN = __uint_as_float(0x7FC00000u);
 
-  const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  const int hg = logical % n_hg;
-  const int s = (logical / n_hg) % num_splits;
-  const int b = logical / (n_hg * num_splits);
+  const WgCoord wc = wg_coord(blockIdx.x, gridDim.x, num_splits, n_hg, split_tok > 0);
+  const int hg = wc.hg, s = wc.s, b = wc.b;
   const int head_base = hg * kHeadsWg;
 
   auto out_o = [&](int h, int dim) -> float* {
@@ -140,7 +138,9 @@ __global__ __launch_bounds__(kThreads) void mla_decode_bf16ws_kernel(
   const bool sparse = indices != nullptr;
   constexpr int kNT = kSeg / kThreads;   // table entries per thread
   constexpr int kNP = kNT + 2 * kLoads;  // and the value waves' pieces of tiles 0 and 1
-  auto split_len = [&](int64_t n) { return ((n + num_splits - 1) / num_splits + kTileTok - 1) / kTileTok * kTileTok; };
+  auto split_len = [&](int64_t n) -> int64_t {
+    return split_tok > 0 ? split_tok : ((n + num_splits - 1) / num_splits + kTileTok - 1) / kTileTok * kTileTok;
+  };
   auto pos_at = [&](int64_t p0, int i) -> int64_t {
     if (i < kNT) return p0 + tid + i * kThreads;
     return p0 + ((i - kNT) / kLoads) * kTileTok + piece_row((i - kNT) % kLoads);
@@ -168,7 +168,14 @@ __global__ __launch_bounds__(kThreads) void mla_decode_bf16ws_kernel(
   const int64_t n = sparse ? (int64_t)k : (int64_t)L;
   const int64_t per = split_len(n);
   const int64_t p_begin = (int64_t)s * per;
-  const int64_t p_end = min(n, p_begin + per);
+  const int64_t p_end = split_tok > 0 && s == num_splits - 1 ? n : min(n, p_begin + per);
+  if (split_tok > 0 && p_begin >= p_end) {
+    // A fixed split length leaves the splits past the request's last token
+    // empty: they only mark their partial as empty (lse -inf).
+    vm_wait<0>();  // the early loads land before the workgroup ends
+    if (tid < kHeadsWg && head_base + tid < n_heads) *out_lse(head_base + tid) = -INFINITY;
+    return;
+  }
   const int32_t* idxb = sparse ? indices + (int64_t)b * k : nullptr;
   const bool any_token = p_begin < p_end;
   // Tokens at split positions and the pages of tokens, for the segments
@@ -599,7 +606,7 @@ int launch_decode_bf16(const DecodeArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(mla_decode_bf16ws_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream,
                      reinterpret_cast<const __bf16*>(a.q), reinterpret_cast<const uint8_t*>(a.kv), a.num_pages,
                      page_shift, a.bt, a.bt_stride, a.lens, a.max_len, a.indices, a.k, a.n_heads, sm_log2,
-                     a.num_splits, n_hg, a.o_part, a.lse_part, a.status);
+                     a.num_splits, a.split_tokens, n_hg, a.o_part, a.lse_part, a.status);
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 

@@ -42,7 +42,8 @@ __global__ __launch_bounds__(kGThreads) void mla_decode_generic_kernel(
     const void* __restrict__ q, const uint8_t* __restrict__ kv, const float* __restrict__ kv_scale, int32_t num_pages,
     int32_t page_shift, const int32_t* __restrict__ bt, int32_t bt_stride, const int32_t* __restrict__ lens,
     int64_t max_len, const int32_t* __restrict__ indices, int32_t k, int32_t n_heads, int32_t d_latent, int32_t d_rope,
-    float sm_scale, int32_t num_splits, int32_t n_hg, float* __restrict__ o_part, float* __restrict__ lse_part,
+    float sm_scale, int32_t num_splits, int32_t split_tok, int32_t n_hg, float* __restrict__ o_part,
+    float* __restrict__ lse_part,
     int32_t* __restrict__ status) {
   extern __shared__ __attribute__((aligned(16))) float gsm[];
   const int D = d_latent + d_rope;
@@ -92,8 +93,13 @@ __global__ __launch_bounds__(kGThreads) void mla_decode_generic_kernel(
 
   const bool sparse = indices != nullptr;
   const int64_t n = sparse ? (int64_t)k : (int64_t)L;
-  const int64_t per = ((n + num_splits - 1) / num_splits + 31) / 32 * 32;
-  const int64_t p_begin = (int64_t)s * per, p_end = min(n, p_begin + per);
+  const int64_t per = split_tok > 0 ? (int64_t)split_tok : ((n + num_splits - 1) / num_splits + 31) / 32 * 32;
+  const int64_t p_begin = (int64_t)s * per;
+  const int64_t p_end = split_tok > 0 && s == num_splits - 1 ? n : min(n, p_begin + per);
+  if (split_tok > 0 && p_begin >= p_end) {  // past the request's last token: only lse -inf
+    if (tid < kGHeads && hg * kGHeads + tid < n_heads) *out_lse(hg * kGHeads + tid) = -INFINITY;
+    return;
+  }
   const int32_t* btb = bt + (int64_t)b * bt_stride;
   const int n_out = (d_latent - ti + 15) / 16;  // output dims of this thread: ti, ti + 16, ...
 
@@ -198,7 +204,7 @@ int launch_generic_t(const DecodeArgs& a, hipStream_t stream) {
     return -3;
   hipLaunchKernelGGL((mla_decode_generic_kernel<QDT, KDT>), dim3((unsigned)grid), dim3(kGThreads), lds, stream, a.q,
                      reinterpret_cast<const uint8_t*>(a.kv), a.kv_scale, a.num_pages, page_shift, a.bt, a.bt_stride,
-                     a.lens, a.max_len, a.indices, a.k, a.n_heads, a.d_latent, a.d_rope, a.sm_scale, a.num_splits, n_hg,
+                     a.lens, a.max_len, a.indices, a.k, a.n_heads, a.d_latent, a.d_rope, a.sm_scale, a.num_splits, a.split_tokens, n_hg,
                      a.o_part, a.lse_part, a.status);
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }

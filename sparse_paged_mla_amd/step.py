@@ -32,20 +32,79 @@ class DeviceBatch:
 
 # KV splits per workload as timed: enough (request, split, head group)
 # workgroups to fill 256 compute units without splitting short token lists.
+# "balanced": one split length for the whole batch (balanced_splits), so a
+# ragged dense batch's long requests take more splits than its short ones.
 # Measured on the box: c4 (128 requests) runs 201 µs per step with one split
 # (256 workgroups, one round) against 224 with two; c2 is best at 4 and c5 at
 # 8 of {2, 4, 8} and {4, 8, 16}.
-DEFAULT_SPLITS = {"c1": 1, "c2": 4, "c3": 2, "c3f": 2, "c4": 1, "c5": 8}
+DEFAULT_SPLITS = {"c1": 1, "c2": "balanced", "c3": 2, "c3f": 2, "c4": 1, "c5": 8}
+
+
+def _busy_per_xcd(lens, c, num_splits, n_hg, xcds=8):
+    """Workgroups with work per XCD when a fixed split length c is used: the
+    decode kernels' order for that case (decode_ws.h, wg_coord): pairs
+    split-major with the requests of split s rotated by s, dealt to the XCDs
+    round-robin, a pair's n_hg workgroups on one XCD."""
+    B = len(lens)
+    pairs = B * num_splits
+    full = pairs // xcds
+    busy = [0] * xcds
+    for p in range(pairs):
+        s = p // B
+        b = (p - s % B + B) % B
+        if s * c < lens[b]:
+            if p < full * xcds:
+                busy[p % xcds] += n_hg
+            else:  # the last, partial round: ids in order, dealt round-robin
+                for hg in range(n_hg):
+                    busy[(full * xcds * n_hg + (p - full * xcds) * n_hg + hg) % xcds] += 1
+    return busy
+
+
+def balanced_splits(lens, n_heads, cus=256, heads_per_group=64, tile=32, max_splits=64, min_tokens=512, xcds=8):
+    """(num_splits, split_tokens) for a ragged dense batch: one split length c
+    for every request, so that a long request takes more splits than a short
+    one and every workgroup gets about the same work whatever the length mix.
+    c is the smallest multiple of `tile`, and at least min_tokens (every
+    workgroup pays a fixed start-up of several microseconds), for which no
+    XCD gets more workgroups with work than it has compute units (cus / xcds;
+    one per (request, split) pair and group of heads_per_group heads): the
+    whole batch then runs in one round.  `lens` are the host-side context
+    lengths (a serving loop's scheduler knows them)."""
+    lens = [max(0, int(x)) for x in lens]
+    if not lens or max(lens) == 0:
+        return 1, 0
+    n_hg = -(-n_heads // heads_per_group)
+    target = max(1, cus // n_hg)
+    c = max(min_tokens, tile, -(-max(1, sum(lens) // target) // tile) * tile)
+    c = -(-c // tile) * tile
+    while c < max(lens):
+        S = max(1, max(-(-L // c) for L in lens))
+        if S <= max_splits and max(_busy_per_xcd(lens, c, S, n_hg, xcds)) <= cus // xcds:
+            break
+        c += tile
+    return max(1, min(max_splits, max(-(-L // c) for L in lens))), c
+
+
+def default_splits(name, lens, n_heads, override=0):
+    """(num_splits, split_tokens) of a workload as timed: `override` splits of
+    equal count when given, else DEFAULT_SPLITS (balanced_splits for
+    "balanced")."""
+    if override:
+        return int(override), 0
+    d = DEFAULT_SPLITS.get(name, 1)
+    return balanced_splits(lens, n_heads) if d == "balanced" else (int(d), 0)
 
 
 class DecodeStep:
     """Holds the step's output and scratch buffers for a fixed batch shape."""
 
-    def __init__(self, batch: DeviceBatch, num_splits: int = 1):
+    def __init__(self, batch: DeviceBatch, num_splits: int = 1, split_tokens: int = 0):
         dev = batch.q.device
         B, H, _ = batch.q.shape
         self.batch = batch
         self.num_splits = num_splits
+        self.split_tokens = split_tokens
         self.sparse = batch.topk > 0
         self.status = torch.zeros(B, dtype=torch.int32, device=dev)
         if self.sparse:
@@ -75,7 +134,7 @@ class DecodeStep:
         b = self.batch
         mla_paged_decode(b.q, b.kv, b.kv_scale, b.block_table, b.lens, b.max_len,
                          self.idx if self.sparse else None, b.d_latent, b.sm_scale, self.o_part, self.lse_part,
-                         self.status, stream)
+                         self.status, stream, split_tokens=self.split_tokens)
 
     def merge(self, stream=None):
         if self.num_splits > 1:

@@ -78,7 +78,8 @@ def _idx(lib, **kw):
 def _dec(lib, **kw):
     a = dict(q=FAKE, q_dtype=BF16, kv=FAKE, kv_scale=FAKE, kv_dtype=FP8, num_pages=10, page_size=64, bt=FAKE,
              bt_stride=4, lens=FAKE, batch=2, max_len=256, indices=FAKE, k=2048, n_heads=128, d_latent=512,
-             d_rope=64, sm_scale=1 / 24, splits=1, o_part=FAKE, lse_part=FAKE, status=None, stream=None)
+             d_rope=64, sm_scale=1 / 24, splits=1, split_tokens=0, o_part=FAKE, lse_part=FAKE, status=None,
+             stream=None)
     a.update(kw)
     return lib.mla_paged_decode(*a.values())
 
@@ -144,8 +145,8 @@ def test_decode_rejects(lib):
                                      ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
                                      ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
                                      ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
-                                     ctypes.c_int32, ctypes.c_float, ctypes.c_int32, ctypes.c_void_p,
-                                     ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+                                     ctypes.c_int32, ctypes.c_float, ctypes.c_int32, ctypes.c_int32,
+                                     ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     assert _dec(lib, d_latent=260) == EUNSUPPORTED          # widths must be multiples of 8
     assert _dec(lib, d_rope=12) == EUNSUPPORTED
     assert _dec(lib, d_latent=0) == EINVAL
@@ -154,6 +155,8 @@ def test_decode_rejects(lib):
     assert _dec(lib, kv_dtype=F32) == EUNSUPPORTED          # bf16 queries need a bf16/FP8 cache
     assert _dec(lib, splits=0) == EUNSUPPORTED
     assert _dec(lib, splits=65) == EUNSUPPORTED
+    assert _dec(lib, split_tokens=-32) == EINVAL
+    assert _dec(lib, split_tokens=48) == EINVAL             # a split length is whole 32-token tiles
     assert _dec(lib, sm_scale=0.0) == EINVAL
     assert _dec(lib, sm_scale=float("nan")) == EINVAL
     assert _dec(lib, n_heads=0) == EUNSUPPORTED

@@ -27,15 +27,16 @@ def _say(msg):
 @pytest.mark.parametrize("name", ["c2", "c3", "c3f", "c4", "c5"])
 def test_full_size_step(name):
     import sparse_paged_mla_amd as spm
-    from sparse_paged_mla_amd.step import DEFAULT_SPLITS, DecodeStep
+    from sparse_paged_mla_amd.step import DecodeStep, default_splits
     spm.load_library()
     _say(f"{name}: generating inputs")
     inp = gen.make_inputs(name)
     cfg = inp.cfg
-    splits = DEFAULT_SPLITS[name]
+    splits, split_tokens = default_splits(name, inp.lens, cfg.n_heads)
     db = device_batch(inp)
-    step = DecodeStep(db, num_splits=splits)
-    _say(f"{name}: B={cfg.batch} sum L={int(inp.lens.sum())} max_len={inp.max_len} splits={splits}: running the step")
+    step = DecodeStep(db, num_splits=splits, split_tokens=split_tokens)
+    _say(f"{name}: B={cfg.batch} sum L={int(inp.lens.sum())} max_len={inp.max_len} splits={splits} "
+         f"split_tokens={split_tokens}: running the step")
     step.run()
     torch.cuda.synchronize()
     status = step.status.cpu().numpy()

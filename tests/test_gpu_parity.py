@@ -20,19 +20,20 @@ def _lib():
     return spm
 
 
-def _step(inp, splits=1):
+def _step(inp, splits=1, split_tokens=0):
     from sparse_paged_mla_amd.step import DecodeStep
     db = device_batch(inp)
-    st = DecodeStep(db, num_splits=splits)
+    st = DecodeStep(db, num_splits=splits, split_tokens=split_tokens)
     st.run()
     torch.cuda.synchronize()
     return db, st
 
 
-def _check_full(inp, splits=1, what=""):
-    print(f"[parity] {what} B={inp.cfg.batch} lens={list(inp.lens[:8])} splits={splits}", flush=True)
+def _check_full(inp, splits=1, what="", split_tokens=0):
+    print(f"[parity] {what} B={inp.cfg.batch} lens={list(inp.lens[:8])} splits={splits} split_tokens={split_tokens}",
+          flush=True)
     cfg = inp.cfg
-    db, st = _step(inp, splits)
+    db, st = _step(inp, splits, split_tokens)
     status = st.status.cpu().numpy()
     assert not status.any(), status
     idx = None
@@ -346,6 +347,45 @@ def test_empty_splits(name):
     _lib()
     cfg = gen.CONFIGS[name].with_(batch=2, topk=32)
     _check_full(gen.make_inputs(cfg, lens=[40, 3000]), 4, f"{name} empty splits")
+
+
+# A fixed split length (split_tokens): long requests take more splits than
+# short ones, splits past a request's end carry lse -inf only, and the last
+# split takes everything from its start on.  Dense and sparse, on every decode
+# kernel (FP8 and bf16 role-specialised, fp32 small shapes, generic shapes).
+FIXED_SPLITS = [
+    pytest.param("c2", dict(), [100, 3000, 777, 5000], 6, 1024, id="bf16-dense"),
+    pytest.param("c2", dict(), [100, 3000, 777, 5000], 2, 1024, id="bf16-dense-last-takes-rest"),
+    pytest.param("c2", dict(cache_dtype=gen.FP8), [2100, 65, 4000], 5, 1024, id="fp8-dense"),
+    pytest.param("c3f", dict(), [3000, 70, 9000], 4, 512, id="fp8-sparse"),
+    pytest.param("c3", dict(), [3000, 5000], 3, 1024, id="bf16-sparse"),
+    pytest.param("c1", dict(idx_heads=0, topk=0), [37, 100], 3, 32, id="f32-small-dense"),
+    pytest.param("c2", dict(d_latent=256, d_rope=32), [900, 3000], 4, 800, id="generic-dense"),
+]
+
+
+@pytest.mark.parametrize("name,over,lens,splits,split_tokens", FIXED_SPLITS)
+def test_fixed_split_length(name, over, lens, splits, split_tokens):
+    _lib()
+    cfg = gen.CONFIGS[name].with_(batch=len(lens), **over)
+    _check_full(gen.make_inputs(cfg, lens=lens), splits, f"{name} fixed split", split_tokens=split_tokens)
+
+
+def test_balanced_splits_on_a_ragged_batch():
+    """The step's balanced policy on a small ragged dense batch, and the
+    partials it leaves: splits past a request's end have lse -inf."""
+    from sparse_paged_mla_amd.step import balanced_splits
+    _lib()
+    cfg = gen.CONFIGS["c2"].with_(batch=5)
+    lens = [300, 6000, 1500, 9000, 64]
+    S, c = balanced_splits(lens, cfg.n_heads)
+    assert c % 32 == 0 and S == max(-(-L // c) for L in lens)
+    _, st = _check_full(gen.make_inputs(cfg, lens=lens), S, "balanced", split_tokens=c)
+    lse_p = st.lse_part.cpu().numpy()
+    for b, L in enumerate(lens):
+        for s in range(S):
+            live = s * c < L
+            assert np.isfinite(lse_p[b, s]).all() == live, (b, s)
 
 
 # ------------------------------------------------------------ fault handling
