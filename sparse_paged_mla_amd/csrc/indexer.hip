@@ -55,6 +55,30 @@ __device__ __forceinline__ int xcd_remap(int bid, int n) {
   return xcd < r ? xcd * (q + 1) + slot : r * (q + 1) + (xcd - r) * q + slot;
 }
 
+// Run of each wave: with two workgroups resident per CU, the two waves that
+// share a SIMD do not progress alike (the older wave is issued first), so a
+// wave of the workgroup placed first on its CU takes a larger share of the
+// steps.  The dispatcher places workgroup ids round-robin over the XCDs and,
+// within an XCD, one per CU before the second ones, so with the full grid
+// the first half of each XCD's logical range (xcd_remap) is the first-placed
+// half.  Shares are (100 + kIdxFirstExtra) : (100 - kIdxFirstExtra); any
+// other grid splits evenly.  Wave i's run starts at step run_start(i).
+// Measured on c3f (64 requests, 32K-128K tokens, FP8 keys): with even runs
+// the first-placed workgroups end at about 96 us and the others at about
+// 115; shares 120 : 80 took the kernel from 133 to 129.5 us (108 : 92 and
+// 114 : 86 less, 126 : 74 slower again).
+constexpr int64_t kIdxFirstExtra = 20;
+__device__ __forceinline__ int64_t run_start(int64_t total, int64_t i, int64_t nw, int grid, bool two_per_cu) {
+  if (!two_per_cu || grid != 2 * kNumCu || kIdxFirstExtra == 0) return total * i / nw;
+  constexpr int64_t kFirst = 100 + kIdxFirstExtra, kSecond = 100 - kIdxFirstExtra;
+  constexpr int64_t kPerXcd = 2 * kNumCu / 8, kHalf = kPerXcd / 2;
+  const int64_t wg = i >> 2, wv = i & 3;
+  const int64_t x = wg / kPerXcd, sl = wg % kPerXcd;
+  const int64_t before = x * kHalf * (kFirst + kSecond) + min(sl, kHalf) * kFirst + max<int64_t>(0, sl - kHalf) * kSecond;
+  const int64_t wcum = 4 * before + wv * (sl < kHalf ? kFirst : kSecond);
+  return total * wcum / (4 * 8 * kHalf * (kFirst + kSecond));
+}
+
 __device__ __forceinline__ int64_t wave_sum_i64(int64_t v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
@@ -139,7 +163,9 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(
   int64_t total = wave_sum_i64(mine);
   total = ((int64_t)__builtin_amdgcn_readfirstlane((int32_t)(total >> 32)) << 32) |
           (uint32_t)__builtin_amdgcn_readfirstlane((int32_t)total);
-  const int64_t u0 = total * gw / nw, u1 = total * (gw + 1) / nw;
+  constexpr bool two_per_cu = IdxWg<MT>::per_cu == 2;
+  const int64_t u0 = run_start(total, gw, nw, gridDim.x, two_per_cu);
+  const int64_t u1 = run_start(total, gw + 1, nw, gridDim.x, two_per_cu);
   if (u0 >= u1) return;
   int32_t b0 = 0;
   int64_t s0 = 0;  // step index of u0 within request b0
