@@ -196,11 +196,19 @@ def time_cache_append(cfg, db, inp, steps, flush, run_flush):
             "note": "one launch of a few hundred bytes per request: launch- and latency-bound"}
 
 
-def time_page_check(cfg, db, inp, steps, flush, run_flush):
-    """The KV-page integrity check a server may run before the step reads the
-    cache (one kv_page_check call over every covered block-table entry),
-    timed cold like the step.  Tags: page p carries p * 0x9E3779B97F4A7C15
-    mod 2^64 (distinct for every page) and every entry records its page's tag."""
+def time_page_check(cfg, db, inp, steps, flush, run_flush, step=None):
+    """The KV-page integrity check a server may run with the step (one
+    kv_page_check call over every covered block-table entry), timed cold like
+    the step: alone, and (with `step`) on a second stream of default priority
+    beside the step, started when the indexer is done (the top-k launches
+    leave most compute units idle; beside the indexer, whose grid fills the
+    GPU, it added twice its own time) and waited for at the step's end (the
+    check reads only block tables and tags, nothing the step writes, and its
+    status bits mark the requests whose outputs to discard).  On c3f it still
+    adds a little more than its own time (8.0 against 6.6 us): the
+    cross-stream hand-off costs about what the overlap hides.  Tags: page p carries
+    p * 0x9E3779B97F4A7C15 mod 2^64 (distinct for every page) and every entry
+    records its page's tag."""
     import numpy as np
     import torch
     import sparse_paged_mla_amd as spm
@@ -229,8 +237,48 @@ def time_page_check(cfg, db, inp, steps, flush, run_flush):
     us = statistics.fmean(e0.elapsed_time(e1) for e0, e1 in evs) * 1e3
     entries = int(((inp.lens + P - 1) // P).sum())
     nbytes = entries * (4 + 8 + 8) + 4 * cfg.batch
-    return {"us": round(us, 2), "entries": entries, "algorithmic_bytes": nbytes,
-            "achieved_GBps": round(nbytes / (us * 1e-6) / 1e9, 1)}
+    out = {"us": round(us, 2), "entries": entries, "algorithmic_bytes": nbytes,
+           "achieved_GBps": round(nbytes / (us * 1e-6) / 1e9, 1)}
+    if step is None:
+        return out
+    side = torch.cuda.Stream()  # default priority, like the step's stream
+    marks = [(torch.cuda.Event(), torch.cuda.Event()) for _ in range(steps)]
+    pair = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+            for _ in range(2)]
+    main = torch.cuda.current_stream()
+
+    def with_check(i):
+        go, done = marks[i]
+        if step.sparse:
+            step.indexer()
+        go.record(main)
+        with torch.cuda.stream(side):
+            side.wait_event(go)
+            check()
+            done.record(side)
+        if step.sparse:
+            step.select()
+        step.attend()
+        step.merge()
+        main.wait_event(done)
+
+    for i in range(3):
+        with_check(i)
+    torch.cuda.synchronize()
+    for i in range(steps):  # interleaved: the step alone, then with the check beside it
+        for mode in (0, 1):
+            if flush:
+                run_flush()
+            e0, e1 = pair[mode][i]
+            e0.record()
+            step.run() if mode == 0 else with_check(i)
+            e1.record()
+    torch.cuda.synchronize()
+    assert not status.cpu().numpy().any(), "page check flagged a request on clean inputs"
+    alone, beside = (statistics.fmean(e0.elapsed_time(e1) for e0, e1 in pair[m]) * 1e3 for m in (0, 1))
+    out.update(step_us_alone=round(alone, 1), step_us_with_check_on_a_second_stream=round(beside, 1),
+               added_us=round(beside - alone, 2), added_frac_of_step=round((beside - alone) / alone, 4))
+    return out
 
 
 def time_multi_query(cfg, db, inp, n_q, splits, steps, flush, run_flush):
@@ -525,7 +573,8 @@ def main():
                                                    run_flush=lambda: flush_sink.copy_(flush_buf.amax()))
     chk = None
     if legs:
-        chk = time_page_check(cfg, db, inp, args.steps, flush, run_flush=lambda: flush_sink.copy_(flush_buf.amax()))
+        chk = time_page_check(cfg, db, inp, args.steps, flush, run_flush=lambda: flush_sink.copy_(flush_buf.amax()),
+                              step=step)
         chk["overhead_frac_of_step"] = round(chk["us"] / (mean_ms * 1e3), 4)
 
     alg = algorithmic(cfg, inp.lens)
