@@ -29,11 +29,18 @@ namespace spmla {
 
 constexpr int kIdxThreads = 256;
 constexpr int kIdxStepBytes = 8192;     // key bytes a wave fetches per step
-// Resident workgroups per compute unit: two, except for kernels holding 8
-// M-tiles of queries (more than 256 registers per lane: one wave per SIMD).
-template <int MT>
+// Workgroup shape.  One query per request (NQ = 1): four waves, each with
+// its own run of steps; two workgroups per compute unit, except for kernels
+// holding 8 M-tiles of queries (more than 256 registers per lane: one wave
+// per SIMD).  Two queries (NQ = 2): two waves, one per query, sharing each
+// step's staged keys; four workgroups per compute unit.
+template <int MT, int NQ = 1>
 struct IdxWg {
-  static constexpr int per_cu = MT >= 8 ? 1 : 2;
+  static constexpr int waves = NQ == 2 ? 2 : 4;
+  static constexpr int per_cu = NQ == 2 ? 4 : MT >= 8 ? 1 : 2;
+  // Waves per SIMD the compiler is held to: two for the pairs (their budget
+  // must stay within 256 registers), no bound otherwise (as measured).
+  static constexpr int min_simd_waves = NQ == 2 ? 2 : 1;
   static constexpr int lds = 160 * 1024 / per_cu;
 };
 constexpr int kIdxMaxHeldSteps = 40;    // steps of scores a wave holds in LDS before writing them
@@ -97,11 +104,16 @@ __device__ __forceinline__ int64_t wave_incl_scan_i64(int64_t v, int lane) {
 // A compile-time choice: with both paths in one kernel the compiler's
 // memory-wait accounting merges them and waits far more than either needs.
 // NQ: queries scored per key read (a multi-query step): the request's NQ
-// queries of n_heads heads each are NQ * n_heads consecutive rows, query i
-// takes M-tiles [i * MT / NQ, (i + 1) * MT / NQ) and writes score row
-// b * NQ + i (status entries likewise).
+// queries of n_heads heads each are NQ * n_heads consecutive rows and query i
+// writes score row b * NQ + i (status entries likewise).  With NQ = 2 a
+// workgroup is a pair of waves that walk one run of steps together: each
+// loads half of a step's keys into the pair's stage (two buffers, one
+// barrier per step) and scores the whole staged step against its own query
+// (MT M-tiles of n_heads heads), so each key is read once for both queries
+// while every wave keeps the one-query register budget.
 template <class Op, int KDT, int KSTEPS, int MT, bool MULTI, int NQ>
-__global__ __launch_bounds__(kIdxThreads) void indexer_kernel(
+__global__ __launch_bounds__(kIdxThreads) __attribute__((amdgpu_waves_per_eu(IdxWg<MT, NQ>::min_simd_waves)))
+void indexer_kernel(
     const void* __restrict__ q_idx, const float* __restrict__ w, const uint8_t* __restrict__ k_pool,
     const float* __restrict__ k_scale, int32_t num_pages, int32_t page_shift,
     const int32_t* __restrict__ bt, int32_t bt_stride, const int32_t* __restrict__ lens, int32_t batch,
@@ -130,13 +142,20 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(
   // request) ends, or when HELD steps are waiting: the stores then come after
   // nearly all of the grid's key reads instead of between them, where each
   // small write costs the reads far more than its bytes.
-  constexpr int STAGE_BYTES = 4 * STEP_TOK * LROW;
-  constexpr int HELD_FIT = (IdxWg<MT>::lds - STAGE_BYTES) / (NQ * 4 * STEP_TOK * 4);
+  static_assert(NQ == 1 || NQ == 2, "one or two queries per request");
+  constexpr bool PAIR = NQ == 2;
+  constexpr int WAVES = IdxWg<MT, NQ>::waves;
+  constexpr int NSTAGE = PAIR ? 2 : 4;  // the pair's two buffers, or one per wave
+  constexpr int NQW = PAIR ? 1 : NQ;    // queries a wave scores
+  constexpr int STAGE_BYTES = NSTAGE * STEP_TOK * LROW;
+  constexpr int HELD_FIT = (IdxWg<MT, NQ>::lds - STAGE_BYTES) / (NQW * WAVES * STEP_TOK * 4);
   constexpr int HELD = HELD_FIT < 1 ? 1 : HELD_FIT > kIdxMaxHeldSteps ? kIdxMaxHeldSteps : HELD_FIT;
-  constexpr int MTQ = MT / NQ;  // M-tiles per query
-  static_assert(MT % NQ == 0, "queries split the M-tiles evenly");
-  __shared__ __attribute__((aligned(16))) uint8_t stage[4][STEP_TOK * LROW];
-  __shared__ __attribute__((aligned(16))) float held[NQ][4][HELD * STEP_TOK];
+  constexpr int MTQ = MT / NQW;  // M-tiles per query
+  static_assert(MT % NQW == 0, "queries split the M-tiles evenly");
+  constexpr int PW = PAIR ? PIECES / 2 : PIECES;  // pieces of a step this wave loads
+  constexpr int WLOADS = (PW + 63) / 64;
+  __shared__ __attribute__((aligned(16))) uint8_t stage[NSTAGE][STEP_TOK * LROW];
+  __shared__ __attribute__((aligned(16))) float held[NQW][WAVES][HELD * STEP_TOK];
   const int32_t rows = NQ * n_heads;  // query rows of one request
 
   const int lane = threadIdx.x & 63;
@@ -145,9 +164,13 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4;
   const int r16 = lane & 15;
-  const int64_t nw = (int64_t)gridDim.x * 4;
-  const int64_t gw = (int64_t)xcd_remap(blockIdx.x, gridDim.x) * 4 + wv;
-  uint8_t* my_stage = stage[wv];
+  // Run units: waves, or pairs of waves (the pair's waves share one run).
+  const int64_t nw = PAIR ? (int64_t)gridDim.x : (int64_t)gridDim.x * 4;
+  const int64_t gw = PAIR ? (int64_t)xcd_remap(blockIdx.x, gridDim.x)
+                          : (int64_t)xcd_remap(blockIdx.x, gridDim.x) * 4 + wv;
+  const int qw = PAIR ? wv : 0;          // the wave's query (pair) or first query
+  const int pbase = PAIR ? wv * PW : 0;  // the wave's first piece of a step
+  int cbuf = 0;                          // the pair's stage buffer for the next step consumed
 
   auto len_ok = [&](int32_t Lb) -> bool { return Lb >= 0 && (int64_t)Lb <= max_len && (int64_t)Lb <= bt_cap; };
   auto steps_of = [&](int32_t Lb) -> int64_t { return len_ok(Lb) ? ((int64_t)Lb + STEP_TOK - 1) / STEP_TOK : 0; };
@@ -157,13 +180,13 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(
   for (int i = lane; i < batch; i += 64) {
     const int32_t Lb = lens[i];
     mine += steps_of(Lb);
-    if (gw == 0 && !len_ok(Lb) && status)
+    if (gw == 0 && wv == 0 && !len_ok(Lb) && status)
       for (int qi = 0; qi < NQ; ++qi) atomicOr(status + (int64_t)i * NQ + qi, kBadLen);
   }
   int64_t total = wave_sum_i64(mine);
   total = ((int64_t)__builtin_amdgcn_readfirstlane((int32_t)(total >> 32)) << 32) |
           (uint32_t)__builtin_amdgcn_readfirstlane((int32_t)total);
-  constexpr bool two_per_cu = IdxWg<MT>::per_cu == 2;
+  constexpr bool two_per_cu = !PAIR && IdxWg<MT, NQ>::per_cu == 2;
   const int64_t u0 = run_start(total, gw, nw, gridDim.x, two_per_cu);
   const int64_t u1 = run_start(total, gw + 1, nw, gridDim.x, two_per_cu);
   if (u0 >= u1) return;
@@ -196,8 +219,9 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(
   auto load_query = [&](int32_t rb) __attribute__((always_inline)) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      const int h = mt * 16 + r16;
-      if (h < rows) {
+      const int hq = mt * 16 + r16;     // row within the wave's queries
+      const int h = qw * n_heads + hq;  // row within the request's queries
+      if (hq < NQW * n_heads) {
         uint32_t raw[(GROUP_ELEMS * QE + 3) / 4];
         const uint8_t* qp =
             reinterpret_cast<const uint8_t*>(q_idx) + (((int64_t)rb * rows + h) * D + g * GROUP_ELEMS) * QE;
@@ -210,7 +234,7 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int hh = mt * 16 + g * 4 + i;
-        wr[mt][i] = hh < rows ? w[(int64_t)rb * rows + hh] : 0.f;
+        wr[mt][i] = hh < NQW * n_heads ? w[(int64_t)rb * rows + qw * n_heads + hh] : 0.f;
       }
     }
   };
@@ -277,8 +301,8 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(
         const int64_t row0 = page_ok ? ((int64_t)page << page_shift) + t0_in_page : 0;
         const uint8_t* base = k_pool + row0 * ROW_BYTES;
 #pragma unroll
-        for (int i = 0; i < LOADS; ++i) {
-          const int piece = min(i * 64 + lane, PIECES - 1);
+        for (int i = 0; i < WLOADS; ++i) {
+          const int piece = pbase + min(i * 64 + lane, PW - 1);
           const int tok = piece / ROW_PIECES;
           const int off = (tok < left ? tok * ROW_BYTES : 0) + (piece % ROW_PIECES) * 16;
           load_nt16(base + off, raw[i]);
@@ -289,8 +313,8 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(
         bad = tok < left && !page_ok;
       } else {
 #pragma unroll
-        for (int i = 0; i < LOADS; ++i) {
-          const int piece = min(i * 64 + lane, PIECES - 1);
+        for (int i = 0; i < WLOADS; ++i) {
+          const int piece = pbase + min(i * 64 + lane, PW - 1);
           bool bad_i;
           const int64_t row = row_of(piece / ROW_PIECES, bad_i);
           load_nt16(k_pool + row * ROW_BYTES + (piece % ROW_PIECES) * 16, raw[i]);
@@ -308,8 +332,8 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(
       __builtin_amdgcn_wave_barrier();
       const int cnt = n_held * STEP_TOK;
 #pragma unroll
-      for (int qi = 0; qi < NQ; ++qi) {
-        float* out = sc_out + qi * score_stride;
+      for (int qi = 0; qi < NQW; ++qi) {
+        float* out = sc_out + (qw + qi) * score_stride;
         for (int i = lane * 4; i < cnt; i += 256) {
           const int64_t t = t_held + i;
           const float4 v4 = *reinterpret_cast<const float4*>(&held[qi][wv][i]);
@@ -327,15 +351,26 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(
     };
     auto consume = [&](int64_t si, const uint32_t (*raw)[4], float sc, int bad_tok) __attribute__((always_inline)) {
       const int64_t t0 = si * STEP_TOK;
-      // Transpose through the wave's own LDS rows (padded by 16 bytes).
+      // Transpose through LDS rows (padded by 16 bytes): the wave's own rows,
+      // or the pair's stage buffer, which both waves fill (one barrier; with
+      // two buffers a buffer is rewritten only after both waves have passed
+      // the barrier of the step after the one that read it).
+      uint8_t* my_stage = stage[PAIR ? cbuf : wv];
 #pragma unroll
-      for (int i = 0; i < LOADS; ++i) {
-        const int piece = i * 64 + lane;
-        if (piece < PIECES)
+      for (int i = 0; i < WLOADS; ++i) {
+        const int piece = pbase + i * 64 + lane;
+        if (i * 64 + lane < PW)
           *reinterpret_cast<uint4*>(my_stage + (piece / ROW_PIECES) * LROW + (piece % ROW_PIECES) * 16) =
               make_uint4(raw[i][0], raw[i][1], raw[i][2], raw[i][3]);
       }
-      __builtin_amdgcn_wave_barrier();
+      if constexpr (PAIR) {
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        cbuf ^= 1;
+      } else {
+        __builtin_amdgcn_wave_barrier();
+      }
 #pragma unroll
       for (int j = 0; j < SUBS; ++j) {
         const int tok = j * 16 + r16;  // token of this lane's MFMA column
@@ -364,7 +399,7 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(
         const float tsc = __shfl(sc, tok);
         const bool bad = __shfl(bad_tok, tok) != 0;
 #pragma unroll
-        for (int qi = 0; qi < NQ; ++qi) {
+        for (int qi = 0; qi < NQW; ++qi) {
           float v = 0.f;
 #pragma unroll
           for (int mt = qi * MTQ; mt < (qi + 1) * MTQ; ++mt) {
@@ -391,7 +426,7 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_kernel(
     // keys are consumed.  Memory requests complete in order, so this
     // ordering keeps two steps of keys in flight.  Steps past the request's
     // share of the run only touch row 0 and are never consumed.
-    uint32_t raw_a[LOADS][4], raw_b[LOADS][4];
+    uint32_t raw_a[WLOADS][4], raw_b[WLOADS][4];
     float sc_a, sc_b;
     int bad_a, bad_b;
     int32_t pg_a = prep(s);
@@ -432,15 +467,17 @@ static int launch_one(const IndexerArgs& a, hipStream_t stream) {
   constexpr int ROW_BYTES = KSTEPS * 4 * Op::KPL * Storage<KDT>::bytes;
   constexpr int STEP_TOK = IdxStep<ROW_BYTES>::tok;
   const int64_t max_steps = (int64_t)a.batch * ((a.max_len + STEP_TOK - 1) / STEP_TOK);
-  const int64_t grid =
-      std::max<int64_t>(1, std::min<int64_t>((int64_t)kNumCu * IdxWg<MT>::per_cu, (max_steps + 3) / 4));
+  constexpr int kUnits = NQ == 2 ? 1 : 4;  // run units per workgroup: one pair, or four waves
+  const int64_t grid = std::max<int64_t>(
+      1, std::min<int64_t>((int64_t)kNumCu * IdxWg<MT, NQ>::per_cu, (max_steps + kUnits - 1) / kUnits));
+  const dim3 threads(IdxWg<MT, NQ>::waves * 64);
   if (a.page_size < STEP_TOK)
-    hipLaunchKernelGGL((indexer_kernel<Op, KDT, KSTEPS, MT, true, NQ>), dim3((unsigned)grid), dim3(kIdxThreads), 0,
+    hipLaunchKernelGGL((indexer_kernel<Op, KDT, KSTEPS, MT, true, NQ>), dim3((unsigned)grid), threads, 0,
                        stream, a.q_idx, a.w, reinterpret_cast<const uint8_t*>(a.k_pool), a.k_scale, a.num_pages,
                        page_shift, a.bt, a.bt_stride, a.lens, a.batch, a.max_len, a.n_heads, a.scores,
                        a.score_stride, a.status);
   else
-    hipLaunchKernelGGL((indexer_kernel<Op, KDT, KSTEPS, MT, false, NQ>), dim3((unsigned)grid), dim3(kIdxThreads), 0,
+    hipLaunchKernelGGL((indexer_kernel<Op, KDT, KSTEPS, MT, false, NQ>), dim3((unsigned)grid), threads, 0,
                        stream, a.q_idx, a.w, reinterpret_cast<const uint8_t*>(a.k_pool), a.k_scale, a.num_pages,
                        page_shift, a.bt, a.bt_stride, a.lens, a.batch, a.max_len, a.n_heads, a.scores,
                        a.score_stride, a.status);
@@ -450,12 +487,12 @@ static int launch_one(const IndexerArgs& a, hipStream_t stream) {
 template <class Op, int KDT, int KSTEPS>
 static int dispatch_heads(const IndexerArgs& a, hipStream_t s) {
   if (a.n_q == 2) {
-    // Two queries per key read (bf16 queries): the M-tiles split evenly
-    // between them.
+    // Two queries per key read (bf16 queries): a pair of waves, one per
+    // query, each with the query's M-tiles.
     if constexpr (std::is_same<Op, OpBF16>::value) {
-      if (a.n_heads == 16) return launch_one<Op, KDT, KSTEPS, 2, 2>(a, s);
-      if (a.n_heads == 32) return launch_one<Op, KDT, KSTEPS, 4, 2>(a, s);
-      if (a.n_heads == 64) return launch_one<Op, KDT, KSTEPS, 8, 2>(a, s);
+      if (a.n_heads == 16) return launch_one<Op, KDT, KSTEPS, 1, 2>(a, s);
+      if (a.n_heads == 32) return launch_one<Op, KDT, KSTEPS, 2, 2>(a, s);
+      if (a.n_heads == 64) return launch_one<Op, KDT, KSTEPS, 4, 2>(a, s);
     }
     return -2;
   }

@@ -89,3 +89,44 @@ def test_mq_one_query_equals_single_step():
     torch.cuda.synchronize()
     assert torch.equal(single.idx, st.idx[:, 0]) and torch.equal(single.o, st.o[:, 0])
     assert torch.equal(single.lse, st.lse[:, 0])
+
+
+MQ_INDEXER_CASES = [
+    ("c3f", {}),                                   # FP8 keys, 64 heads, page 64
+    ("c3", {}),                                    # bf16 keys
+    ("c3f", {"idx_heads": 32}),
+    ("c3f", {"idx_heads": 16}),
+    ("c3f", {"page_size": 16}),
+]
+
+
+@pytest.mark.parametrize("name,kw", MQ_INDEXER_CASES, ids=lambda v: str(v))
+def test_mq_indexer_equals_one_query_at_a_time(name, kw):
+    """Two queries scored per key read give each query, bit for bit, the
+    scores and status the one-query indexer gives it alone (the per-query
+    sum runs in the same order), over ragged lengths with an empty request,
+    partial pages and several runs per workgroup."""
+    spm = _lib()
+    lens = [0, 1, 63, 65, 3000, 9000, 20000, 70]
+    cfg = gen.CONFIGS[name].with_(batch=len(lens), **kw)
+    print(f"[mq-indexer] {name} {kw} lens={lens}", flush=True)
+    inp = gen.make_inputs(cfg, lens=lens)
+    _, qi, w = gen.make_mq_queries(inp, 2)
+    db = device_batch(inp)
+    B, S = cfg.batch, inp.score_stride
+    qi_d, w_d = tensor(qi, "cuda"), torch.from_numpy(w).cuda()
+    both = torch.full((B * 2, S), float("nan"), device="cuda")
+    st_both = torch.zeros(B, dtype=torch.int32, device="cuda")
+    spm.dsa_indexer_scores_mq(qi_d, w_d, db.k_idx, db.k_idx_scale, db.block_table, db.lens, db.max_len, both,
+                              req_status=st_both)
+    for i in range(2):
+        one = torch.full((B, S), float("nan"), device="cuda")
+        st_one = torch.zeros(B, dtype=torch.int32, device="cuda")
+        spm.dsa_indexer_scores(qi_d[:, i].contiguous(), w_d[:, i].contiguous(), db.k_idx, db.k_idx_scale,
+                               db.block_table, db.lens, db.max_len, one, req_status=st_one)
+        torch.cuda.synchronize()
+        a = both.view(B, 2, S)[:, i].cpu().numpy().view(np.uint32)
+        b = one.cpu().numpy().view(np.uint32)
+        for r, n in enumerate(lens):
+            np.testing.assert_array_equal(a[r, :n], b[r, :n], err_msg=f"request {r} query {i}")
+        np.testing.assert_array_equal(st_both.cpu().numpy(), st_one.cpu().numpy())
