@@ -305,8 +305,8 @@ def time_multi_query(cfg, db, inp, n_q, splits, steps, flush, run_flush):
     assert not st.status.cpu().numpy().any(), "multi-query step flagged a request on clean inputs"
     us = statistics.fmean(e0.elapsed_time(e1) for e0, e1 in evs) * 1e3
     # Roofline of the method: every query's scores, top-k and attention, with
-    # the indexer keys read once for all n_q queries (what a fused indexer
-    # would move; this composition reads them once per query).
+    # the indexer keys read once for all n_q queries (as the two-query
+    # indexer reads them) and one score row written per query.
     alg = algorithmic(cfg, inp.lens)
     sumL = int(inp.lens.sum())
     t_star = (max((alg["indexer"]["bytes"] + (n_q - 1) * 4 * sumL) / (HBM_PEAK_GBS * 1e9),

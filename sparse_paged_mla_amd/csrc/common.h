@@ -19,6 +19,8 @@ typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
 typedef __bf16 v4bf16_t __attribute__((ext_vector_type(4)));
+typedef int v8i_t __attribute__((ext_vector_type(8)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 
@@ -149,6 +151,44 @@ __device__ __forceinline__ float wave_sum_xor16_32(float v) {
   v += __shfl_xor(v, 16);
   v += __shfl_xor(v, 32);
   return v;
+}
+
+// Writes this lane's 32 bf16 values (w[i] holds values 2i, low half, and
+// 2i + 1) as v = 2^(E-7) * (hi + lo/16), hi and lo e4m3 codes, where
+// E = floor(log2 M) and M is the largest |v| over the four lanes of the row
+// (lanes l, l^16, l^32, l^48: the 128 k-slots of one MFMA row), so one scale
+// per row and term serves the block.  hi is v scaled below 256 and rounded
+// to 4 significant bits; the remainder of an element within 2^14 of M is a
+// multiple of its last bf16 bit below half an e4m3 step, so 16 times it is
+// an e4m3 value and the sum is exact; a smaller element keeps an error below
+// 2^-22 of M.  A non-finite element turns the hi codes of its lane into NaN,
+// so the scores it feeds come out NaN.  Magnitudes are compared as bf16
+// bits: without the sign, finite values order as integers and Inf and NaN
+// lie above them.  Call with the whole wave active.
+__device__ __forceinline__ void split_q32(const uint32_t (&w)[16], v8i_t& hi, v8i_t& lo, int& shi, int& slo) {
+  u16x2 m = {0, 0};
+#pragma unroll
+  for (int i = 0; i < 16; ++i) m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, w[i] & 0x7FFF7FFFu));
+  uint32_t mb = max((uint32_t)m[0], (uint32_t)m[1]);
+  const bool bad = mb >= 0x7F80u;
+  mb = max(mb, (uint32_t)__shfl_xor((int)mb, 16));
+  mb = max(mb, (uint32_t)__shfl_xor((int)mb, 32));
+  const int E = max((int)(mb >> 7) - 127, -115);
+  const float mul = __uint_as_float((uint32_t)(134 - E) << 23);  // 2^(7 - E)
+  shi = E + 120;
+  slo = E + 116;
+#pragma unroll
+  for (int d = 0; d < 8; ++d) {
+    const float x0 = __uint_as_float(w[2 * d] << 16) * mul, x1 = __uint_as_float(w[2 * d] & 0xFFFF0000u) * mul;
+    const float x2 = __uint_as_float(w[2 * d + 1] << 16) * mul, x3 = __uint_as_float(w[2 * d + 1] & 0xFFFF0000u) * mul;
+    int h = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
+    h = __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, h, true);
+    const f32x2 r01 = __builtin_amdgcn_cvt_pk_f32_fp8(h, false), r23 = __builtin_amdgcn_cvt_pk_f32_fp8(h, true);
+    int l = __builtin_amdgcn_cvt_pk_fp8_f32((x0 - r01[0]) * 16.f, (x1 - r01[1]) * 16.f, 0, false);
+    l = __builtin_amdgcn_cvt_pk_fp8_f32((x2 - r23[0]) * 16.f, (x3 - r23[1]) * 16.f, l, true);
+    hi[d] = bad ? 0x7F7F7F7F : h;
+    lo[d] = l;
+  }
 }
 
 }  // namespace spmla

@@ -19,8 +19,11 @@
 // while the request does not change) and the tokens on N.  Because a dot
 // product may sum its terms in any order, lane group g owns the contiguous
 // quarter [g*d/4, (g+1)*d/4) of the key row and k-step s takes KPL elements
-// of it; the query fragments use the same permutation.  The ReLU-weighted
-// head sum is a per-lane sum over the 4 rows it holds per M-tile plus two
+// of it; the query fragments use the same permutation.  In the two-query
+// kernel FP8 keys of 128 dims skip the widening: the query is held as two scaled e4m3 terms
+// (exact for every element within 2^14 of its row's largest, off by less
+// than 2^-22 of it otherwise) and each 16x16 block is two scaled FP8 MFMAs
+// over the stored key codes.  The ReLU-weighted head sum is a per-lane sum over the 4 rows it holds per M-tile plus two
 // xor shuffles.
 #include "common.h"
 #include "launch.h"
@@ -147,6 +150,10 @@ void indexer_kernel(
   constexpr int WAVES = IdxWg<MT, NQ>::waves;
   constexpr int NSTAGE = PAIR ? 2 : 4;  // the pair's two buffers, or one per wave
   constexpr int NQW = PAIR ? 1 : NQ;    // queries a wave scores
+  // Scaled FP8 MFMA on the stored key codes (FP8 keys of 128 dims, pairs):
+  // measured on c3f (64 requests, 32K-128K tokens), the pair kernel 238 ->
+  // about 219 us; the one-query kernel 131.5 -> 139 us, so it keeps bf16.
+  constexpr bool F8S = PAIR && kBf && KDT == kFP8 && D == 128;
   constexpr int STAGE_BYTES = NSTAGE * STEP_TOK * LROW;
   constexpr int HELD_FIT = (IdxWg<MT, NQ>::lds - STAGE_BYTES) / (NQW * WAVES * STEP_TOK * 4);
   constexpr int HELD = HELD_FIT < 1 ? 1 : HELD_FIT > kIdxMaxHeldSteps ? kIdxMaxHeldSteps : HELD_FIT;
@@ -214,14 +221,24 @@ void indexer_kernel(
 
   // Query fragments (A operand: rows = heads), permuted like the key slices,
   // and head weights of request `rb`.
+  // With FP8 keys of 128 dims the query is held instead as two scaled e4m3
+  // terms per row (qh, ql with E8M0 scales sh, sl; exact, see split_q32) and
+  // the keys go to the scaled FP8 MFMA as they are stored: no widening.
   typename Op::frag qa[MT][KSTEPS];
+  v8i_t qh[MT], ql[MT];
+  int qsh[MT], qsl[MT];
   float wr[MT][4];
   auto load_query = [&](int32_t rb) __attribute__((always_inline)) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       const int hq = mt * 16 + r16;     // row within the wave's queries
       const int h = qw * n_heads + hq;  // row within the request's queries
-      if (hq < NQW * n_heads) {
+      if constexpr (F8S) {
+        uint32_t raw[16] = {};
+        if (hq < NQW * n_heads)
+          load_raw<64>(reinterpret_cast<const uint8_t*>(q_idx) + (((int64_t)rb * rows + h) * D + g * 32) * 2, raw);
+        split_q32(raw, qh[mt], ql[mt], qsh[mt], qsl[mt]);  // the whole wave, every row
+      } else if (hq < NQW * n_heads) {
         uint32_t raw[(GROUP_ELEMS * QE + 3) / 4];
         const uint8_t* qp =
             reinterpret_cast<const uint8_t*>(q_idx) + (((int64_t)rb * rows + h) * D + g * GROUP_ELEMS) * QE;
@@ -386,15 +403,27 @@ void indexer_kernel(
             for (int y = x; y < RAW_DW; ++y) sl[y] = *reinterpret_cast<const uint32_t*>(src + 4 * y);
           }
         }
-        typename Op::frag kb[KSTEPS];
-        raw_to_frags<Op, KDT, KSTEPS>(sl, kb);
         f32x4 acc[MT];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if constexpr (F8S) {
+          // The lane's 32 key codes are its 32 k-slots, as the query terms'.
+          const v8i_t kc = {(int)sl[0], (int)sl[1], (int)sl[2], (int)sl[3],
+                            (int)sl[4], (int)sl[5], (int)sl[6], (int)sl[7]};
 #pragma unroll
-        for (int st = 0; st < KSTEPS; ++st) {
+          for (int mt = 0; mt < MT; ++mt)
+            acc[mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qh[mt], kc, acc[mt], 0, 0, 0, qsh[mt], 0, 127);
 #pragma unroll
-          for (int mt = 0; mt < MT; ++mt) acc[mt] = Op::mma(qa[mt][st], kb[st], acc[mt]);
+          for (int mt = 0; mt < MT; ++mt)
+            acc[mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ql[mt], kc, acc[mt], 0, 0, 0, qsl[mt], 0, 127);
+        } else {
+          typename Op::frag kb[KSTEPS];
+          raw_to_frags<Op, KDT, KSTEPS>(sl, kb);
+#pragma unroll
+          for (int st = 0; st < KSTEPS; ++st) {
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) acc[mt] = Op::mma(qa[mt][st], kb[st], acc[mt]);
+          }
         }
         const float tsc = __shfl(sc, tok);
         const bool bad = __shfl(bad_tok, tok) != 0;

@@ -101,11 +101,13 @@ MQ_INDEXER_CASES = [
 
 
 @pytest.mark.parametrize("name,kw", MQ_INDEXER_CASES, ids=lambda v: str(v))
-def test_mq_indexer_equals_one_query_at_a_time(name, kw):
-    """Two queries scored per key read give each query, bit for bit, the
-    scores and status the one-query indexer gives it alone (the per-query
-    sum runs in the same order), over ragged lengths with an empty request,
-    partial pages and several runs per workgroup."""
+def test_mq_indexer_against_one_query_at_a_time(name, kw):
+    """Two queries scored per key read, over ragged lengths with an empty
+    request, partial pages and several runs per workgroup.  With bf16 keys
+    each query gets, bit for bit, the scores and status the one-query
+    indexer gives it alone (same arithmetic in the same order); with FP8
+    keys the pair runs the scaled FP8 MFMA, so each query's scores are
+    checked against the oracle's and the status words must agree."""
     spm = _lib()
     lens = [0, 1, 63, 65, 3000, 9000, 20000, 70]
     cfg = gen.CONFIGS[name].with_(batch=len(lens), **kw)
@@ -116,17 +118,25 @@ def test_mq_indexer_equals_one_query_at_a_time(name, kw):
     B, S = cfg.batch, inp.score_stride
     qi_d, w_d = tensor(qi, "cuda"), torch.from_numpy(w).cuda()
     both = torch.full((B * 2, S), float("nan"), device="cuda")
-    st_both = torch.zeros(B, dtype=torch.int32, device="cuda")
+    st_both = torch.zeros(B * 2, dtype=torch.int32, device="cuda")
     spm.dsa_indexer_scores_mq(qi_d, w_d, db.k_idx, db.k_idx_scale, db.block_table, db.lens, db.max_len, both,
                               req_status=st_both)
+    torch.cuda.synchronize()
     for i in range(2):
         one = torch.full((B, S), float("nan"), device="cuda")
         st_one = torch.zeros(B, dtype=torch.int32, device="cuda")
         spm.dsa_indexer_scores(qi_d[:, i].contiguous(), w_d[:, i].contiguous(), db.k_idx, db.k_idx_scale,
                                db.block_table, db.lens, db.max_len, one, req_status=st_one)
         torch.cuda.synchronize()
-        a = both.view(B, 2, S)[:, i].cpu().numpy().view(np.uint32)
-        b = one.cpu().numpy().view(np.uint32)
+        a = both.view(B, 2, S)[:, i].cpu().numpy()
+        np.testing.assert_array_equal(st_both.view(B, 2)[:, i].cpu().numpy(), st_one.cpu().numpy())
+        if cfg.idx_dtype != gen.FP8:
+            b = one.cpu().numpy()
+            for r, n in enumerate(lens):
+                np.testing.assert_array_equal(a[r, :n].view(np.uint32), b[r, :n].view(np.uint32),
+                                              err_msg=f"request {r} query {i}")
+            continue
+        s_ref, mags, _ = oracle.indexer_scores(qi[:, i], w[:, i], inp.k_idx, inp.k_idx_scale, inp.block_table,
+                                               inp.lens, max_len=inp.max_len, score_stride=S)
         for r, n in enumerate(lens):
-            np.testing.assert_array_equal(a[r, :n], b[r, :n], err_msg=f"request {r} query {i}")
-        np.testing.assert_array_equal(st_both.cpu().numpy(), st_one.cpu().numpy())
+            parity.check_scores(a[r, :n], s_ref[r, :n], mags[r, :n], f"pair scores b={r} q={i}")
