@@ -97,6 +97,8 @@ MQ_INDEXER_CASES = [
     ("c3f", {"idx_heads": 32}),
     ("c3f", {"idx_heads": 16}),
     ("c3f", {"page_size": 16}),
+    ("c3", {"idx_heads": 32}),
+    ("c3", {"page_size": 16}),                     # bf16 keys, pages shorter than a step
 ]
 
 
