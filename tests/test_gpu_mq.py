@@ -142,3 +142,63 @@ def test_mq_indexer_against_one_query_at_a_time(name, kw):
                                                inp.lens, max_len=inp.max_len, score_stride=S)
         for r, n in enumerate(lens):
             parity.check_scores(a[r, :n], s_ref[r, :n], mags[r, :n], f"pair scores b={r} q={i}")
+
+
+def test_mq_indexer_flags_bad_length_when_max_len_is_zero():
+    """The two-query indexer with max_len 0 and a request of length 5: both
+    of its queries are flagged, the empty request's are not."""
+    spm = _lib()
+    cfg = gen.CONFIGS["c3f"].with_(batch=2)
+    inp = gen.make_inputs(cfg, lens=[0, 5])
+    _, qi, w = gen.make_mq_queries(inp, 2)
+    db = device_batch(inp)
+    scores = torch.zeros(4, 64, dtype=torch.float32, device="cuda")
+    st = torch.zeros(4, dtype=torch.int32, device="cuda")
+    spm.dsa_indexer_scores_mq(tensor(qi, "cuda"), torch.from_numpy(w).cuda(), db.k_idx, db.k_idx_scale,
+                              db.block_table, db.lens, 0, scores, req_status=st)
+    torch.cuda.synchronize()
+    assert list(st.cpu().numpy()) == [0, 0, spm.BAD_LEN, spm.BAD_LEN]
+
+
+@pytest.mark.parametrize("name", ["c3", "c3f"])
+def test_mq_indexer_bad_pages(name):
+    """Block-table entries out of range (negative, and past the pool) in two
+    requests: the two-query indexer flags both queries of those requests and
+    leaves their tokens on the bad pages NaN, like the one-query indexer;
+    every other score and status is untouched (bit for bit with bf16 keys)."""
+    spm = _lib()
+    lens = [3000, 700, 5000]
+    cfg = gen.CONFIGS[name].with_(batch=3)
+    inp = gen.make_inputs(cfg, lens=lens)
+    P = cfg.page_size
+    bt = inp.block_table.copy()
+    bt[0, 5] = -3
+    bt[2, (5000 - 1) // P] = inp.k_idx.shape[0] + 7
+    _, qi, w = gen.make_mq_queries(inp, 2)
+    db = device_batch(inp)
+    bt_d = tensor(bt, "cuda")
+    B, S = 3, inp.score_stride
+    qi_d, w_d = tensor(qi, "cuda"), torch.from_numpy(w).cuda()
+    both = torch.full((B * 2, S), float("nan"), device="cuda")
+    st_both = torch.zeros(B * 2, dtype=torch.int32, device="cuda")
+    spm.dsa_indexer_scores_mq(qi_d, w_d, db.k_idx, db.k_idx_scale, bt_d, db.lens, db.max_len, both,
+                              req_status=st_both)
+    torch.cuda.synchronize()
+    assert list(st_both.cpu().numpy()) == [spm.BAD_PAGE] * 2 + [0] * 2 + [spm.BAD_PAGE] * 2
+    a = both.view(B, 2, S).cpu().numpy()
+    for i in range(2):
+        one = torch.full((B, S), float("nan"), device="cuda")
+        st_one = torch.zeros(B, dtype=torch.int32, device="cuda")
+        spm.dsa_indexer_scores(qi_d[:, i].contiguous(), w_d[:, i].contiguous(), db.k_idx, db.k_idx_scale, bt_d,
+                               db.lens, db.max_len, one, req_status=st_one)
+        torch.cuda.synchronize()
+        b = one.cpu().numpy()
+        np.testing.assert_array_equal(st_one.cpu().numpy(), st_both.view(B, 2)[:, i].cpu().numpy())
+        for r, n in enumerate(lens):
+            np.testing.assert_array_equal(np.isnan(a[r, i, :n]), np.isnan(b[r, :n]), err_msg=f"request {r} query {i}")
+            if cfg.idx_dtype != gen.FP8:
+                np.testing.assert_array_equal(a[r, i, :n].view(np.uint32), b[r, :n].view(np.uint32))
+    assert np.isnan(a[0, :, 5 * P:6 * P]).all() and not np.isnan(a[0, :, :5 * P]).any()
+    last = (5000 - 1) // P * P
+    assert np.isnan(a[2, :, last:5000]).all() and not np.isnan(a[2, :, :last]).any()
+    assert not np.isnan(a[1, :, :700]).any()
