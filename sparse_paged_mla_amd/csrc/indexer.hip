@@ -20,11 +20,12 @@
 // product may sum its terms in any order, lane group g owns the contiguous
 // quarter [g*d/4, (g+1)*d/4) of the key row and k-step s takes KPL elements
 // of it; the query fragments use the same permutation.  In the two-query
-// kernel FP8 keys of 128 dims skip the widening: the query is held as two scaled e4m3 terms
-// (exact for every element within 2^14 of its row's largest, off by less
-// than 2^-22 of it otherwise) and each 16x16 block is two scaled FP8 MFMAs
-// over the stored key codes.  The ReLU-weighted head sum is a per-lane sum over the 4 rows it holds per M-tile plus two
-// xor shuffles.
+// kernel FP8 keys of 128 dims skip the widening: the query is held as two
+// scaled e4m3 terms (exact for every element within 2^14 of its row's
+// largest, off by less than 2^-22 of it otherwise) and each 16x16 block is
+// two scaled FP8 MFMAs over the stored key codes.  The ReLU-weighted head
+// sum is a per-lane sum over the 4 rows it holds per M-tile plus two xor
+// shuffles.
 #include "common.h"
 #include "launch.h"
 
@@ -149,20 +150,17 @@ void indexer_kernel(
   constexpr bool PAIR = NQ == 2;
   constexpr int WAVES = IdxWg<MT, NQ>::waves;
   constexpr int NSTAGE = PAIR ? 2 : 4;  // the pair's two buffers, or one per wave
-  constexpr int NQW = PAIR ? 1 : NQ;    // queries a wave scores
   // Scaled FP8 MFMA on the stored key codes (FP8 keys of 128 dims, pairs):
   // measured on c3f (64 requests, 32K-128K tokens), the pair kernel 238 ->
   // about 219 us; the one-query kernel 131.5 -> 139 us, so it keeps bf16.
   constexpr bool F8S = PAIR && kBf && KDT == kFP8 && D == 128;
   constexpr int STAGE_BYTES = NSTAGE * STEP_TOK * LROW;
-  constexpr int HELD_FIT = (IdxWg<MT, NQ>::lds - STAGE_BYTES) / (NQW * WAVES * STEP_TOK * 4);
+  constexpr int HELD_FIT = (IdxWg<MT, NQ>::lds - STAGE_BYTES) / (WAVES * STEP_TOK * 4);
   constexpr int HELD = HELD_FIT < 1 ? 1 : HELD_FIT > kIdxMaxHeldSteps ? kIdxMaxHeldSteps : HELD_FIT;
-  constexpr int MTQ = MT / NQW;  // M-tiles per query
-  static_assert(MT % NQW == 0, "queries split the M-tiles evenly");
   constexpr int PW = PAIR ? PIECES / 2 : PIECES;  // pieces of a step this wave loads
   constexpr int WLOADS = (PW + 63) / 64;
   __shared__ __attribute__((aligned(16))) uint8_t stage[NSTAGE][STEP_TOK * LROW];
-  __shared__ __attribute__((aligned(16))) float held[NQW][WAVES][HELD * STEP_TOK];
+  __shared__ __attribute__((aligned(16))) float held[WAVES][HELD * STEP_TOK];
   const int32_t rows = NQ * n_heads;  // query rows of one request
 
   const int lane = threadIdx.x & 63;
@@ -175,7 +173,7 @@ void indexer_kernel(
   const int64_t nw = PAIR ? (int64_t)gridDim.x : (int64_t)gridDim.x * 4;
   const int64_t gw = PAIR ? (int64_t)xcd_remap(blockIdx.x, gridDim.x)
                           : (int64_t)xcd_remap(blockIdx.x, gridDim.x) * 4 + wv;
-  const int qw = PAIR ? wv : 0;          // the wave's query (pair) or first query
+  const int qw = PAIR ? wv : 0;          // the wave's query: every wave scores one
   const int pbase = PAIR ? wv * PW : 0;  // the wave's first piece of a step
   int cbuf = 0;                          // the pair's stage buffer for the next step consumed
 
@@ -221,9 +219,10 @@ void indexer_kernel(
 
   // Query fragments (A operand: rows = heads), permuted like the key slices,
   // and head weights of request `rb`.
-  // With FP8 keys of 128 dims the query is held instead as two scaled e4m3
-  // terms per row (qh, ql with E8M0 scales sh, sl; exact, see split_q32) and
-  // the keys go to the scaled FP8 MFMA as they are stored: no widening.
+  // In the two-query kernel with FP8 keys of 128 dims the query is held
+  // instead as two scaled e4m3 terms per row (qh, ql with E8M0 scales qsh,
+  // qsl, the representation split_q32 states) and the keys go to the scaled
+  // FP8 MFMA as they are stored: no widening.
   typename Op::frag qa[MT][KSTEPS];
   v8i_t qh[MT], ql[MT];
   int qsh[MT], qsl[MT];
@@ -235,10 +234,10 @@ void indexer_kernel(
       const int h = qw * n_heads + hq;  // row within the request's queries
       if constexpr (F8S) {
         uint32_t raw[16] = {};
-        if (hq < NQW * n_heads)
+        if (hq < n_heads)
           load_raw<64>(reinterpret_cast<const uint8_t*>(q_idx) + (((int64_t)rb * rows + h) * D + g * 32) * 2, raw);
         split_q32(raw, qh[mt], ql[mt], qsh[mt], qsl[mt]);  // the whole wave, every row
-      } else if (hq < NQW * n_heads) {
+      } else if (hq < n_heads) {
         uint32_t raw[(GROUP_ELEMS * QE + 3) / 4];
         const uint8_t* qp =
             reinterpret_cast<const uint8_t*>(q_idx) + (((int64_t)rb * rows + h) * D + g * GROUP_ELEMS) * QE;
@@ -251,7 +250,7 @@ void indexer_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int hh = mt * 16 + g * 4 + i;
-        wr[mt][i] = hh < NQW * n_heads ? w[(int64_t)rb * rows + qw * n_heads + hh] : 0.f;
+        wr[mt][i] = hh < n_heads ? w[(int64_t)rb * rows + qw * n_heads + hh] : 0.f;
       }
     }
   };
@@ -276,7 +275,7 @@ void indexer_kernel(
     int n_held = 0;     // steps whose scores wait in held[wv]
     int64_t t_held = 0; // first token of those steps (they are consecutive)
     const int32_t* btb = bt + (int64_t)b * bt_stride;
-    float* sc_out = scores + (int64_t)b * NQ * score_stride;  // query qi's row: sc_out + qi * score_stride
+    float* sc_out = scores + (int64_t)b * NQ * score_stride;  // query i's row: sc_out + i * score_stride
     const int64_t last_page = ((int64_t)L - 1) >> page_shift;
 
     // Block-table entries of step si: lane j < 4 loads the entry of the
@@ -348,19 +347,16 @@ void indexer_kernel(
     auto write_held = [&]() __attribute__((always_inline)) {
       __builtin_amdgcn_wave_barrier();
       const int cnt = n_held * STEP_TOK;
-#pragma unroll
-      for (int qi = 0; qi < NQW; ++qi) {
-        float* out = sc_out + (qw + qi) * score_stride;
-        for (int i = lane * 4; i < cnt; i += 256) {
-          const int64_t t = t_held + i;
-          const float4 v4 = *reinterpret_cast<const float4*>(&held[qi][wv][i]);
-          if (t + 3 < L) {
-            *reinterpret_cast<float4*>(out + t) = v4;
-          } else {
-            if (t < L) out[t] = v4.x;
-            if (t + 1 < L) out[t + 1] = v4.y;
-            if (t + 2 < L) out[t + 2] = v4.z;
-          }
+      float* out = sc_out + qw * score_stride;
+      for (int i = lane * 4; i < cnt; i += 256) {
+        const int64_t t = t_held + i;
+        const float4 v4 = *reinterpret_cast<const float4*>(&held[wv][i]);
+        if (t + 3 < L) {
+          *reinterpret_cast<float4*>(out + t) = v4;
+        } else {
+          if (t < L) out[t] = v4.x;
+          if (t + 1 < L) out[t + 1] = v4.y;
+          if (t + 2 < L) out[t + 2] = v4.z;
         }
       }
       __builtin_amdgcn_wave_barrier();
@@ -427,22 +423,19 @@ void indexer_kernel(
         }
         const float tsc = __shfl(sc, tok);
         const bool bad = __shfl(bad_tok, tok) != 0;
+        float v = 0.f;
 #pragma unroll
-        for (int qi = 0; qi < NQW; ++qi) {
-          float v = 0.f;
+        for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
-          for (int mt = qi * MTQ; mt < (qi + 1) * MTQ; ++mt) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              // ReLU as an integer max on the bit pattern (one instruction: a
-              // negative float has a negative integer pattern).
-              const float r = __int_as_float(max(__float_as_int(acc[mt][i]), 0));
-              v += wr[mt][i] * r;
-            }
+          for (int i = 0; i < 4; ++i) {
+            // ReLU as an integer max on the bit pattern (one instruction: a
+            // negative float has a negative integer pattern).
+            const float r = __int_as_float(max(__float_as_int(acc[mt][i]), 0));
+            v += wr[mt][i] * r;
           }
-          v = wave_sum_xor16_32(v);
-          if (g == 0) held[qi][wv][n_held * STEP_TOK + tok] = bad ? __uint_as_float(0x7FC00000u) : v * tsc;
         }
+        v = wave_sum_xor16_32(v);
+        if (g == 0) held[wv][n_held * STEP_TOK + tok] = bad ? __uint_as_float(0x7FC00000u) : v * tsc;
       }
       if (n_held == 0) t_held = t0;
       if (++n_held == HELD) write_held();
