@@ -178,13 +178,13 @@ class MultiQueryStep:
         self.real = batch
         self.q_idx_mq, self.w_mq = q_idx, w
         H_I = q_idx.shape[2]
-        self.fused_indexer = batch.topk > 0 and n_q == 2 and H_I in (16, 32, 64) and q_idx.dtype == torch.bfloat16
+        self.two_query_indexer = batch.topk > 0 and n_q == 2 and H_I in (16, 32, 64) and q_idx.dtype == torch.bfloat16
 
     def expand(self, stream=None):
         mq_expand_requests(self.real_bt, self.real_lens, self.n_q, self.bt, self.lens, stream)
 
     def indexer(self, stream=None):
-        if self.fused_indexer:
+        if self.two_query_indexer:
             r = self.real
             dsa_indexer_scores_mq(self.q_idx_mq, self.w_mq, r.k_idx, r.k_idx_scale, r.block_table, r.lens, r.max_len,
                                   self.step.scores, self.step.status, stream)

@@ -105,7 +105,7 @@ def test_full_size_multi_query_c3f():
     q, qi, w = gen.make_mq_queries(inp, n_q)
     st = MultiQueryStep(device_batch(inp), tensor(q, "cuda"), tensor(qi, "cuda"), torch.from_numpy(w).cuda(),
                         num_splits=DEFAULT_SPLITS["c3f"])
-    assert st.fused_indexer
+    assert st.two_query_indexer
     _say("c3f n_q=2: running the multi-query step")
     st.run()
     torch.cuda.synchronize()
