@@ -118,6 +118,13 @@ int dsa_indexer_scores(const void* q_idx, int32_t q_dtype, const float* weights,
  * (see mq_expand_requests): all n_q queries of a request are scored against
  * each key as it is read, so the key pool is read once for all of them.
  * Same arguments and arithmetic as dsa_indexer_scores, except:
+ *  arithmetic with n_q = 2, FP8 keys and d = 128: each query row is held as
+ *          2^(E-7) * (hi + lo/16), hi and lo e4m3 codes and E the exponent
+ *          of the row's largest |q| (exact for every element within 2^14 of
+ *          it, off by less than 2^-22 of it otherwise), and the products run
+ *          on the scaled FP8 MFMA over the stored key codes: the scores agree
+ *          with dsa_indexer_scores' to fp32 rounding, not bit for bit (with
+ *          bf16 keys they are equal bit for bit);
  *  q_idx   [batch, n_q, n_heads, d], weights [batch, n_q, n_heads];
  *  scores  [batch * n_q, score_stride]: row b * n_q + i holds query i's
  *          scores for every t < context_lens[b] (the tokens that query may
