@@ -66,7 +66,7 @@ __device__ __forceinline__ uint32_t lds_addr(T* p) {
 // Logical workgroup index: the hardware deals workgroup ids round-robin over
 // the 8 XCDs, so logical indices [x * n / 8, (x + 1) * n / 8) are given the
 // ids that land on XCD x, and neighbours in the logical order share an L2.
-__device__ __forceinline__ int xcd_remap(int bid, int n) {
+__host__ __device__ __forceinline__ int xcd_remap(int bid, int n) {
   const int q = n >> 3, r = n & 7;
   const int xcd = bid & 7, slot = bid >> 3;
   return xcd < r ? xcd * (q + 1) + slot : r * (q + 1) + (xcd - r) * q + slot;
@@ -87,7 +87,7 @@ __device__ __forceinline__ int xcd_remap(int bid, int n) {
 struct WgCoord {
   int b, s, hg;
 };
-__device__ __forceinline__ WgCoord wg_coord(int bid, int n, int num_splits, int n_hg, bool spread) {
+__host__ __device__ __forceinline__ WgCoord wg_coord(int bid, int n, int num_splits, int n_hg, bool spread) {
   if (!spread) {
     const int logical = xcd_remap(bid, n);
     return {logical / (n_hg * num_splits), (logical / n_hg) % num_splits, logical % n_hg};
