@@ -99,6 +99,8 @@ MQ_INDEXER_CASES = [
     ("c3f", {"page_size": 16}),
     ("c3", {"idx_heads": 32}),
     ("c3", {"page_size": 16}),                     # bf16 keys, pages shorter than a step
+    ("c3", {"page_size": 128}),                    # steps starting inside a page
+    ("c3f", {"page_size": 32, "idx_heads": 16}),   # two pages per step
 ]
 
 
